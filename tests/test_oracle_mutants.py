@@ -1,0 +1,76 @@
+"""The pins can see a plausible mistake: each planted mistake, compiled into a
+separate copy of the oracle on the CPU, must fail at least one pin.  (Only the
+oracle is ever mutated; nothing here runs on a GPU.)"""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import brute
+from oracle import oracle as O
+
+from .test_oracle_quant import WORKED
+
+MUTANTS = {
+    1: "round half to even",
+    2: "divide by the unrounded binary32 scale",
+    3: "q4_0 signed maximum taken at the last index on ties",
+    4: "q4_0 nibbles packed as adjacent pairs",
+    5: "combine drops the last split",
+}
+
+
+def worked_blocks_pass(lib) -> bool:
+    for _, t, x, scale, data in WORKED:
+        d, s = O.quantize(t, x[None, :], lib=lib)
+        if int(s[0, 0]) != scale or d[0].tobytes() != data:
+            return False
+    return True
+
+
+def brute_agrees(lib) -> bool:
+    rng = np.random.default_rng(21)
+    x = np.concatenate([rng.standard_normal((200, 32)),
+                        rng.integers(-20, 20, (200, 32)) / 8.0]).astype(np.float16).view(np.uint16)
+    for t in ("q8_0", "q4_0"):
+        data, scales = O.quantize(t, x, lib=lib)
+        for i in range(x.shape[0]):
+            if t == "q8_0":
+                s, q = brute.quant_q8_0([int(v) for v in x[i]])
+                got = bytes((v & 0xFF) for v in q)
+            else:
+                s, got = brute.quant_q4_0([int(v) for v in x[i]])
+                got = bytes(got)
+            if s != int(scales[i, 0]) or got != data[i].tobytes():
+                return False
+    return True
+
+
+def split_combine_matches(lib) -> bool:
+    rng = np.random.default_rng(22)
+    D, Hkv, C = 32, 1, 100
+    q = rng.standard_normal((1, 2, D)).astype(np.float16)
+    k = rng.standard_normal((1, Hkv, C, D)).astype(np.float16)
+    v = rng.standard_normal((1, Hkv, C, D)).astype(np.float16)
+    kc = ("f16",) + O.quantize("f16", k, lib=lib)
+    vc = ("f16",) + O.quantize("f16", v, lib=lib)
+    po, pl = O.attend_split(q, kc, vc, [C], Hkv, 0.2, 16, 7, lib=lib)
+    out, lse = O.combine(po, pl, lib=lib)
+    ref, ref_lse = O.attend(q, kc, vc, [C], Hkv, 0.2, lib=lib)
+    return bool(np.allclose(out, ref, atol=1e-12) and np.allclose(lse, ref_lse, atol=1e-12))
+
+
+BATTERY = [worked_blocks_pass, brute_agrees, split_combine_matches]
+
+
+def test_unmutated_oracle_passes_battery():
+    lib = O.load()
+    assert all(f(lib) for f in BATTERY)
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=[MUTANTS[m] for m in sorted(MUTANTS)])
+def test_planted_mistake_is_caught(mutant, tmp_path):
+    path = O.build(str(tmp_path / f"liboracle_m{mutant}.so"), mutant=mutant)
+    lib = O.load(path)
+    results = {f.__name__: f(lib) for f in BATTERY}
+    assert not all(results.values()), f"mutant '{MUTANTS[mutant]}' passed every pin: {results}"
