@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark over a block-quantised KV cache on one MI355X.
+
+One step = the whole hot path for every layer of the workload: quantise-append
+one new token per sequence (kvq_quantize_append), split-KV decode attention
+(kvq_decode_attn) and the log-sum-exp combine (kvq_combine), on inputs already
+resident in HBM.  The default workload is the 48-layer stack at 65536 rows
+(40 query / 8 KV heads, head_dim 128) with the f16, q8_0K/q4_0V and q4_0/q4_0
+arms; the headline value is the q8_0K/q4_0V arm.
+
+value = stored KV bytes read per step / step time (GB/s, 1e9 bytes/s), where
+stored bytes = sum_b L_b * Hkv * (row bytes of K + row bytes of V) summed over
+layers (f16 2*D, q8_0 34*D/32, q4_0 18*D/32 bytes per row).
+
+Prints ONE JSON line.  Steps are captured once in a HIP graph and replayed
+(--no-graph replays eager launches instead).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn KV GB/s (stored bytes) and % of MI355X HBM peak; µs/step at 64k–256k"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="stack48_d128_ctx64k")
+    p.add_argument("--arms", default=None, help="comma list like q8_0/q4_0,f16/f16 (default: all)")
+    p.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
+    p.add_argument("--split-tokens", type=int, default=None)
+    p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="approximate CPU time budget of the oracle baseline (0 disables it)")
+    p.add_argument("--replicas", type=int, default=0,
+                   help="cache copies rotated per step so the working set exceeds the 256 MB "
+                        "last-level cache (0 = automatic)")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Arm:
+    """All device state of one (K type, V type) arm of a workload."""
+
+    def __init__(self, wl, tk, tv, split_tokens, replicas, dev):
+        import torch
+
+        from quantised_kv_long_amd import cache as C
+        from quantised_kv_long_amd import synth
+
+        self.tk, self.tv = tk, tv
+        self.lens = wl.lengths()
+        cap = max(self.lens)
+        B, Hkv, Hq, D = wl.B, wl.Hkv, wl.Hq, wl.D
+        self.wl = wl
+        self.layers = []  # per layer: dict of planes and per-step tensors
+        zero = torch.zeros(B, dtype=torch.int32, device=dev)
+        n_copies = wl.layers * replicas
+        for i in range(n_copies):
+            layer = i % wl.layers
+            k = synth.normal_f16((B, cap, Hkv, D), synth.seed_for(wl.seed, layer, "k"), dev)
+            v = synth.normal_f16((B, cap, Hkv, D), synth.seed_for(wl.seed, layer, "v"), dev)
+            q = synth.normal_f16((B, Hq, D), synth.seed_for(wl.seed, layer, "q"), dev)
+            if wl.k_outlier_frac:
+                ch = synth.outlier_channels(D, synth.seed_for(wl.seed, layer, "aux"), wl.k_outlier_frac)
+                k[..., ch] = (k[..., ch].float() * 8).half()
+            if wl.needle:
+                p = self.lens[0] // 3
+                for g in range(Hkv):
+                    k[0, p, g] = synth.needle_row(q[0, g * wl.G], synth.seed_for(wl.seed, g, "aux"))
+            kc = C.CachePlanes.alloc(tk, B, Hkv, cap, D, dev)
+            vc = C.CachePlanes.alloc(tv, B, Hkv, cap, D, dev)
+            C.append(kc, vc, k[:, :cap - 1].contiguous(), v[:, :cap - 1].contiguous(), zero, cap - 1)
+            del k, v
+            knew = synth.normal_f16((B, 1, Hkv, D), synth.seed_for(wl.seed, layer, "k_new"), dev)
+            vnew = synth.normal_f16((B, 1, Hkv, D), synth.seed_for(wl.seed, layer, "v_new"), dev)
+            self.layers.append(dict(kc=kc, vc=vc, q=q, knew=knew, vnew=vnew))
+        torch.cuda.synchronize()
+        self.pos = torch.tensor([L - 1 for L in self.lens], dtype=torch.int32, device=dev)
+        self.lens_t = torch.tensor(self.lens, dtype=torch.int32, device=dev)
+        self.max_len = cap
+        self.part = C.Partials(B, Hq, D, cap, split_tokens, dev)
+        self.out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+        self.stored_bytes_layer = kc.stored_bytes(self.lens) + vc.stored_bytes(self.lens)
+        self.stored_bytes_step = self.stored_bytes_layer * wl.layers
+        self.replicas = replicas
+
+    def prepare_calls(self, variant):
+        """Pre-marshalled C calls (descriptors and pointers built once)."""
+        import ctypes
+
+        from quantised_kv_long_amd import _lib
+
+        lib = _lib.load()
+        wl = self.wl
+        vcode = _lib.VARIANTS[variant]
+        scale = 1.0 / math.sqrt(wl.D)
+        self.calls = []
+        for L in self.layers:
+            kd, vd = L["kc"].desc(), L["vc"].desc()
+            L["descs"] = (kd, vd)  # keep alive
+            self.calls.append((
+                (ctypes.byref(kd), ctypes.byref(vd), L["knew"].data_ptr(), L["vnew"].data_ptr(),
+                 self.pos.data_ptr(), wl.B, 1, wl.Hkv, wl.D, self.max_len),
+                (ctypes.byref(kd), ctypes.byref(vd), L["q"].data_ptr(), self.lens_t.data_ptr(), wl.B,
+                 wl.Hq, wl.Hkv, wl.D, scale, self.max_len, self.part.split_tokens,
+                 self.part.max_splits, self.part.o.data_ptr(), self.part.lse.data_ptr(), vcode),
+                (self.part.o.data_ptr(), self.part.lse.data_ptr(), self.lens_t.data_ptr(), wl.B,
+                 wl.Hq, wl.D, self.part.split_tokens, self.part.max_splits, 0, self.out.data_ptr(),
+                 None),
+            ))
+        self.lib = lib
+
+    def step(self, stream, rep=0, decode_only=False):
+        lib = self.lib
+        n = self.wl.layers
+        for a, d, c in self.calls[rep * n:(rep + 1) * n]:
+            if not decode_only:
+                rc = lib.kvq_quantize_append(*a, stream)
+                assert rc == 0, rc
+            rc = lib.kvq_decode_attn_variant(*d, stream)
+            assert rc == 0, rc
+            if not decode_only:
+                rc = lib.kvq_combine(*c, stream)
+                assert rc == 0, rc
+
+
+def time_arm(arm, steps, warmup, use_graph, variant):
+    import torch
+
+    arm.prepare_calls(variant)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    R = arm.replicas
+    for i in range(warmup):
+        arm.step(sh, i % R)
+    torch.cuda.synchronize()
+
+    graphs = []
+    dgraphs = []
+    if use_graph:
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                arm.step(torch.cuda.current_stream().cuda_stream, r)
+            graphs.append(g)
+            dg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(dg):
+                arm.step(torch.cuda.current_stream().cuda_stream, r, decode_only=True)
+            dgraphs.append(dg)
+        for r in range(R):
+            graphs[r].replay()
+            dgraphs[r].replay()
+        torch.cuda.synchronize()
+
+    def run(k, decode_only=False):
+        for i in range(k):
+            r = i % R
+            if use_graph:
+                (dgraphs if decode_only else graphs)[r].replay()
+            else:
+                arm.step(sh, r, decode_only)
+
+    # whole step
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    run(steps)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    # decode kernel alone (same launches, same stream)
+    e0.record(stream)
+    run(steps, decode_only=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_decode_launch = e0.elapsed_time(e1) / (steps * arm.wl.layers)
+    return ms_step, ms_decode_launch
+
+
+def cpu_baseline(arm, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same step: whole
+    layers (quantise the new row, fp64 attention per split, exact combine) of
+    the same cache bytes, timed on this host's cores."""
+    import numpy as np
+    import torch
+
+    from oracle import oracle as O
+
+    wl = arm.wl
+    threads = min(16, len(os.sched_getaffinity(0)))
+    u16 = lambda t: t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    done, elapsed = 0, 0.0
+    for L in arm.layers[: wl.layers]:
+        kc, vc = L["kc"], L["vc"]
+        name = {0: "f16", 1: "q8_0", 2: "q4_0"}
+        kp = (name[kc.type], kc.data.cpu().numpy(),
+              kc.scales.cpu().numpy().view(np.uint16) if kc.scales is not None else None)
+        vp = (name[vc.type], vc.data.cpu().numpy(),
+              vc.scales.cpu().numpy().view(np.uint16) if vc.scales is not None else None)
+        q = u16(L["q"])
+        knew, vnew = u16(L["knew"]), u16(L["vnew"])
+        t0 = time.perf_counter()
+        O.quantize(kp[0], knew)
+        O.quantize(vp[0], vnew)
+        po, pl = O.attend_split(q, kp, vp, arm.lens, wl.Hkv, 1 / math.sqrt(wl.D),
+                                arm.part.split_tokens, arm.part.max_splits, nthreads=threads)
+        O.combine(po, pl)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed >= budget_s:
+            break
+    s_per_layer = elapsed / done
+    gbs = arm.stored_bytes_layer / s_per_layer / 1e9
+    sample = (f"{done} of {wl.layers} layer(s) of {wl.name}, {arm.tk}/{arm.tv}: quantise the new "
+              f"row, fp64 attention over {arm.part.max_splits} splits of {arm.part.split_tokens} "
+              f"rows, exact combine; {s_per_layer * 1e3:.1f} ms per layer")
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "us_per_step_scaled": round(s_per_layer * wl.layers * 1e6, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the decode path would shard by sequence or KV head with no exchange, or by "
+              "context with one all-gather of split partials; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantised_kv_long_amd as kvq
+    from quantised_kv_long_amd import synth
+
+    kvq.load()
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    arms = wl.arms
+    if args.arms:
+        arms = [tuple(a.split("/")) for a in args.arms.split(",")]
+    split_tokens = args.split_tokens or wl.split_tokens
+    headline = ("q8_0", "q4_0") if ("q8_0", "q4_0") in arms else arms[0]
+
+    results = {}
+    head_arm = None
+    for tk, tv in arms:
+        per_layer = sum(wl.lengths()) * wl.Hkv * (
+            kvq.kvq_data_row_bytes(tk, wl.D) + kvq.kvq_scale_row_bytes(tk, wl.D) +
+            kvq.kvq_data_row_bytes(tv, wl.D) + kvq.kvq_scale_row_bytes(tv, wl.D))
+        reps = args.replicas or max(1, math.ceil(1.0e9 / (per_layer * wl.layers)))
+        log(f"arm {tk}/{tv}: building {wl.layers} layer(s) x {reps} replica(s)")
+        arm = Arm(wl, tk, tv, split_tokens, reps, dev)
+        log(f"arm {tk}/{tv}: timing {args.steps} steps")
+        ms_step, ms_dec = time_arm(arm, args.steps, args.warmup, not args.no_graph, args.variant)
+        gbs = arm.stored_bytes_step / (ms_step * 1e-3) / 1e9
+        dec_gbs = arm.stored_bytes_layer / (ms_dec * 1e-3) / 1e9
+        results[f"{tk}/{tv}"] = {
+            "us_per_step": round(ms_step * 1e3, 2),
+            "stored_bytes_per_step": arm.stored_bytes_step,
+            "GBps": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "decode_us_per_launch": round(ms_dec * 1e3, 3),
+            "decode_GBps": round(dec_gbs, 1),
+            "replicas": reps,
+        }
+        log(f"arm {tk}/{tv}: {results[f'{tk}/{tv}']}")
+        if (tk, tv) == headline:
+            head_arm = arm
+        else:
+            del arm
+            torch.cuda.empty_cache()
+
+    h = results[f"{headline[0]}/{headline[1]}"]
+    cpu = None
+    if args.cpu_seconds > 0:
+        log("oracle CPU baseline")
+        cpu = cpu_baseline(head_arm, args.cpu_seconds)
+    ratios = {}
+    if "q4_0/q4_0" in results and "q8_0/q4_0" in results:
+        ratios["q4q4_over_q8q4_speedup"] = round(results["q8_0/q4_0"]["us_per_step"] /
+                                                 results["q4_0/q4_0"]["us_per_step"], 3)
+    if "f16/f16" in results and "q8_0/q4_0" in results:
+        ratios["q8q4_over_f16_speedup"] = round(results["f16/f16"]["us_per_step"] /
+                                                results["q8_0/q4_0"]["us_per_step"], 3)
+    line = {
+        "metric": METRIC,
+        "value": h["GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["us_per_step"] / 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "arm": f"{headline[0]}K/{headline[1]}V",
+                   "layers": wl.layers, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+                   "head_dim": wl.D, "ctx": wl.ctx, "split_tokens": split_tokens,
+                   "variant": args.variant, "graph": not args.no_graph},
+        "roofline": {"bound": "hbm", "achieved": h["decode_GBps"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(h["decode_GBps"] / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "kvq_decode_attn",
+                     "avg_launch_us": h["decode_us_per_launch"]},
+        "cpu_baseline": cpu,
+        "arms": results,
+        "ratios": ratios,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,204 @@
+/*
+ * kvq.h -- C ABI of the block-quantised KV-cache decode-attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (HAL #582 "per-layer KV compression study"):
+ *   - section 1 (size model table): each token's K and V row per KV head is
+ *     stored either as f16 or as 32-value blocks with one fp16 scale:
+ *     q8_0 = 32 int8 codes (34 bytes per block), q4_0 = 32 four-bit codes
+ *     (18 bytes per block).  K and V types are chosen independently (section 2
+ *     quality bar and section 5 P1: "-ctk/-ctv", asymmetric q8_0 K + q4_0 V).
+ *   - section 5 P2 "write path": a new token is quantised once, when written.
+ *   - section 3b and section 5 P0: decode attention reads the stored blocks and
+ *     dequantises them in registers, so the bytes moved per token fall with
+ *     the format (the bandwidth-bound reader the study asks for).
+ *   - section 5 P2 "read path": attention over separate regions is merged
+ *     with an exact online-softmax combine; here the regions are the splits of
+ *     a split-KV (flash-decoding) launch.
+ *
+ * Conventions shared by every entry point:
+ *   - The caller owns all memory.  Every pointer marked "device" is HIP device
+ *     memory of the current device; the library allocates nothing and keeps
+ *     no state between calls, so calls are thread-safe.
+ *   - Calls only enqueue work on `stream` (a hipStream_t; NULL means the
+ *     legacy default stream) and return.  KVQ_OK means "enqueued".
+ *   - Scalar arguments are validated on the host before any HIP call; an
+ *     invalid call returns a negative status and enqueues nothing.  Contents
+ *     of device arrays (positions, lengths) are preconditions and are not
+ *     checked.
+ *   - Layouts are row-major C arrays unless stated otherwise.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage type of one cache tensor (K or V). */
+typedef enum {
+    KVQ_F16 = 0,  /* IEEE binary16 values, 2*D bytes per row, no scale plane   */
+    KVQ_Q8_0 = 1, /* per 32-value block: 32 int8 codes + one fp16 scale        */
+    KVQ_Q4_0 = 2  /* per 32-value block: 32 codes in [0,15] (value = code - 8),
+                     packed two per byte, + one fp16 scale                     */
+} kvq_type;
+
+/* Status codes (negative = error, nothing was enqueued). */
+enum {
+    KVQ_OK = 0,
+    KVQ_ERR_NULL = -1,     /* a required pointer is NULL                        */
+    KVQ_ERR_SHAPE = -2,    /* a size is out of range or inconsistent            */
+    KVQ_ERR_TYPE = -3,     /* unknown storage or output type                    */
+    KVQ_ERR_ALIGN = -4,    /* a plane or array is not aligned as required       */
+    KVQ_ERR_CAPACITY = -5, /* rows requested beyond a cache's capacity          */
+    KVQ_ERR_SPLITS = -6,   /* split arithmetic does not fit                     */
+    KVQ_ERR_LAUNCH = -7    /* the HIP runtime reported an error at launch       */
+};
+
+/* Granule of `split_tokens`: every split is a whole number of this many rows. */
+#define KVQ_SPLIT_GRANULE 64
+
+/* Largest head dimension and query-group size the kernels accept. */
+#define KVQ_MAX_HEAD_DIM 512
+#define KVQ_MAX_GROUP 16
+
+/*
+ * One cache tensor (K or V) of one layer, stored as two planes in device
+ * memory (the same bytes as the 34-/18-byte blocks of the storage format,
+ * split so that every data row starts on a 16-byte boundary):
+ *   data plane : rows of kvq_data_row_bytes(type, D) bytes.
+ *                f16: D binary16 values.  q8_0: D int8 codes, block b at
+ *                bytes [32b, 32b+32).  q4_0: D/2 bytes, block b at bytes
+ *                [16b, 16b+16); byte j of a block holds the code of element j
+ *                in its low nibble and of element j+16 in its high nibble.
+ *   scale plane: rows of D/32 binary16 scales (scale of block b at index b);
+ *                unused (may be NULL) for f16.
+ * Row t of KV head g of sequence b is row index
+ *     b * seq_stride_rows + g * head_stride_rows + t
+ * in both planes; rows t in [0, capacity) are addressable.  The usual layout
+ * is head_stride_rows = capacity, seq_stride_rows = Hkv * capacity.
+ * Alignment: data and scales must be 16-byte aligned.
+ */
+typedef struct {
+    int32_t type;             /* kvq_type                                   */
+    int32_t capacity;         /* addressable rows per (sequence, KV head)   */
+    void* data;               /* device: data plane                         */
+    void* scales;             /* device: scale plane (NULL for f16)         */
+    int64_t seq_stride_rows;  /* rows between sequences                     */
+    int64_t head_stride_rows; /* rows between KV heads of one sequence      */
+} kvq_plane_desc;
+
+/* Bytes of one data-plane row: 2*D (f16), D (q8_0), D/2 (q4_0); 0 for an
+ * unknown type or a D that is not a positive multiple of 32. */
+size_t kvq_data_row_bytes(int type, int head_dim);
+
+/* Bytes of one scale-plane row: 0 (f16), D/16 (q8_0, q4_0); 0 when invalid. */
+size_t kvq_scale_row_bytes(int type, int head_dim);
+
+/* Static, human-readable name of a status code. */
+const char* kvq_status_string(int status);
+
+/*
+ * Quantise-on-write (HAL #582 section 5 P2 write path: tokens are quantised
+ * once when written; section 1 gives the block formats).
+ *
+ * For every sequence b < B, new row r < n_new and KV head g < Hkv, converts
+ * the f16 row k_new[b][r][g][0..D) into k_cache's type and stores it at row
+ * positions[b] + r of KV head g of sequence b; likewise v_new into v_cache.
+ * Block quantiser (the pages do not print one; this is the library's fixed
+ * definition, bit-exact):
+ *   q8_0: d = fp16_rne(max_i |x_i| / 127) (binary32 division);
+ *         code_i = round_half_away_from_zero(x_i / d) clamped to [-127, 127]
+ *         (binary32 division by the stored d); all codes 0 when d == 0.
+ *   q4_0: s = the x_i of largest magnitude (lowest i on ties, +0 if none);
+ *         d = fp16_rne(s / -8); code_i = clamp(round_half_away(x_i / d),
+ *         -8, 7) + 8; all codes 8 when d == 0.
+ *   f16 : the bits are copied unchanged.
+ *
+ *   k_cache, v_cache : plane descriptors (host memory, read during the call).
+ *   k_new, v_new     : device, [B][n_new][Hkv][D] binary16.
+ *   positions        : device, [B] int32, first row written per sequence.
+ *   max_end          : host, max over b of positions[b] + n_new; must not
+ *                      exceed either cache's capacity (KVQ_ERR_CAPACITY).
+ *   Requirements: B >= 0, n_new >= 0, Hkv >= 1, D % 32 == 0, 32 <= D <= 512.
+ *   B == 0 or n_new == 0 enqueues nothing and returns KVQ_OK.
+ */
+int kvq_quantize_append(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache,
+                        const void* k_new, const void* v_new, const int32_t* positions,
+                        int B, int n_new, int Hkv, int D, int max_end, void* stream);
+
+/*
+ * Split-KV decode attention (HAL #582 section 3b finding 2 and section 5 P0:
+ * a reader that streams the stored blocks and dequantises them in registers;
+ * section 5 P2: regions merged exactly by log-sum-exp).
+ *
+ * One query row per query head.  Query head h reads KV head h / (Hq / Hkv).
+ * Sequence b attends over its rows [0, seq_lens[b]) with no mask.  The rows
+ * are cut into splits of split_tokens rows; split s of sequence b covers rows
+ * [s*split_tokens, min((s+1)*split_tokens, L_b)).  For every (b, h, s) with
+ * s < max_splits the call writes, in fp32,
+ *   part_lse[b][h][s]   = ln sum_t exp(score_t)   (-inf for an empty split)
+ *   part_o[b][h][s][:]  = sum_t exp(score_t - part_lse) * v_t   (0 if empty)
+ * with score_t = softmax_scale * sum_d q[b][h][d] * k_t[d] and k_t, v_t the
+ * dequantised rows (code * scale, exactly).
+ *
+ *   q              : device, [B][Hq][D] binary16.
+ *   seq_lens       : device, [B] int32, 1 <= L_b <= max_seq_len <= capacity.
+ *   max_seq_len    : host, an upper bound of every L_b.
+ *   split_tokens   : host, a positive multiple of KVQ_SPLIT_GRANULE.
+ *   max_splits     : host, >= ceil(max_seq_len / split_tokens).
+ *   part_o         : device, [B][Hq][max_splits][D] fp32, 16-byte aligned.
+ *   part_lse       : device, [B][Hq][max_splits] fp32.
+ *   Requirements: B >= 1, Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 16,
+ *   D % 32 == 0, 32 <= D <= 512, K and V caches with the same strides' meaning.
+ */
+int kvq_decode_attn(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache,
+                    const void* q, const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                    float softmax_scale, int max_seq_len, int split_tokens, int max_splits,
+                    float* part_o, float* part_lse, void* stream);
+
+/* Kernel family for kvq_decode_attn_variant. */
+enum {
+    KVQ_VARIANT_AUTO = 0, /* what kvq_decode_attn uses                         */
+    KVQ_VARIANT_VALU = 1, /* dot products on the vector ALUs                   */
+    KVQ_VARIANT_MFMA = 2  /* dot products on the matrix cores (16x16x32 f16)   */
+};
+
+/*
+ * kvq_decode_attn with an explicit kernel family; same arguments and results
+ * (within floating-point rounding).  KVQ_ERR_TYPE for an unknown variant.
+ */
+int kvq_decode_attn_variant(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache,
+                            const void* q, const int32_t* seq_lens, int B, int Hq, int Hkv,
+                            int D, float softmax_scale, int max_seq_len, int split_tokens,
+                            int max_splits, float* part_o, float* part_lse, int variant,
+                            void* stream);
+
+/*
+ * Exact log-sum-exp merge of split partials (HAL #582 section 5 P2 read path:
+ * regions merged by an exact online-softmax combine).  For each (b, h), with
+ * S_b = ceil(seq_lens[b] / split_tokens) (at most max_splits):
+ *   LSE = ln sum_{s<S_b} exp(part_lse[b][h][s])
+ *   out[b][h][:] = sum_{s<S_b} exp(part_lse[b][h][s] - LSE) * part_o[b][h][s][:]
+ * computed in fp32; a sequence whose splits are all empty gets out = 0 and
+ * LSE = -inf.
+ *
+ *   part_o, part_lse : device, as written by kvq_decode_attn.
+ *   seq_lens         : device, [B] int32 (the same lengths).
+ *   out_type         : KVQ_F16 or a value of 3 for fp32 (KVQ_OUT_F32).
+ *   out              : device, [B][Hq][D] of out_type.
+ *   lse_out          : device, [B][Hq] fp32, or NULL.
+ */
+#define KVQ_OUT_F32 3
+int kvq_combine(const float* part_o, const float* part_lse, const int32_t* seq_lens, int B,
+                int Hq, int D, int split_tokens, int max_splits, int out_type, void* out,
+                float* lse_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -234,6 +234,13 @@ static double deq(int type, const uint8_t* data, const uint16_t* scales,
     return d * (double)(n - 8);
 }
 
+/* Whole row r dequantised into out[0..D) (the same values as deq()). */
+static void deq_row(int type, const uint8_t* data, const uint16_t* scales,
+                    int64_t r, int D, double* out)
+{
+    for (int i = 0; i < D; ++i) out[i] = deq(type, data, scales, r, D, i);
+}
+
 int kvo_dequant_rows(int type, const uint8_t* data, const uint16_t* scales,
                      int64_t nrows, int D, double* out)
 {
@@ -269,18 +276,20 @@ typedef struct {
  * s_t = scale * sum_d q_d k_td;  o = sum_t exp(s_t - m) v_t / sum_t exp(s_t - m);
  * lse = m + ln sum_t exp(s_t - m).  An empty range gives o = 0, lse = -inf. */
 static void attend_region(const attn_job* J, int b, int h, int t0, int t1,
-                          double* o, double* lse, double* s)
+                          double* o, double* lse, double* s, double* row)
 {
     int D = J->D, G = J->Hq / J->Hkv, g = h / G;
     int64_t row0 = ((int64_t)b * J->Hkv + g) * J->capacity;
     for (int i = 0; i < D; ++i) o[i] = 0.0;
     if (t1 <= t0) { *lse = -INFINITY; return; }
     const uint16_t* qh = J->q + ((int64_t)b * J->Hq + h) * D;
+    double* qd = row + D;
+    for (int i = 0; i < D; ++i) qd[i] = kvo_f16_value(qh[i]);
     double m = -INFINITY;
     for (int t = t0; t < t1; ++t) {
+        deq_row(J->tK, J->k_data, J->k_scales, row0 + t, D, row);
         double acc = 0.0;
-        for (int i = 0; i < D; ++i)
-            acc += kvo_f16_value(qh[i]) * deq(J->tK, J->k_data, J->k_scales, row0 + t, D, i);
+        for (int i = 0; i < D; ++i) acc += qd[i] * row[i];
         s[t - t0] = J->scale * acc;
         if (s[t - t0] > m) m = s[t - t0];
     }
@@ -288,8 +297,8 @@ static void attend_region(const attn_job* J, int b, int h, int t0, int t1,
     for (int t = t0; t < t1; ++t) {
         double p = exp(s[t - t0] - m);
         l += p;
-        for (int i = 0; i < D; ++i)
-            o[i] += p * deq(J->tV, J->v_data, J->v_scales, row0 + t, D, i);
+        deq_row(J->tV, J->v_data, J->v_scales, row0 + t, D, row);
+        for (int i = 0; i < D; ++i) o[i] += p * row[i];
     }
     for (int i = 0; i < D; ++i) o[i] /= l;
     *lse = m + log(l);
@@ -302,6 +311,7 @@ static void* attn_worker(void* arg)
     int64_t maxL = 0;
     for (int b = 0; b < J->B; ++b) if (J->seq_lens[b] > maxL) maxL = J->seq_lens[b];
     double* s = (double*)malloc(sizeof(double) * (size_t)(maxL > 0 ? maxL : 1));
+    double* row = (double*)malloc(sizeof(double) * 2 * (size_t)J->D);
     for (;;) {
         pthread_mutex_lock(&J->lock);
         int64_t it = J->next_item++;
@@ -310,7 +320,7 @@ static void* attn_worker(void* arg)
         int b = (int)(it / J->Hq), h = (int)(it % J->Hq);
         int L = J->seq_lens[b];
         if (J->split_tokens <= 0) {
-            attend_region(J, b, h, 0, L, J->out + it * J->D, J->lse + it, s);
+            attend_region(J, b, h, 0, L, J->out + it * J->D, J->lse + it, s, row);
         } else {
             for (int sp = 0; sp < J->max_splits; ++sp) {
                 int t0 = sp * J->split_tokens;
@@ -318,11 +328,12 @@ static void* attn_worker(void* arg)
                 if (t0 > L) t0 = L;
                 if (t1 > L) t1 = L;
                 int64_t k = it * J->max_splits + sp;
-                attend_region(J, b, h, t0, t1, J->out + k * J->D, J->lse + k, s);
+                attend_region(J, b, h, t0, t1, J->out + k * J->D, J->lse + k, s, row);
             }
         }
     }
     free(s);
+    free(row);
     return NULL;
 }
 

@@ -1,0 +1,164 @@
+"""ctypes binding of the C ABI in include/kvq.h (argument marshalling only).
+
+Every function here has the name of the C entry point it calls and does
+nothing but check and convert arguments: torch tensors become device pointers,
+``stream=None`` becomes torch's current HIP stream.  All computation happens in
+the HIP kernels of ``libkvq.so``.  If the library is missing, every call raises
+``KVQLibraryMissing``; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkvq.so")
+
+F16, Q8_0, Q4_0 = 0, 1, 2
+OUT_F32 = 3
+TYPES = {"f16": F16, "q8_0": Q8_0, "q4_0": Q4_0}
+VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
+VARIANTS = {"auto": VARIANT_AUTO, "valu": VARIANT_VALU, "mfma": VARIANT_MFMA}
+SPLIT_GRANULE = 64
+STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_NULL", -2: "KVQ_ERR_SHAPE", -3: "KVQ_ERR_TYPE",
+          -4: "KVQ_ERR_ALIGN", -5: "KVQ_ERR_CAPACITY", -6: "KVQ_ERR_SPLITS", -7: "KVQ_ERR_LAUNCH"}
+
+
+class KVQLibraryMissing(RuntimeError):
+    pass
+
+
+class KVQError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class kvq_plane_desc(ctypes.Structure):
+    _fields_ = [
+        ("type", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("data", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("seq_stride_rows", ctypes.c_int64),
+        ("head_stride_rows", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libkvq.so (built by ``quantised_kv_long_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    # Bind to the HIP runtime torch has loaded (one runtime per process: the
+    # library's libamdhip64.so.7 dependency resolves to the copy already loaded),
+    # so torch's streams and events are valid handles for the library.
+    import torch  # noqa: F401
+    if not os.path.exists(path):
+        raise KVQLibraryMissing(
+            f"{path} is not built; run `python -m quantised_kv_long_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    P, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    DP = ctypes.POINTER(kvq_plane_desc)
+    lib.kvq_data_row_bytes.argtypes = [i32, i32]
+    lib.kvq_data_row_bytes.restype = ctypes.c_size_t
+    lib.kvq_scale_row_bytes.argtypes = [i32, i32]
+    lib.kvq_scale_row_bytes.restype = ctypes.c_size_t
+    lib.kvq_status_string.argtypes = [i32]
+    lib.kvq_status_string.restype = ctypes.c_char_p
+    lib.kvq_quantize_append.argtypes = [DP, DP, P, P, P, i32, i32, i32, i32, i32, P]
+    lib.kvq_quantize_append.restype = i32
+    lib.kvq_decode_attn.argtypes = [DP, DP, P, P, i32, i32, i32, i32, f32, i32, i32, i32, P, P, P]
+    lib.kvq_decode_attn.restype = i32
+    lib.kvq_decode_attn_variant.argtypes = [DP, DP, P, P, i32, i32, i32, i32, f32, i32, i32, i32,
+                                            P, P, i32, P]
+    lib.kvq_decode_attn_variant.restype = i32
+    lib.kvq_combine.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, P, P, P]
+    lib.kvq_combine.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, rc: int) -> int:
+    if rc != 0:
+        raise KVQError(fn, rc, load().kvq_status_string(rc).decode())
+    return rc
+
+
+def _ptr(x) -> int | None:
+    """A torch tensor (must be on a GPU and contiguous), an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not x.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _tcode(t) -> int:
+    return TYPES[t] if isinstance(t, str) else int(t)
+
+
+def kvq_data_row_bytes(t, head_dim: int) -> int:
+    return int(load().kvq_data_row_bytes(_tcode(t), head_dim))
+
+
+def kvq_scale_row_bytes(t, head_dim: int) -> int:
+    return int(load().kvq_scale_row_bytes(_tcode(t), head_dim))
+
+
+def kvq_status_string(status: int) -> str:
+    return load().kvq_status_string(status).decode()
+
+
+def kvq_quantize_append(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, k_new, v_new, positions,
+                        B: int, n_new: int, Hkv: int, D: int, max_end: int, stream=None) -> int:
+    rc = load().kvq_quantize_append(ctypes.byref(k_cache), ctypes.byref(v_cache), _ptr(k_new),
+                                    _ptr(v_new), _ptr(positions), B, n_new, Hkv, D, max_end,
+                                    _stream(stream))
+    return _check("kvq_quantize_append", rc)
+
+
+def kvq_decode_attn(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, q, seq_lens, B: int, Hq: int,
+                    Hkv: int, D: int, softmax_scale: float, max_seq_len: int, split_tokens: int,
+                    max_splits: int, part_o, part_lse, stream=None) -> int:
+    rc = load().kvq_decode_attn(ctypes.byref(k_cache), ctypes.byref(v_cache), _ptr(q),
+                                _ptr(seq_lens), B, Hq, Hkv, D, float(softmax_scale), max_seq_len,
+                                split_tokens, max_splits, _ptr(part_o), _ptr(part_lse),
+                                _stream(stream))
+    return _check("kvq_decode_attn", rc)
+
+
+def kvq_decode_attn_variant(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, q, seq_lens, B: int,
+                            Hq: int, Hkv: int, D: int, softmax_scale: float, max_seq_len: int,
+                            split_tokens: int, max_splits: int, part_o, part_lse, variant,
+                            stream=None) -> int:
+    v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+    rc = load().kvq_decode_attn_variant(ctypes.byref(k_cache), ctypes.byref(v_cache), _ptr(q),
+                                        _ptr(seq_lens), B, Hq, Hkv, D, float(softmax_scale),
+                                        max_seq_len, split_tokens, max_splits, _ptr(part_o),
+                                        _ptr(part_lse), v, _stream(stream))
+    return _check("kvq_decode_attn_variant", rc)
+
+
+def kvq_combine(part_o, part_lse, seq_lens, B: int, Hq: int, D: int, split_tokens: int,
+                max_splits: int, out_type, out, lse_out=None, stream=None) -> int:
+    ot = OUT_F32 if out_type in ("f32", OUT_F32) else _tcode(out_type)
+    rc = load().kvq_combine(_ptr(part_o), _ptr(part_lse), _ptr(seq_lens), B, Hq, D, split_tokens,
+                            max_splits, ot, _ptr(out), _ptr(lse_out), _stream(stream))
+    return _check("kvq_combine", rc)

@@ -1,0 +1,58 @@
+"""Build the HIP library ``libkvq.so`` in-tree for gfx950.
+
+Usage: ``python -m quantised_kv_long_amd.build`` (or ``build()`` from Python).
+Every source under ``csrc/`` is compiled by hipcc in one invocation.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libkvq.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    # code object v5: loadable by the HIP runtime that ships with torch as well
+    # as by the system one
+    "-mcode-object-version=5",
+    # never emit packed-fp32 VALU instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # binary32 division and square root stay correctly rounded (the quantiser
+    # depends on it); this is hipcc's default, stated explicitly
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-fno-fast-math",
+]
+
+
+def sources() -> list[str]:
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+
+
+def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
+    cmd = [HIPCC, *HIP_FLAGS, *(extra or []), f"-I{INCLUDE}", f"-I{CSRC}", *sources(), "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
+    if err.strip() and verbose:
+        print(err, file=sys.stderr)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,87 @@
+"""Device memory for the KV cache planes and the split partials, allocated with
+torch, and the plane descriptors the C ABI takes.  No computation happens
+here: every step of the decode path runs in the library's HIP kernels.
+
+Layout (matches kvq_plane_desc): for cache tensor X of one layer,
+    data   : uint8  [B, Hkv, capacity, data_row_bytes(type, D)]
+    scales : int16  [B, Hkv, capacity, D / 32]      (absent for f16)
+so row t of KV head g of sequence b is row (b * Hkv + g) * capacity + t.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+
+@dataclass
+class CachePlanes:
+    type: int
+    B: int
+    Hkv: int
+    capacity: int
+    D: int
+    data: torch.Tensor
+    scales: torch.Tensor | None
+
+    @classmethod
+    def alloc(cls, t, B: int, Hkv: int, capacity: int, D: int, device="cuda") -> "CachePlanes":
+        t = _lib._tcode(t)
+        rb = _lib.kvq_data_row_bytes(t, D)
+        if rb == 0:
+            raise ValueError(f"unsupported type/head_dim {t}/{D}")
+        data = torch.empty((B, Hkv, capacity, rb), dtype=torch.uint8, device=device)
+        scales = None
+        if t != _lib.F16:
+            scales = torch.empty((B, Hkv, capacity, D // 32), dtype=torch.int16, device=device)
+        return cls(t, B, Hkv, capacity, D, data, scales)
+
+    def desc(self) -> _lib.kvq_plane_desc:
+        return _lib.kvq_plane_desc(
+            self.type, self.capacity, self.data.data_ptr(),
+            self.scales.data_ptr() if self.scales is not None else None,
+            self.Hkv * self.capacity, self.capacity)
+
+    def stored_bytes(self, lengths) -> int:
+        """Bytes of the rows [0, L_b) of every (b, head): the algorithmic bytes a
+        decode pass over this tensor reads."""
+        per_row = _lib.kvq_data_row_bytes(self.type, self.D) + _lib.kvq_scale_row_bytes(self.type, self.D)
+        return int(sum(lengths)) * self.Hkv * per_row
+
+
+class Partials:
+    """Split partial buffers for kvq_decode_attn / kvq_combine."""
+
+    def __init__(self, B: int, Hq: int, D: int, max_seq_len: int, split_tokens: int, device="cuda"):
+        self.split_tokens = split_tokens
+        self.max_splits = max(1, math.ceil(max_seq_len / split_tokens))
+        self.o = torch.empty((B, Hq, self.max_splits, D), dtype=torch.float32, device=device)
+        self.lse = torch.empty((B, Hq, self.max_splits), dtype=torch.float32, device=device)
+
+
+def append(kc: CachePlanes, vc: CachePlanes, k_new: torch.Tensor, v_new: torch.Tensor,
+           positions: torch.Tensor, max_end: int, stream=None):
+    """kvq_quantize_append on torch tensors: k_new, v_new (B, n_new, Hkv, D) fp16."""
+    B, n_new, Hkv, D = k_new.shape
+    return _lib.kvq_quantize_append(kc.desc(), vc.desc(), k_new, v_new, positions, B, n_new, Hkv,
+                                    D, max_end, stream)
+
+
+def decode(kc: CachePlanes, vc: CachePlanes, q: torch.Tensor, seq_lens: torch.Tensor,
+           max_seq_len: int, part: Partials, softmax_scale: float, variant="auto", stream=None):
+    """kvq_decode_attn_variant on torch tensors: q (B, Hq, D) fp16."""
+    B, Hq, D = q.shape
+    return _lib.kvq_decode_attn_variant(kc.desc(), vc.desc(), q, seq_lens, B, Hq, kc.Hkv, D,
+                                        softmax_scale, max_seq_len, part.split_tokens,
+                                        part.max_splits, part.o, part.lse, variant, stream)
+
+
+def combine(part: Partials, seq_lens: torch.Tensor, out: torch.Tensor, lse_out=None, stream=None):
+    """kvq_combine into ``out`` (B, Hq, D) fp16 or fp32."""
+    B, Hq, D = out.shape
+    ot = "f16" if out.dtype == torch.float16 else "f32"
+    return _lib.kvq_combine(part.o, part.lse, seq_lens, B, Hq, D, part.split_tokens,
+                            part.max_splits, ot, out, lse_out, stream)

@@ -1,0 +1,50 @@
+// kvq_internal.hpp -- host-side interface between the C ABI layer (argument
+// validation, kvq_api.cpp) and the kernel launchers (*.hip).  Every launcher
+// assumes its arguments were validated and only enqueues kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_device.hpp"
+
+namespace kvq {
+
+struct AppendArgs {
+    Plane k, v;
+    int tk, tv;
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    const int32_t* positions;
+    int B, n_new, Hkv, D;
+};
+
+struct DecodeArgs {
+    Plane k, v;
+    int tk, tv;
+    const uint16_t* q;
+    const int32_t* seq_lens;
+    int B, Hq, Hkv, D, G;
+    float scale_log2;  // softmax scale * log2(e)
+    int max_seq_len, split_tokens, max_splits;
+    float* part_o;
+    float* part_lse;
+};
+
+struct CombineArgs {
+    const float* part_o;
+    const float* part_lse;
+    const int32_t* seq_lens;
+    int B, Hq, D, split_tokens, max_splits;
+    bool out_f16;
+    void* out;
+    float* lse_out;
+};
+
+hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
+bool decode_mfma_supports(const DecodeArgs& a);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace kvq

@@ -1,0 +1,193 @@
+"""The C-ABI library on the host, no GPU: it builds, loads, exports every entry
+point include/kvq.h declares, reproduces the pages' byte counts, and rejects
+every invalid argument with the documented status before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+from quantised_kv_long_amd import _lib  # noqa: E402
+from quantised_kv_long_amd import build as B  # noqa: E402
+
+from .test_page_sizes import ROWS, UNIT  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def lib():
+    srcs = B.sources()
+    if not os.path.exists(B.LIB) or os.path.getmtime(B.LIB) < max(os.path.getmtime(s) for s in srcs):
+        B.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kvq_quantize_append", "kvq_decode_attn", "kvq_combine", "kvq_decode_attn_variant",
+              "kvq_data_row_bytes", "kvq_scale_row_bytes", "kvq_status_string"):
+        assert n in names
+
+
+def test_every_declared_function_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in kvq.h but not exported"
+
+
+def test_status_strings(lib):
+    for code in range(-7, 1):
+        assert _lib.kvq_status_string(code) != "unknown status"
+    assert _lib.kvq_status_string(5) == "unknown status"
+
+
+def test_row_bytes(lib):
+    for D in (32, 64, 128, 256, 512):
+        assert _lib.kvq_data_row_bytes("f16", D) == 2 * D
+        assert _lib.kvq_data_row_bytes("q8_0", D) == D
+        assert _lib.kvq_data_row_bytes("q4_0", D) == D // 2
+        assert _lib.kvq_scale_row_bytes("f16", D) == 0
+        assert _lib.kvq_scale_row_bytes("q8_0", D) == D // 16
+        assert _lib.kvq_scale_row_bytes("q4_0", D) == D // 16
+    assert _lib.kvq_data_row_bytes("q8_0", 48) == 0
+    assert _lib.kvq_data_row_bytes(7, 128) == 0
+
+
+@pytest.mark.parametrize("layers,heads,D,tK,tV,tokens,value,unit,cite", ROWS,
+                         ids=[f"{r[3]}-{r[4]}-{r[5]}-{r[2]}" for r in ROWS])
+def test_library_sizes_reproduce_page_figures(lib, layers, heads, D, tK, tV, tokens, value, unit,
+                                              cite):
+    per_row = lambda t: _lib.kvq_data_row_bytes(t, D) + _lib.kvq_scale_row_bytes(t, D)
+    total = layers * heads * tokens * (per_row(tK) + per_row(tV))
+    assert total / UNIT[unit] == pytest.approx(value, rel=1e-12), cite
+
+
+# ------------------------------------------------------------- validation
+# Fake, well-aligned device addresses: every call below must fail validation,
+# which happens before any HIP call.  The fake addresses are never dereferenced;
+# to stay safe even if validation had a bug, these tests run only where no GPU
+# is visible.
+
+def _no_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+nogpu = pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation tests run only without a GPU")
+A = 0x10000  # aligned fake address
+
+
+def plane(t=2, cap=100, data=A, scales=A + 0x100000, seq=800, head=100):
+    return _lib.kvq_plane_desc(t, cap, data, scales, seq, head)
+
+
+def append(lib, k=None, v=None, kn=A, vn=A, pos=A, B=2, n=1, H=8, D=128, max_end=100):
+    k = k if k is not None else plane()
+    v = v if v is not None else plane()
+    kp = ctypes.byref(k) if k is not False else None
+    vp = ctypes.byref(v) if v is not False else None
+    return lib.kvq_quantize_append(kp, vp, kn, vn, pos, B, n, H, D, max_end, None)
+
+
+@nogpu
+def test_append_validation(lib):
+    assert append(lib, kn=None) == -1
+    assert append(lib, pos=None) == -1
+    assert append(lib, k=False) == -1
+    assert append(lib, k=plane(t=2, scales=None)) == -1        # quant type needs a scale plane
+    assert append(lib, k=plane(data=None)) == -1
+    assert append(lib, B=-1) == -2
+    assert append(lib, n=-1) == -2
+    assert append(lib, H=0) == -2
+    assert append(lib, D=48) == -2
+    assert append(lib, D=544) == -2
+    assert append(lib, D=0) == -2
+    assert append(lib, k=plane(t=3)) == -3
+    assert append(lib, v=plane(t=-1)) == -3
+    assert append(lib, k=plane(data=A + 8)) == -4
+    assert append(lib, v=plane(scales=A + 2)) == -4
+    assert append(lib, kn=A + 2) == -4
+    assert append(lib, pos=A + 2) == -4
+    assert append(lib, max_end=101) == -5
+    assert append(lib, v=plane(cap=50), max_end=60) == -5
+    assert append(lib, k=plane(seq=0)) == -2                   # B > 1 with a zero sequence stride
+    assert append(lib, k=plane(head=0)) == -2
+    assert append(lib, max_end=0, n=1) == -2                    # max_end < n_new
+    # nothing to do: returns OK without touching the device
+    assert append(lib, B=0) == 0
+    assert append(lib, n=0, max_end=0) == 0
+
+
+def decode(lib, k=None, v=None, q=A, lens=A, B=1, Hq=40, Hkv=8, D=128, scale=0.088, max_len=100,
+           split=64, max_splits=2, po=A, pl=A, variant=None):
+    k = k if k is not None else plane()
+    v = v if v is not None else plane()
+    args = (ctypes.byref(k), ctypes.byref(v), q, lens, B, Hq, Hkv, D, scale, max_len, split,
+            max_splits, po, pl)
+    if variant is None:
+        return lib.kvq_decode_attn(*args, None)
+    return lib.kvq_decode_attn_variant(*args, variant, None)
+
+
+@nogpu
+def test_decode_validation(lib):
+    assert decode(lib, q=None) == -1
+    assert decode(lib, lens=None) == -1
+    assert decode(lib, po=None) == -1
+    assert decode(lib, pl=None) == -1
+    assert decode(lib, k=plane(scales=None)) == -1
+    assert decode(lib, Hq=41) == -2                             # Hq % Hkv != 0
+    assert decode(lib, Hq=8 * 17) == -2                         # group of 17 > 16
+    assert decode(lib, B=0) == -2
+    assert decode(lib, D=96 + 8) == -2
+    assert decode(lib, D=1024) == -2
+    assert decode(lib, scale=float("nan")) == -2
+    assert decode(lib, max_len=0) == -2
+    assert decode(lib, k=plane(t=5)) == -3
+    assert decode(lib, variant=3) == -3
+    assert decode(lib, q=A + 4) == -4
+    assert decode(lib, po=A + 4) == -4
+    assert decode(lib, max_len=101) == -5
+    assert decode(lib, v=plane(cap=99)) == -5
+    assert decode(lib, split=100) == -6                         # not a multiple of 64
+    assert decode(lib, split=0) == -6
+    assert decode(lib, max_splits=1) == -6                      # 1 * 64 < 100
+    assert decode(lib, max_splits=0) == -6
+
+
+def combine(lib, po=A, pl=A, lens=A, B=1, Hq=40, D=128, split=64, max_splits=4, ot=3, out=A,
+            lse=None):
+    return lib.kvq_combine(po, pl, lens, B, Hq, D, split, max_splits, ot, out, lse, None)
+
+
+@nogpu
+def test_combine_validation(lib):
+    assert combine(lib, po=None) == -1
+    assert combine(lib, out=None) == -1
+    assert combine(lib, lens=None) == -1
+    assert combine(lib, ot=1) == -3
+    assert combine(lib, ot=2) == -3
+    assert combine(lib, B=0) == -2
+    assert combine(lib, D=40) == -2
+    assert combine(lib, split=32) == -6
+    assert combine(lib, max_splits=0) == -6
+    assert combine(lib, po=A + 8) == -4
+    assert combine(lib, out=A + 1, ot=0) == -4
+    assert combine(lib, lse=A + 2) == -4
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """The product path has no fallback: a missing library raises."""
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.KVQLibraryMissing):
+        _lib.load(str(tmp_path / "libkvq.so"))

@@ -1,0 +1,158 @@
+"""K1 (kvq_quantize_append) on the GPU against the CPU oracle: bit-exact data
+and scale planes, untouched rows left alone."""
+import itertools
+import os
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+
+from .gpu_util import note, require_gpu, to_host_u16
+from .test_oracle_quant import WORKED
+
+torch = pytest.importorskip("torch")
+from quantised_kv_long_amd import cache as C  # noqa: E402
+from quantised_kv_long_amd import synth  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+TYPES = ["f16", "q8_0", "q4_0"]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def sentinel_planes(t, B, Hkv, cap, D):
+    p = C.CachePlanes.alloc(t, B, Hkv, cap, D)
+    p.data.fill_(0xA5)
+    if p.scales is not None:
+        p.scales.fill_(0x5A5A)
+    return p
+
+
+def expected_planes(t, x_host, positions, B, Hkv, cap, D):
+    """Sentinel planes with the oracle's rows written at positions[b] + r."""
+    rb = O.data_row_bytes(t, D)
+    data = np.full((B, Hkv, cap, rb), 0xA5, np.uint8)
+    sc = np.full((B, Hkv, cap, D // 32), 0x5A5A, np.uint16)
+    qd, qs = O.quantize(t, x_host)  # (B, n_new, Hkv, rb), (B, n_new, Hkv, nb)
+    n_new = x_host.shape[1]
+    for b in range(B):
+        p0 = positions[b]
+        data[b, :, p0:p0 + n_new] = qd[b].transpose(1, 0, 2)
+        if t != "f16":
+            sc[b, :, p0:p0 + n_new] = qs[b].transpose(1, 0, 2)
+    return data, sc
+
+
+def structured_rows(shape, seed, dev):
+    """N(0,1) rows, with some rows scaled tiny (subnormal scales), some huge,
+    some all-zero, and some holding exact rounding ties."""
+    x = synth.normal_f16(shape, seed, dev).float()
+    B, n, H, D = shape
+    x[:, ::7] *= 1e-5
+    x[:, 1::7] *= 2000.0
+    x[:, 2::7] = 0.0
+    ties = torch.randint(-20, 20, x[:, 3::7].shape, device=dev).float() / 8.0
+    x[:, 3::7] = ties
+    return x.half()
+
+
+@pytest.mark.parametrize("tk,tv", list(itertools.product(TYPES, TYPES)))
+def test_append_bit_exact_ragged_positions(tk, tv):
+    dev = "cuda"
+    B, n_new, Hkv, D, cap = 3, 37, 2, 128, 160
+    positions = [0, 5, 123]
+    note(f"append {tk}/{tv} B={B} n_new={n_new} D={D}")
+    k = structured_rows((B, n_new, Hkv, D), 11, dev)
+    v = structured_rows((B, n_new, Hkv, D), 12, dev)
+    kc = sentinel_planes(tk, B, Hkv, cap, D)
+    vc = sentinel_planes(tv, B, Hkv, cap, D)
+    pos = torch.tensor(positions, dtype=torch.int32, device=dev)
+    C.append(kc, vc, k, v, pos, max(positions) + n_new)
+    torch.cuda.synchronize()
+    for t, planes, x in ((tk, kc, k), (tv, vc, v)):
+        want_d, want_s = expected_planes(t, to_host_u16(x), positions, B, Hkv, cap, D)
+        got_d = planes.data.cpu().numpy()
+        assert np.array_equal(got_d, want_d), f"{t} data plane differs"
+        if t != "f16":
+            got_s = planes.scales.cpu().numpy().view(np.uint16)
+            assert np.array_equal(got_s, want_s), f"{t} scale plane differs"
+
+
+@pytest.mark.parametrize("t", ["q8_0", "q4_0"])
+def test_append_every_finite_f16_value(t):
+    """All 63488 finite binary16 values, in 8 seeded shuffles, through K1."""
+    dev = "cuda"
+    note(f"append every f16 value {t}")
+    pos = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16)
+    vals = np.concatenate([pos, pos | 0x8000])
+    rng = np.random.default_rng(99)
+    allv = np.concatenate([rng.permutation(vals) for _ in range(8)])
+    D = 128
+    rows = allv.reshape(1, -1, 1, D)
+    x = torch.from_numpy(rows.view(np.int16)).to(dev).view(torch.float16)
+    n_new = rows.shape[1]
+    kc = sentinel_planes(t, 1, 1, n_new, D)
+    vc = sentinel_planes("f16", 1, 1, n_new, D)
+    C.append(kc, vc, x, x, torch.zeros(1, dtype=torch.int32, device=dev), n_new)
+    torch.cuda.synchronize()
+    want_d, want_s = O.quantize(t, rows[0, :, 0])
+    assert np.array_equal(kc.data[0, 0].cpu().numpy(), want_d)
+    assert np.array_equal(kc.scales[0, 0].cpu().numpy().view(np.uint16), want_s)
+    # and the f16 type copies the bits
+    assert np.array_equal(vc.data[0, 0].cpu().numpy().view(np.uint16), rows[0, :, 0])
+
+
+def test_append_worked_blocks():
+    dev = "cuda"
+    note("append worked blocks")
+    for t in ("q8_0", "q4_0"):
+        blocks = [x for _, tt, x, _, _ in WORKED if tt == t]
+        want = [(s, d) for _, tt, _, s, d in WORKED if tt == t]
+        rows = np.stack(blocks).reshape(1, len(blocks), 1, 32)
+        x = torch.from_numpy(rows.view(np.int16)).to(dev).view(torch.float16)
+        kc = sentinel_planes(t, 1, 1, len(blocks), 32)
+        C.append(kc, kc, x, x, torch.zeros(1, dtype=torch.int32, device=dev), len(blocks))
+        torch.cuda.synchronize()
+        got_d = kc.data[0, 0].cpu().numpy()
+        got_s = kc.scales[0, 0].cpu().numpy().view(np.uint16)
+        for i, (s, d) in enumerate(want):
+            assert int(got_s[i, 0]) == s and got_d[i].tobytes() == d, f"{t} block {i}"
+
+
+def test_append_zero_rows_is_a_no_op():
+    dev = "cuda"
+    kc = sentinel_planes("q4_0", 1, 1, 64, 64)
+    x = torch.zeros((1, 0, 1, 64), dtype=torch.float16, device=dev)
+    C.append(kc, kc, x, x, torch.zeros(1, dtype=torch.int32, device=dev), 0)
+    torch.cuda.synchronize()
+    assert bool((kc.data == 0xA5).all())
+
+
+@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0")])
+def test_append_full_long_context_sampled_rows(tk, tv):
+    """262144-row prefill of 8 KV heads x head_dim 128 in one call (the long
+    context workload's cache build); 4096 sampled rows per tensor checked
+    bit-exactly against the oracle."""
+    dev = "cuda"
+    wl = synth.WORKLOADS["long_d128_ctx256k"]
+    L, Hkv, D = wl.ctx, wl.Hkv, wl.D
+    note(f"append full {wl.name} {tk}/{tv}")
+    k = synth.normal_f16((1, L, Hkv, D), synth.seed_for(wl.seed, 0, "k"), dev)
+    v = synth.normal_f16((1, L, Hkv, D), synth.seed_for(wl.seed, 0, "v"), dev)
+    kc = C.CachePlanes.alloc(tk, 1, Hkv, L, D)
+    vc = C.CachePlanes.alloc(tv, 1, Hkv, L, D)
+    C.append(kc, vc, k, v, torch.zeros(1, dtype=torch.int32, device=dev), L)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, L - 2, L - 1], rng.integers(0, L, 4092)]))
+    ridx = torch.from_numpy(rows).to(dev)
+    for t, planes, x in ((tk, kc, k), (tv, vc, v)):
+        xs = to_host_u16(x[0, ridx])  # (n, Hkv, D)
+        want_d, want_s = O.quantize(t, xs)
+        got_d = planes.data[0][:, ridx].permute(1, 0, 2).cpu().numpy()
+        got_s = planes.scales[0][:, ridx].permute(1, 0, 2).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got_d, want_d) and np.array_equal(got_s, want_s)
