@@ -124,7 +124,8 @@ const char* kvq_status_string(int status);
  *   max_end          : host, max over b of positions[b] + n_new; must not
  *                      exceed either cache's capacity (KVQ_ERR_CAPACITY).
  *   Requirements: B >= 0, n_new >= 0, Hkv >= 1, D % 32 == 0, 32 <= D <= 512.
- *   B == 0 or n_new == 0 enqueues nothing and returns KVQ_OK.
+ *   B == 0 or n_new == 0 (with valid Hkv and D) enqueues nothing and returns
+ *   KVQ_OK without looking at any pointer.
  */
 int kvq_quantize_append(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache,
                         const void* k_new, const void* v_new, const int32_t* positions,
@@ -189,7 +190,7 @@ int kvq_decode_attn_variant(const kvq_plane_desc* k_cache, const kvq_plane_desc*
  *   part_o, part_lse : device, as written by kvq_decode_attn.
  *   seq_lens         : device, [B] int32 (the same lengths).
  *   out_type         : KVQ_F16 or a value of 3 for fp32 (KVQ_OUT_F32).
- *   out              : device, [B][Hq][D] of out_type.
+ *   out              : device, [B][Hq][D] of out_type, 16-byte aligned.
  *   lse_out          : device, [B][Hq] fp32, or NULL.
  */
 #define KVQ_OUT_F32 3

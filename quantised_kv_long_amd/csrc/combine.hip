@@ -5,8 +5,10 @@
 // One workgroup (256 threads) per (sequence, query head).  fp32 throughout:
 //   LSE = m + ln sum_s exp(lse_s - m),  m = max_s lse_s
 //   out = sum_s exp(lse_s - LSE) * o_s
-// The weights are staged in LDS in chunks; threads stride over the D columns
-// (coalesced reads of each partial row) and over splits when D < 256.
+// The weights go to LDS; then each thread owns four adjacent columns (one
+// 16-byte load per split row) and a residue class of splits, with UNROLL
+// independent loads in flight so the pass costs about one memory round trip
+// rather than one per split.  The split groups are summed through LDS.
 #include <math.h>
 
 #include "kvq_internal.hpp"
@@ -15,7 +17,8 @@ namespace kvq {
 namespace {
 
 constexpr int NT = 256;
-constexpr int WCHUNK = 1024;
+constexpr int WCHUNK = 4096;
+constexpr int UNROLL = 8;
 
 __device__ float block_reduce(float v, bool is_max, float* tmp)
 {
@@ -38,11 +41,11 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a)
     const int S = L > 0 ? min((L + a.split_tokens - 1) / a.split_tokens, a.max_splits) : 0;
     const int64_t bh = (int64_t)b * a.Hq + h;
     const float* pl = a.part_lse + bh * a.max_splits;
-    const float* po = a.part_o + bh * a.max_splits * D;
+    const float4* po = reinterpret_cast<const float4*>(a.part_o + bh * a.max_splits * D);
 
     __shared__ float tmp[NT / 64];
     __shared__ float w[WCHUNK];
-    __shared__ float red[NT * 2];
+    __shared__ float4 red[NT];
 
     float m = -INFINITY;
     for (int s = tid; s < S; s += NT) m = fmaxf(m, pl[s]);
@@ -56,12 +59,11 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a)
         lse = m + logf(sum);
     }
 
-    const int nd = D < NT ? D : NT;       // threads per split row
-    const int R = NT / nd;                // splits processed side by side
-    const int dd = tid % nd, rr = tid / nd;
-    const bool on = rr < R;
-    constexpr int MAXD_PER_THREAD = 2;    // D <= 512
-    float acc[MAXD_PER_THREAD] = {0.0f, 0.0f};
+    const int D4 = D >> 2;                 // float4 columns (D <= 512: at most 128)
+    const int R = NT / D4;                 // split residue classes
+    const int c = tid % D4, r = tid / D4;
+    const bool on = r < R;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 
     if (lse != -INFINITY) {
         for (int c0 = 0; c0 < S; c0 += WCHUNK) {
@@ -70,32 +72,52 @@ __global__ void __launch_bounds__(NT) combine_kernel(CombineArgs a)
             for (int i = tid; i < n; i += NT) w[i] = expf(pl[c0 + i] - lse);
             __syncthreads();
             if (on) {
-                for (int i = rr; i < n; i += R) {
-                    const float wi = w[i];
-                    const float* row = po + (int64_t)(c0 + i) * D;
+                for (int i0 = r; i0 < n; i0 += R * UNROLL) {
+                    float4 v[UNROLL];
+                    float wi[UNROLL];
 #pragma unroll
-                    for (int k = 0; k < MAXD_PER_THREAD; ++k) {
-                        const int d = dd + k * nd;
-                        if (d < D) acc[k] += wi * row[d];
+                    for (int u = 0; u < UNROLL; ++u) {
+                        const int i = i0 + u * R;
+                        if (i < n) {
+                            v[u] = po[(int64_t)(c0 + i) * D4 + c];
+                            wi[u] = w[i];
+                        } else {
+                            v[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                            wi[u] = 0.0f;
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < UNROLL; ++u) {
+                        acc.x += wi[u] * v[u].x;
+                        acc.y += wi[u] * v[u].y;
+                        acc.z += wi[u] * v[u].z;
+                        acc.w += wi[u] * v[u].w;
                     }
                 }
             }
         }
     }
 
-    // sum the R split groups (each thread holds up to 2 columns)
-    for (int k = 0; k < MAXD_PER_THREAD; ++k) {
-        __syncthreads();
-        if (on) red[rr * nd + dd] = acc[k];
-        __syncthreads();
-        const int d = tid + k * nd;
-        if (tid < nd && d < D) {
-            float v = 0.0f;
-            for (int r = 0; r < R; ++r) v += red[r * nd + tid];
-            if (a.out_f16)
-                reinterpret_cast<uint16_t*>(a.out)[bh * D + d] = f2h_rne(v);
-            else
-                reinterpret_cast<float*>(a.out)[bh * D + d] = v;
+    __syncthreads();
+    if (on) red[r * D4 + c] = acc;
+    __syncthreads();
+    if (tid < D4) {
+        float4 v = red[tid];
+        for (int k = 1; k < R; ++k) {
+            const float4 u = red[k * D4 + tid];
+            v.x += u.x;
+            v.y += u.y;
+            v.z += u.z;
+            v.w += u.w;
+        }
+        if (a.out_f16) {
+            uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + bh * D + 4 * tid;
+            o[0] = f2h_rne(v.x);
+            o[1] = f2h_rne(v.y);
+            o[2] = f2h_rne(v.z);
+            o[3] = f2h_rne(v.w);
+        } else {
+            reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + bh * D)[tid] = v;
         }
     }
     if (tid == 0 && a.lse_out) a.lse_out[bh] = lse;

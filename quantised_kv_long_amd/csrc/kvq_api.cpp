@@ -124,8 +124,9 @@ int kvq_quantize_append(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_c
                         const void* k_new, const void* v_new, const int32_t* positions, int B,
                         int n_new, int Hkv, int D, int max_end, void* stream)
 {
-    if (!k_new || !v_new || !positions) return KVQ_ERR_NULL;
     if (B < 0 || n_new < 0 || Hkv < 1 || !valid_head_dim(D)) return KVQ_ERR_SHAPE;
+    if (B == 0 || n_new == 0) return KVQ_OK;  // nothing to write (pointers may be NULL)
+    if (!k_new || !v_new || !positions) return KVQ_ERR_NULL;
     if (max_end < n_new) return KVQ_ERR_SHAPE;
     int rc = check_plane(k_cache, B, Hkv, max_end);
     if (rc != KVQ_OK) return rc;
@@ -134,7 +135,6 @@ int kvq_quantize_append(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_c
     if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(positions, 4)) return KVQ_ERR_ALIGN;
     const int64_t n_blocks = (int64_t)B * n_new * Hkv * (D / 32);
     if ((n_blocks + 255) / 256 > 0x7fffffffLL) return KVQ_ERR_SHAPE;
-    if (n_blocks == 0) return KVQ_OK;
 
     kvq::AppendArgs a;
     a.k = to_plane(k_cache);
@@ -193,7 +193,7 @@ int kvq_combine(const float* part_o, const float* part_lse, const int32_t* seq_l
     if (split_tokens < KVQ_SPLIT_GRANULE || split_tokens % KVQ_SPLIT_GRANULE != 0) return KVQ_ERR_SPLITS;
     if (max_splits < 1 || max_splits > 65535) return KVQ_ERR_SPLITS;
     if (!aligned(part_o, 16) || !aligned(part_lse, 4) || !aligned(seq_lens, 4) ||
-        !aligned(out, out_type == KVQ_F16 ? 2 : 4) || (lse_out && !aligned(lse_out, 4)))
+        !aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
         return KVQ_ERR_ALIGN;
     kvq::CombineArgs a;
     a.part_o = part_o;

@@ -68,7 +68,13 @@ __device__ __forceinline__ void quantize_block(const uint16_t* __restrict__ src,
                 const float a = fabsf(x[i]);
                 if (a > amax) { amax = a; smax = x[i]; }
             }
-            const uint16_t d16 = f2h_rne(smax / -8.0f);
+            // smax / -8 rounded to fp16.  Formed as magnitude and sign: the
+            // compiler otherwise fuses x * -0.125 and the fp16 conversion into a
+            // mixed-precision FMA with a +0 addend, which turns the -0 scale of
+            // an all-zero block into +0.  |smax| / 8 is exact in binary32 and
+            // round-to-nearest-even is symmetric, so the bits are identical.
+            const uint16_t mag16 = f2h_rne(fabsf(smax) * 0.125f);
+            const uint16_t d16 = (uint16_t)(mag16 | (smax < 0.0f ? 0 : 0x8000));
             const float d = h2f(d16);
             int n[32];
 #pragma unroll

@@ -126,6 +126,7 @@ def test_append_validation(lib):
     # nothing to do: returns OK without touching the device
     assert append(lib, B=0) == 0
     assert append(lib, n=0, max_end=0) == 0
+    assert append(lib, B=0, kn=None, vn=None, pos=None, k=False, v=False) == 0
 
 
 def decode(lib, k=None, v=None, q=A, lens=A, B=1, Hq=40, Hkv=8, D=128, scale=0.088, max_len=100,
@@ -183,6 +184,7 @@ def test_combine_validation(lib):
     assert combine(lib, max_splits=0) == -6
     assert combine(lib, po=A + 8) == -4
     assert combine(lib, out=A + 1, ot=0) == -4
+    assert combine(lib, out=A + 8, ot=3) == -4
     assert combine(lib, lse=A + 2) == -4
 
 
