@@ -1,10 +1,13 @@
 #!/usr/bin/env python3
 """Decode-attention benchmark over a block-quantised KV cache on one MI355X.
 
-One step = the whole hot path for every layer of the workload: quantise-append
-one new token per sequence (kvq_quantize_append), split-KV decode attention
-(kvq_decode_attn) and the log-sum-exp combine (kvq_combine), on inputs already
-resident in HBM.  The default workload is the 48-layer stack at 65536 rows
+One step = the whole hot path for every layer of the workload: quantise-on-write
+of one new token per sequence, split-KV decode attention over every row and
+the exact log-sum-exp combine, on inputs already resident in HBM.  The timed
+path is kvq_decode_step (one launch per layer where the matrix-core kernel
+covers the shape); the same step as three calls (kvq_quantize_append,
+kvq_decode_attn, kvq_combine) and the attention launch alone are timed beside
+it and reported per arm.  The default workload is the 48-layer stack at 65536 rows
 (40 query / 8 KV heads, head_dim 128) with the f16, q8_0K/q4_0V and q4_0/q4_0
 arms; the headline value is the q8_0K/q4_0V arm.
 
@@ -110,87 +113,94 @@ class Arm:
         wl = self.wl
         vcode = _lib.VARIANTS[variant]
         scale = 1.0 / math.sqrt(wl.D)
+        part = self.part
+        ctr = part.counters(wl.Hkv)
         self.calls = []
         for L in self.layers:
             kd, vd = L["kc"].desc(), L["vc"].desc()
             L["descs"] = (kd, vd)  # keep alive
-            self.calls.append((
-                (ctypes.byref(kd), ctypes.byref(vd), L["knew"].data_ptr(), L["vnew"].data_ptr(),
-                 self.pos.data_ptr(), wl.B, 1, wl.Hkv, wl.D, self.max_len),
-                (ctypes.byref(kd), ctypes.byref(vd), L["q"].data_ptr(), self.lens_t.data_ptr(), wl.B,
-                 wl.Hq, wl.Hkv, wl.D, scale, self.max_len, self.part.split_tokens,
-                 self.part.max_splits, self.part.o.data_ptr(), self.part.lse.data_ptr(), vcode),
-                (self.part.o.data_ptr(), self.part.lse.data_ptr(), self.lens_t.data_ptr(), wl.B,
-                 wl.Hq, wl.D, self.part.split_tokens, self.part.max_splits, 0, self.out.data_ptr(),
-                 None),
+            self.calls.append(dict(
+                step=(ctypes.byref(kd), ctypes.byref(vd), L["knew"].data_ptr(), L["vnew"].data_ptr(),
+                      L["q"].data_ptr(), self.lens_t.data_ptr(), wl.B, wl.Hq, wl.Hkv, wl.D, scale,
+                      self.max_len, part.split_tokens, part.max_splits, part.o.data_ptr(),
+                      part.lse.data_ptr(), ctr.data_ptr(), 0, self.out.data_ptr(), None),
+                append=(ctypes.byref(kd), ctypes.byref(vd), L["knew"].data_ptr(), L["vnew"].data_ptr(),
+                        self.pos.data_ptr(), wl.B, 1, wl.Hkv, wl.D, self.max_len),
+                decode=(ctypes.byref(kd), ctypes.byref(vd), L["q"].data_ptr(), self.lens_t.data_ptr(),
+                        wl.B, wl.Hq, wl.Hkv, wl.D, scale, self.max_len, part.split_tokens,
+                        part.max_splits, part.o.data_ptr(), part.lse.data_ptr(), vcode),
+                combine=(part.o.data_ptr(), part.lse.data_ptr(), self.lens_t.data_ptr(), wl.B, wl.Hq,
+                         wl.D, part.split_tokens, part.max_splits, 0, self.out.data_ptr(), None),
             ))
         self.lib = lib
 
-    def step(self, stream, rep=0, decode_only=False):
+    def step(self, stream, rep=0, mode="step"):
+        """One step over all layers of replica `rep`: mode "step" (kvq_decode_step),
+        "three" (append + decode + combine) or "decode" (the attention launch alone)."""
         lib = self.lib
         n = self.wl.layers
-        for a, d, c in self.calls[rep * n:(rep + 1) * n]:
-            if not decode_only:
-                rc = lib.kvq_quantize_append(*a, stream)
+        for c in self.calls[rep * n:(rep + 1) * n]:
+            if mode == "step":
+                rc = lib.kvq_decode_step(*c["step"], stream)
                 assert rc == 0, rc
-            rc = lib.kvq_decode_attn_variant(*d, stream)
+                continue
+            if mode == "three":
+                rc = lib.kvq_quantize_append(*c["append"], stream)
+                assert rc == 0, rc
+            rc = lib.kvq_decode_attn_variant(*c["decode"], stream)
             assert rc == 0, rc
-            if not decode_only:
-                rc = lib.kvq_combine(*c, stream)
+            if mode == "three":
+                rc = lib.kvq_combine(*c["combine"], stream)
                 assert rc == 0, rc
+
+
+MODES = ("step", "three", "decode")
 
 
 def time_arm(arm, steps, warmup, use_graph, variant):
+    """ms per step for every mode, timed with HIP events on the stream the
+    launches go to (graphs are replayed on torch's current stream)."""
     import torch
 
     arm.prepare_calls(variant)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     R = arm.replicas
-    for i in range(warmup):
-        arm.step(sh, i % R)
+    for mode in MODES:
+        for i in range(warmup):
+            arm.step(sh, i % R, mode)
     torch.cuda.synchronize()
 
-    graphs = []
-    dgraphs = []
+    graphs = {m: [] for m in MODES}
     if use_graph:
-        for r in range(R):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                arm.step(torch.cuda.current_stream().cuda_stream, r)
-            graphs.append(g)
-            dg = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(dg):
-                arm.step(torch.cuda.current_stream().cuda_stream, r, decode_only=True)
-            dgraphs.append(dg)
-        for r in range(R):
-            graphs[r].replay()
-            dgraphs[r].replay()
+        for m in MODES:
+            for r in range(R):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    arm.step(torch.cuda.current_stream().cuda_stream, r, m)
+                graphs[m].append(g)
+            for g in graphs[m]:
+                g.replay()
         torch.cuda.synchronize()
 
-    def run(k, decode_only=False):
+    def run(k, mode):
         for i in range(k):
             r = i % R
             if use_graph:
-                (dgraphs if decode_only else graphs)[r].replay()
+                graphs[mode][r].replay()
             else:
-                arm.step(sh, r, decode_only)
+                arm.step(sh, r, mode)
 
-    # whole step
+    ms = {}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    run(steps)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / steps
-    # decode kernel alone (same launches, same stream)
-    e0.record(stream)
-    run(steps, decode_only=True)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_decode_launch = e0.elapsed_time(e1) / (steps * arm.wl.layers)
-    return ms_step, ms_decode_launch
+    for mode in MODES:
+        torch.cuda.synchronize()
+        e0.record(stream)
+        run(steps, mode)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms[mode] = e0.elapsed_time(e1) / steps
+    return ms
 
 
 def cpu_baseline(arm, budget_s):
@@ -268,16 +278,17 @@ def main():
         log(f"arm {tk}/{tv}: building {wl.layers} layer(s) x {reps} replica(s)")
         arm = Arm(wl, tk, tv, split_tokens, reps, dev)
         log(f"arm {tk}/{tv}: timing {args.steps} steps")
-        ms_step, ms_dec = time_arm(arm, args.steps, args.warmup, not args.no_graph, args.variant)
-        gbs = arm.stored_bytes_step / (ms_step * 1e-3) / 1e9
-        dec_gbs = arm.stored_bytes_layer / (ms_dec * 1e-3) / 1e9
+        ms = time_arm(arm, args.steps, args.warmup, not args.no_graph, args.variant)
+        per_launch = {m: ms[m] / wl.layers for m in MODES}
         results[f"{tk}/{tv}"] = {
-            "us_per_step": round(ms_step * 1e3, 2),
+            "us_per_step": round(ms["step"] * 1e3, 2),
             "stored_bytes_per_step": arm.stored_bytes_step,
-            "GBps": round(gbs, 1),
-            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "decode_us_per_launch": round(ms_dec * 1e3, 3),
-            "decode_GBps": round(dec_gbs, 1),
+            "GBps": round(arm.stored_bytes_step / (ms["step"] * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(arm.stored_bytes_step / (ms["step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "step_us_per_layer": round(per_launch["step"] * 1e3, 3),
+            "three_call_us_per_step": round(ms["three"] * 1e3, 2),
+            "decode_only_us_per_launch": round(per_launch["decode"] * 1e3, 3),
+            "decode_only_GBps": round(arm.stored_bytes_layer / (per_launch["decode"] * 1e-3) / 1e9, 1),
             "replicas": reps,
         }
         log(f"arm {tk}/{tv}: {results[f'{tk}/{tv}']}")
@@ -315,11 +326,14 @@ def main():
         "config": {"workload": wl.name, "arm": f"{headline[0]}K/{headline[1]}V",
                    "layers": wl.layers, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
                    "head_dim": wl.D, "ctx": wl.ctx, "split_tokens": split_tokens,
-                   "variant": args.variant, "graph": not args.no_graph},
-        "roofline": {"bound": "hbm", "achieved": h["decode_GBps"], "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(h["decode_GBps"] / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "kvq_decode_attn",
-                     "avg_launch_us": h["decode_us_per_launch"]},
+                   "path": "kvq_decode_step", "graph": not args.no_graph},
+        # the step is one launch per layer: its average launch duration is the
+        # step time over the layers (gaps between graph-replayed launches included)
+        "roofline": {"bound": "hbm", "achieved": round(h["GBps"], 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(h["GBps"] / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "decode_mfma_kernel (kvq_decode_step)",
+                     "avg_launch_us": h["step_us_per_layer"],
+                     "algorithmic_bytes_per_launch": head_arm.stored_bytes_layer},
         "cpu_baseline": cpu,
         "arms": results,
         "ratios": ratios,

@@ -198,6 +198,42 @@ int kvq_combine(const float* part_o, const float* part_lse, const int32_t* seq_l
                 int Hq, int D, int split_tokens, int max_splits, int out_type, void* out,
                 float* lse_out, void* stream);
 
+/*
+ * One decode step of one layer in a single call: quantise-on-write of the new
+ * token, split-KV attention over every row including the new one, and the
+ * exact log-sum-exp merge (HAL #582 section 5 P2: the write path quantises a
+ * token once, the read path streams the stored blocks and merges regions by an
+ * exact online-softmax combine).
+ *
+ * Results equal kvq_quantize_append (one new row per sequence, written at row
+ * seq_lens[b] - 1) followed by kvq_decode_attn and kvq_combine with the same
+ * arguments: the cache rows are bit-identical, and out / lse_out agree within
+ * floating-point rounding.  Where the matrix-core kernel covers the shape
+ * (D = 128 or 256) this is one kernel launch: the workgroup whose split holds
+ * row seq_lens[b] - 1 writes that row before reading it, and the last
+ * workgroup of each (sequence, KV head) to finish merges the splits of its
+ * query heads.  Other shapes run the three kernels in order.
+ *
+ *   k_new, v_new : device, [B][Hkv][D] binary16: the new token's K and V rows.
+ *   seq_lens     : device, [B] int32: lengths *including* the new token,
+ *                  1 <= L_b <= max_seq_len <= capacity.
+ *   counters     : device, [B][Hkv] uint32 arrival counters, all zero before
+ *                  the first call; every call leaves them zero when it has
+ *                  completed.  Calls that may run concurrently (different
+ *                  streams) need separate counters and partial buffers.
+ *   out_type     : KVQ_F16 or KVQ_OUT_F32.
+ *   out          : device, [B][Hq][D] of out_type, 16-byte aligned.
+ *   lse_out      : device, [B][Hq] fp32 (natural-log LSE of the scores), or
+ *                  NULL.
+ *   Other arguments and requirements as for kvq_decode_attn; part_o and
+ *   part_lse are scratch of the same shapes, overwritten.
+ */
+int kvq_decode_step(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache,
+                    const void* k_new, const void* v_new, const void* q, const int32_t* seq_lens,
+                    int B, int Hq, int Hkv, int D, float softmax_scale, int max_seq_len,
+                    int split_tokens, int max_splits, float* part_o, float* part_lse,
+                    uint32_t* counters, int out_type, void* out, float* lse_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,6 +33,8 @@ HIP_FLAGS = [
     # depends on it); this is hipcc's default, stated explicitly
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-fast-math",
+    # LDS tiles are written and read through different pointer types
+    "-fno-strict-aliasing",
 ]
 
 

@@ -60,6 +60,15 @@ class Partials:
         self.max_splits = max(1, math.ceil(max_seq_len / split_tokens))
         self.o = torch.empty((B, Hq, self.max_splits, D), dtype=torch.float32, device=device)
         self.lse = torch.empty((B, Hq, self.max_splits), dtype=torch.float32, device=device)
+        self._counters = None
+
+    def counters(self, Hkv: int) -> torch.Tensor:
+        """Arrival counters of kvq_decode_step, [B][Hkv] uint32 (held as int32),
+        zeroed once here; each completed step leaves them zero."""
+        B = self.o.shape[0]
+        if self._counters is None or self._counters.shape != (B, Hkv):
+            self._counters = torch.zeros((B, Hkv), dtype=torch.int32, device=self.o.device)
+        return self._counters
 
 
 def append(kc: CachePlanes, vc: CachePlanes, k_new: torch.Tensor, v_new: torch.Tensor,
@@ -85,3 +94,15 @@ def combine(part: Partials, seq_lens: torch.Tensor, out: torch.Tensor, lse_out=N
     ot = "f16" if out.dtype == torch.float16 else "f32"
     return _lib.kvq_combine(part.o, part.lse, seq_lens, B, Hq, D, part.split_tokens,
                             part.max_splits, ot, out, lse_out, stream)
+
+
+def decode_step(kc: CachePlanes, vc: CachePlanes, k_new: torch.Tensor, v_new: torch.Tensor,
+                q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, part: Partials,
+                softmax_scale: float, out: torch.Tensor, lse_out=None, stream=None):
+    """kvq_decode_step: k_new, v_new (B, Hkv, D) fp16 written at row seq_lens[b] - 1,
+    then attention over rows [0, seq_lens[b]) into ``out`` (B, Hq, D)."""
+    B, Hq, D = q.shape
+    ot = "f16" if out.dtype == torch.float16 else "f32"
+    return _lib.kvq_decode_step(kc.desc(), vc.desc(), k_new, v_new, q, seq_lens, B, Hq, kc.Hkv, D,
+                                softmax_scale, max_seq_len, part.split_tokens, part.max_splits,
+                                part.o, part.lse, part.counters(kc.Hkv), ot, out, lse_out, stream)

@@ -5,38 +5,51 @@
 // partials merged by an exact log-sum-exp combine).
 //
 // One workgroup (4 wave64) per (sequence, KV head, split); each wave walks its
-// own 32-row tiles of the split (tiles w, w+4, ...) with private LDS buffers,
-// so waves never wait for each other until the final merge.
+// own 32-row tiles of the split (tiles w, w+4, ...) with a private LDS buffer,
+// so waves never wait for each other until the final merge.  The global loads
+// of a wave's next tile are issued before its current tile is computed.
+//
+// Codes enter the matrix cores as fp16 *subnormals*: the bit pattern of a
+// nibble n (or of a byte u = code + 128) in the low bits of an fp16 is the
+// value n * 2^-24, exact, and one AND (or one byte permute) builds two of them.
+// The offset (8 for q4_0, 128 for q8_0) is removed exactly once per block:
+//   QK  : the MFMA accumulator starts at -offset * 2^-24 * sum(q over the block);
+//   PV  : one extra MFMA per block and tile accumulates offset * 2^-24 * sum(P'),
+//         subtracted at the end.
+// The 2^24 is applied once to the scores and once to the final output.
 //
 // Per 32-row tile:
 //   QK^T as S^T = K * Q^T with v_mfma_f32_16x16x32_f16: A = 16 K rows x 32
-//     values of one 32-value block (the raw codes, exactly representable in
-//     fp16), B = the GQA group's Q (16 columns, G used).  One MFMA per block;
-//     its fp32 result is multiplied by the row's block scale (exact products,
-//     fp32 sums).  K goes straight from HBM to registers with coalesced
-//     16-byte loads; a 4x4 exchange between the four 16-lane rows
-//     (v_permlane32_swap / v_permlane16_swap) turns "lane row q holds block q"
-//     into "lane row q holds a quarter of every block".
+//     values of one 32-value block, B = the GQA group's Q (16 columns, G
+//     used).  One MFMA per block; its fp32 result is multiplied by the row's
+//     block scale (exact products, fp32 sums).  K goes straight from HBM to
+//     registers with coalesced 16-byte loads; a 4x4 exchange between the four
+//     16-lane rows (v_permlane32_swap / v_permlane16_swap) turns "lane row q
+//     holds block q" into "lane row q holds a quarter of every block".
 //   online softmax in fp32, log2 domain; the running maximum is only moved
 //     when a score exceeds it by more than 2^8 (exact either way: every
 //     partial sum is kept relative to the same reference), so rescaling the
 //     accumulators is rare.
-//   PV as O^T = V^T * P'^T: V is staged in LDS with direct global->LDS 16-byte
-//     loads and read back transposed (ds_read_b64_tr_b4 / _b8 / _b16) so each
-//     lane holds one value column for 8 rows; codes become fp16 exactly
-//     (nibble | 0x6400 minus 1032, byte ^ 0x80 | 0x6400 minus 1152).  The
-//     V block scale is folded into P (P' = p * scale per row and block, fp16),
-//     since every 16-column MFMA tile lies inside one 32-value block.
+//   PV as O^T = V^T * P'^T: V rows are loaded with coalesced 16-byte loads,
+//     written to the wave's LDS buffer and read back transposed
+//     (ds_read_b64_tr_b4 / _b8 / _b16) so each lane holds one value column
+//     for 8 rows.  The V block scale is folded into P (P' = p * scale per row
+//     and block, fp16), since every 16-column MFMA tile lies inside one block.
+//   Block scales are kept in LDS transposed ([block][row]) so the per-row
+//   scales a lane needs are contiguous.
 // The four waves' (max, sum, O) are merged through LDS into one normalised
 // partial per (head, split).
 #include <math.h>
 
+#include "kvq_combine.hpp"
 #include "kvq_internal.hpp"
+#include "kvq_quant.hpp"
 
 namespace kvq {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -47,8 +60,11 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 
 constexpr int WAVES = 4;
 constexpr int NT = 64 * WAVES;
-constexpr int TT = 32;          // rows per tile
-constexpr float TAU = 8.0f;     // lazy rescale threshold, log2 units
+constexpr int TT = 32;                 // rows per tile
+constexpr float TAU = 8.0f;            // lazy rescale threshold, log2 units
+constexpr float TWO24 = 16777216.0f;   // 2^24
+constexpr float TWOM24 = 1.0f / 16777216.0f;
+constexpr int VMCNT0 = 0x0F70;         // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
 
 __host__ __device__ constexpr int rb(int t, int D) { return data_row_bytes(t, D); }
 
@@ -58,14 +74,6 @@ __device__ __forceinline__ half8 make_half8(uint32_t a, uint32_t b, uint32_t c, 
 {
     u32x4 u = {a, b, c, d};
     return __builtin_bit_cast(half8, u);
-}
-
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pk_add_h(uint32_t x, uint32_t c)
-{
-    half2v a = __builtin_bit_cast(half2v, x), b = __builtin_bit_cast(half2v, c);
-    return __builtin_bit_cast(uint32_t, a + b);
 }
 
 __device__ __forceinline__ uint32_t pk_mul_h(uint32_t x, uint32_t c)
@@ -80,30 +88,21 @@ __device__ __forceinline__ uint32_t cvt_pk_h(float lo, float hi)
     return __builtin_bit_cast(uint32_t, r);
 }
 
-// 8 nibbles of one dword -> 8 fp16 values (code - 8), element order
-// [nib0, nib4, nib1, nib5, nib2, nib6, nib3, nib7].
-__device__ __forceinline__ half8 q4_dword_to_half8(uint32_t w)
+// 8 nibbles of one dword as fp16 subnormals (value = nibble * 2^-24), element
+// order [nib0, nib4, nib1, nib5, nib2, nib6, nib3, nib7].
+__device__ __forceinline__ half8 q4_sub8(uint32_t w)
 {
-    const uint32_t M = 0x000F000Fu, MAGIC = 0x64006400u, BIAS = 0xE408E408u;  // -1032, -1032
-    const uint32_t p0 = pk_add_h((w & M) | MAGIC, BIAS);
-    const uint32_t p1 = pk_add_h(((w >> 4) & M) | MAGIC, BIAS);
-    const uint32_t p2 = pk_add_h(((w >> 8) & M) | MAGIC, BIAS);
-    const uint32_t p3 = pk_add_h(((w >> 12) & M) | MAGIC, BIAS);
-    return make_half8(p0, p1, p2, p3);
+    const uint32_t M = 0x000F000Fu;
+    return make_half8(w & M, (w >> 4) & M, (w >> 8) & M, (w >> 12) & M);
 }
 
-// 8 signed bytes (two dwords) -> 8 fp16 values in byte order.
-__device__ __forceinline__ half8 q8_dwords_to_half8(uint32_t w0, uint32_t w1)
+// 8 signed bytes (two dwords) as fp16 subnormals of (byte + 128) * 2^-24, in
+// byte order.  v_perm_b32 selector 0x0C produces a zero byte.
+__device__ __forceinline__ half8 q8_sub8(uint32_t w0, uint32_t w1)
 {
-    const uint32_t BIAS = 0xE480E480u;  // -1152, -1152
     const uint32_t u0 = w0 ^ 0x80808080u, u1 = w1 ^ 0x80808080u;
-    const uint32_t K64 = 0x64646464u;
-    // v_perm_b32: bytes 0..3 from the second operand, 4..7 from the first
-    const uint32_t a = pk_add_h(__builtin_amdgcn_perm(K64, u0, 0x04010400u), BIAS);
-    const uint32_t b = pk_add_h(__builtin_amdgcn_perm(K64, u0, 0x04030402u), BIAS);
-    const uint32_t c = pk_add_h(__builtin_amdgcn_perm(K64, u1, 0x04010400u), BIAS);
-    const uint32_t d = pk_add_h(__builtin_amdgcn_perm(K64, u1, 0x04030402u), BIAS);
-    return make_half8(a, b, c, d);
+    return make_half8(__builtin_amdgcn_perm(u0, u0, 0x0C010C00u), __builtin_amdgcn_perm(u0, u0, 0x0C030C02u),
+                      __builtin_amdgcn_perm(u1, u1, 0x0C010C00u), __builtin_amdgcn_perm(u1, u1, 0x0C030C02u));
 }
 
 // 4x4 exchange between the four 16-lane rows: on entry lane row g holds
@@ -141,31 +140,6 @@ __device__ __forceinline__ float xsum4(float v)
     return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
 }
 
-// Explicit waits for the direct global->LDS loads, whose completion the
-// compiler does not track for later LDS reads.  The memory clobber also keeps
-// the compiler from moving loads across the wait.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void wait_lgkm0()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
-
-__device__ __forceinline__ void lds_load16(const void* g, LDS_AS void* l)
-{
-    __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-}
-
-__device__ __forceinline__ void lds_load4(const void* g, LDS_AS void* l)
-{
-    __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
-}
-
 // --------------------------------------------------------------- the kernel
 
 template <int TK, int TV, int D>
@@ -175,31 +149,34 @@ struct Cfg {
     static constexpr int RBK = rb(TK, D);
     static constexpr int RBV = rb(TV, D);
     static constexpr int KU = TK == T_Q4 ? 1 : (TK == T_Q8 ? 2 : 4);   // dwords per lane per block
-    static constexpr int KDW = 4 * KU * NBG;                           // dwords per lane per subtile
+    static constexpr int KDW = 4 * KU * NBG;                           // K dwords per lane per subtile
     static constexpr int V_BYTES = TT * RBV;                           // V tile bytes
-    static constexpr int V_LOADS = V_BYTES / 1024;                     // 16-byte direct loads per tile
-    static constexpr int S_BYTES = TT * 2 * NB;                        // one scale tile
-    static constexpr int S_LOADS = S_BYTES / 256;                      // 4-byte direct loads per tile
+    static constexpr int V_LOADS = V_BYTES / 1024;                     // 16-byte loads per lane
+    static constexpr int V_DW = 4 * V_LOADS;
     static constexpr int K_SCALE = TK != T_F16;
     static constexpr int V_SCALE = TV != T_F16;
-    // per-wave LDS buffer: V tile, K scales, V scales
-    static constexpr int BUF = V_BYTES + S_BYTES * (K_SCALE + V_SCALE);
+    static constexpr int S_BYTES = TT * 2 * NB;                        // one scale tile
+    static constexpr int S_LOADS = S_BYTES / 256;                      // 4-byte loads per lane
+    static constexpr int S_DW = (K_SCALE + V_SCALE) * S_LOADS > 0 ? (K_SCALE + V_SCALE) * S_LOADS : 1;
     static constexpr int KS_OFF = V_BYTES;
     static constexpr int VS_OFF = V_BYTES + S_BYTES * K_SCALE;
-    static constexpr int WAVE_LDS = 2 * BUF;
+    static constexpr int BUF = V_BYTES + S_BYTES * (K_SCALE + V_SCALE);
     static constexpr int NDT = D / 16;                                 // PV output tiles
-    // vector-memory ops issued per tile (for the explicit LDS wait)
-    static constexpr int K_VM = 2 * NBG * KU;                          // 16-byte K loads (2 subtiles)
-    static constexpr int TILE_VM = K_VM + V_LOADS + (K_SCALE ? S_LOADS : 0) + (V_SCALE ? S_LOADS : 0);
-    static constexpr bool VALID = V_BYTES % 1024 == 0 && S_BYTES % 256 == 0 && TILE_VM < 64 &&
-                                  WAVES * WAVE_LDS <= 160 * 1024;
+    static constexpr float KOFF = TK == T_Q4 ? 8.0f : (TK == T_Q8 ? 128.0f : 0.0f);
+    static constexpr uint32_t VOFF_BITS = TV == T_Q4 ? 0x00080008u : 0x00800080u;
+    static constexpr bool VALID = V_BYTES % 1024 == 0 && S_BYTES % 256 == 0 && V_DW <= 32 &&
+                                  WAVES * BUF <= 64 * 1024 &&
+                                  4 * CMB_GROUP_LDS_MIN(16) <= WAVES * BUF;
 };
 
 template <int TK, int TV, int D>
 __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
 {
     using C = Cfg<TK, TV, D>;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    // One LDS buffer per wave: the V rows of the current tile, then the K and
+    // V scale tiles, transposed to [block][row].
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[WAVES * C::BUF];
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -210,6 +187,7 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
     const int t_end = min(t_begin + a.split_tokens, L);
     const int h0 = g * G;
     const int64_t ho_stride = (int64_t)a.max_splits * D;
+    const bool fused = a.counters != nullptr;
     float* po = a.part_o + (((int64_t)b * a.Hq + h0) * a.max_splits + s) * D;
     float* pl = a.part_lse + ((int64_t)b * a.Hq + h0) * a.max_splits + s;
 
@@ -226,12 +204,39 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
     const uint8_t* vdata = a.v.data + vrow0 * C::RBV;
     const uint8_t* vscl = reinterpret_cast<const uint8_t*>(a.v.scales + vrow0 * C::NB);
 
+    // ---- fused decode step: the workgroup whose split holds row L-1 first
+    //      quantises the new K and V rows of its KV head into that row (the
+    //      same block quantiser as kvq_quantize_append), then makes them
+    //      visible to its own loads
+    if (a.k_new != nullptr && t_end == L) {
+        if (tid < 2 * C::NB) {
+            const bool isv = tid >= C::NB;
+            const int blk = isv ? tid - C::NB : tid;
+            const uint16_t* src = (isv ? a.v_new : a.k_new) + ((int64_t)b * a.Hkv + g) * D + 32 * blk;
+            const int64_t row = (isv ? vrow0 : krow0) + (L - 1);
+            if (isv) {
+                quantize_block<TV>(src, a.v.data + row * C::RBV + blk * rb(TV, 32),
+                                   a.v.scales + row * C::NB + blk);
+            } else {
+                quantize_block<TK>(src, a.k.data + row * C::RBK + blk * rb(TK, 32),
+                                   a.k.scales + row * C::NB + blk);
+            }
+        }
+        // the row is read back only by this workgroup, whose loads of that
+        // tile are issued after the barrier: the stores must be complete
+        // (acknowledged by L2) first; no other workgroup reads these lines
+        __builtin_amdgcn_s_waitcnt(VMCNT0);
+        __syncthreads();
+    }
+
     // ---- Q as the B operand of S^T = K Q^T: column ln = head, lane row lq
     half8 qop[C::NB];
+    floatx4 kbias[C::NB];
     {
         const uint16_t* qh = a.q + ((int64_t)b * a.Hq + h0 + min(ln, G - 1)) * D;
 #pragma unroll
         for (int kb = 0; kb < C::NB; ++kb) {
+            float part = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 int el;
@@ -241,72 +246,111 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
                 } else {
                     el = 8 * lq + e;
                 }
-                qop[kb][e] = ln < G ? __builtin_bit_cast(_Float16, qh[32 * kb + el]) : (_Float16)0.0f;
+                const _Float16 qv = __builtin_bit_cast(_Float16, qh[32 * kb + el]);
+                qop[kb][e] = ln < G ? qv : (_Float16)0.0f;
+                part += (float)qop[kb][e];
             }
+            // the accumulator's start removes the code offset exactly once
+            const float bias = -C::KOFF * TWOM24 * xsum4(part);
+            kbias[kb] = floatx4{bias, bias, bias, bias};
         }
     }
+    // scores: fp32 MFMA sums times block scale, then softmax scale * log2(e)
+    // (and 2^24 for the subnormal codes)
+    const float cK = a.scale_log2 * (C::K_SCALE ? TWO24 : 1.0f);
 
-    uint8_t* wbuf = smem + wave * C::WAVE_LDS;
+    uint8_t* const wbuf = lds_a + wave * C::BUF;
     floatx4 oacc[C::NDT];
+    floatx4 bacc[C::NB];
 #pragma unroll
     for (int i = 0; i < C::NDT; ++i) oacc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < C::NB; ++i) bacc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     float m_ref = -INFINITY, l_part = 0.0f;
 
     const int ntiles = (t_end - t_begin + TT - 1) / TT;
+    // K row of subtile j read by this lane (tile-relative): rows of the A
+    // operand are ordered so that the score layout gives lane row lq the rows
+    // 8*lq .. 8*lq+7 of the tile
+    const int krow_rel0 = 8 * (ln >> 2) + (ln & 3);
+    const int kpiece = lq * (16 * C::KU);
 
-    // ---- issue all loads of tile `it` (K rows to registers, V rows and both
-    //      scale tiles to LDS buffer `buf`)
-    auto issue = [&](int it, uint32_t (&kr)[2][C::KDW], int buf) {
+    // ---- global loads of tile `it` into registers: K rows in the MFMA layout
+    //      (issue_k), and the V rows and scale rows (issue_vs) that stage()
+    //      then copies to this wave's LDS buffer
+    auto issue_k = [&](int it, uint32_t (&kr)[2][C::KDW]) {
         const int t0 = t_begin + it * TT;
-        uint8_t* vb = wbuf + buf * C::BUF;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int tok = t0 + 8 * (ln >> 2) + 4 * j + (ln & 3);
-            const uint8_t* row = kdata + (int64_t)min(tok, L - 1) * C::RBK;
+            const int tok = min(t0 + krow_rel0 + 4 * j, L - 1);
+            const uint8_t* row = kdata + (uint32_t)(tok * C::RBK) + kpiece;
 #pragma unroll
             for (int bg = 0; bg < C::NBG; ++bg) {
 #pragma unroll
                 for (int u = 0; u < C::KU; ++u) {
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(
-                        row + bg * (C::RBK / C::NBG) + lq * (16 * C::KU) + 16 * u);
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(row + bg * (C::RBK / C::NBG) + 16 * u);
 #pragma unroll
                     for (int c = 0; c < 4; ++c) kr[j][(bg * C::KU + u) * 4 + c] = v[c];
                 }
             }
         }
+    };
+    auto issue_vs = [&](int it, uint32_t (&vr)[C::V_DW], uint32_t (&sr)[C::S_DW]) {
+        const int t0 = t_begin + it * TT;
 #pragma unroll
         for (int k = 0; k < C::V_LOADS; ++k) {
             const int c16 = k * 64 + lane;
-            const int tok = c16 / (C::RBV / 16), off = c16 % (C::RBV / 16);
-            lds_load16(vdata + (int64_t)min(t0 + tok, L - 1) * C::RBV + 16 * off,
-                       (LDS_AS void*)(vb + 1024 * k));
-        }
-        if constexpr (C::K_SCALE) {
+            const int tok = min(t0 + c16 / (C::RBV / 16), L - 1);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(
+                vdata + (uint32_t)(tok * C::RBV) + 16 * (c16 % (C::RBV / 16)));
 #pragma unroll
-            for (int k = 0; k < C::S_LOADS; ++k) {
-                const int c4 = k * 64 + lane;
-                const int tok = c4 / (C::NB / 2), dw = c4 % (C::NB / 2);
-                lds_load4(kscl + (int64_t)min(t0 + tok, L - 1) * (2 * C::NB) + 4 * dw,
-                          (LDS_AS void*)(vb + C::KS_OFF + 256 * k));
+            for (int c = 0; c < 4; ++c) vr[4 * k + c] = v[c];
+        }
+#pragma unroll
+        for (int k = 0; k < C::S_LOADS; ++k) {
+            const int c4 = k * 64 + lane;
+            const int tok = min(t0 + c4 / (C::NB / 2), L - 1);
+            const uint32_t off = (uint32_t)(tok * (2 * C::NB)) + 4 * (c4 % (C::NB / 2));
+            if constexpr (C::K_SCALE) sr[k] = *reinterpret_cast<const uint32_t*>(kscl + off);
+            if constexpr (C::V_SCALE)
+                sr[C::K_SCALE * C::S_LOADS + k] = *reinterpret_cast<const uint32_t*>(vscl + off);
+        }
+    };
+
+    // ---- copy the staged V rows (natural order, [32 rows][row bytes]) and the
+    //      scale rows (transposed to [block][32 rows]) to the wave's LDS buffer
+    auto stage = [&](const uint32_t (&vr)[C::V_DW], const uint32_t (&sr)[C::S_DW]) {
+        uint8_t* vb = wbuf;
+#pragma unroll
+        for (int k = 0; k < C::V_LOADS; ++k) {
+            const u32x4 v = {vr[4 * k], vr[4 * k + 1], vr[4 * k + 2], vr[4 * k + 3]};
+            *reinterpret_cast<u32x4*>(vb + 1024 * k + 16 * lane) = v;
+        }
+#pragma unroll
+        for (int k = 0; k < C::S_LOADS; ++k) {
+            const int c4 = k * 64 + lane;
+            const int tok = c4 / (C::NB / 2), blk = 2 * (c4 % (C::NB / 2));
+            if constexpr (C::K_SCALE) {
+                const uint32_t w = sr[k];
+                uint16_t* st = reinterpret_cast<uint16_t*>(vb + C::KS_OFF);
+                st[blk * TT + tok] = (uint16_t)(w & 0xffff);
+                st[(blk + 1) * TT + tok] = (uint16_t)(w >> 16);
             }
-        }
-        if constexpr (C::V_SCALE) {
-#pragma unroll
-            for (int k = 0; k < C::S_LOADS; ++k) {
-                const int c4 = k * 64 + lane;
-                const int tok = c4 / (C::NB / 2), dw = c4 % (C::NB / 2);
-                lds_load4(vscl + (int64_t)min(t0 + tok, L - 1) * (2 * C::NB) + 4 * dw,
-                          (LDS_AS void*)(vb + C::VS_OFF + 256 * k));
+            if constexpr (C::V_SCALE) {
+                const uint32_t w = sr[C::K_SCALE * C::S_LOADS + k];
+                uint16_t* st = reinterpret_cast<uint16_t*>(vb + C::VS_OFF);
+                st[blk * TT + tok] = (uint16_t)(w & 0xffff);
+                st[(blk + 1) * TT + tok] = (uint16_t)(w >> 16);
             }
         }
     };
 
-    // ---- compute tile `it` whose data is in kr / LDS buffer `buf`
-    auto compute = [&](int it, uint32_t (&kr)[2][C::KDW], int buf) {
+    // ---- compute tile `it` whose K rows are in kr and V rows / scales in LDS
+    auto compute = [&](int it, uint32_t (&kr)[2][C::KDW], int next_it) {
         const int t0 = t_begin + it * TT;
-        const uint8_t* vb = wbuf + buf * C::BUF;
-        const uint8_t* ksb = vb + C::KS_OFF;
-        const uint8_t* vsb = vb + C::VS_OFF;
+        const uint8_t* vb = wbuf;
+        const uint16_t* kst = reinterpret_cast<const uint16_t*>(vb + C::KS_OFF);
+        const uint16_t* vst = reinterpret_cast<const uint16_t*>(vb + C::VS_OFF);
 
         // -- QK: S^T for the two 16-row subtiles; lane (ln, lq) reg i holds the
         //    score of row t0 + 8*lq + 4*j + i for head ln
@@ -326,9 +370,7 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
                     xpose4(base[0 * C::KU + u], base[1 * C::KU + u], base[2 * C::KU + u],
                            base[3 * C::KU + u]);
             }
-            floatx4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
-            // block scales of this lane's four rows (t0 + 8*lq + 4*j + i)
-            const uint16_t* srow = reinterpret_cast<const uint16_t*>(ksb) + (8 * lq + 4 * j) * C::NB;
+            floatx4 cb[C::NB];
 #pragma unroll
             for (int bg = 0; bg < C::NBG; ++bg) {
 #pragma unroll
@@ -336,23 +378,36 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
                     const int kb = 4 * bg + kb4;
                     const uint32_t* q = x + bg * 4 * C::KU + kb4 * C::KU;
                     half8 av;
-                    if constexpr (TK == T_Q4) av = q4_dword_to_half8(q[0]);
-                    else if constexpr (TK == T_Q8) av = q8_dwords_to_half8(q[0], q[1]);
+                    if constexpr (TK == T_Q4) av = q4_sub8(q[0]);
+                    else if constexpr (TK == T_Q8) av = q8_sub8(q[0], q[1]);
                     else av = make_half8(q[0], q[1], q[2], q[3]);
-                    const floatx4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qop[kb], z, 0, 0, 0);
-                    if constexpr (C::K_SCALE) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            sc[i] = fmaf(c[i], h2f(srow[i * C::NB + kb]), sc[i]);
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) sc[i] += c[i];
-                    }
+                    cb[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qop[kb], kbias[kb], 0, 0, 0);
                 }
+            }
+            floatx4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (C::K_SCALE) {
+                // block scales of this lane's four rows (8*lq + 4*j + i): four
+                // contiguous fp16 values per block in the transposed tile
+#pragma unroll
+                for (int kb = 0; kb < C::NB; ++kb) {
+                    const u32x2 sw = *reinterpret_cast<const u32x2*>(kst + kb * TT + 8 * lq + 4 * j);
+                    // the element is copied out first: hipcc (clang) bit-casts
+                    // a vector-element lvalue from the vector's first element
+                    const half2v s01 = __builtin_bit_cast(half2v, (uint32_t)sw[0]);
+                    const half2v s23 = __builtin_bit_cast(half2v, (uint32_t)sw[1]);
+                    sc[0] = fmaf(cb[kb][0], (float)s01[0], sc[0]);
+                    sc[1] = fmaf(cb[kb][1], (float)s01[1], sc[1]);
+                    sc[2] = fmaf(cb[kb][2], (float)s23[0], sc[2]);
+                    sc[3] = fmaf(cb[kb][3], (float)s23[1], sc[3]);
+                }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < C::NB; ++kb) sc += cb[kb];
             }
             sacc[j] = sc;
         }
+        // the K registers are free: start loading the next tile's K rows
+        if (next_it < ntiles) issue_k(next_it, kr);
 
         // -- online softmax (log2 domain)
         float sv[8];
@@ -361,140 +416,136 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float x = sacc[j][i] * a.scale_log2;
+                const float x = sacc[j][i] * cK;
                 sv[4 * j + i] = (tail && t0 + 8 * lq + 4 * j + i >= t_end) ? -INFINITY : x;
             }
         float mx = sv[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-        const bool need = mx > m_ref + TAU;
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        if (__builtin_amdgcn_ballot_w64(mx > m_ref + TAU) != 0) {
             const float hmax = xmax4(mx);
             const float m_new = hmax > m_ref + TAU ? hmax : m_ref;
             const float al = exp2f(m_ref - m_new);
             l_part *= al;
 #pragma unroll
             for (int t = 0; t < C::NDT; ++t) oacc[t] *= al;
+#pragma unroll
+            for (int t = 0; t < C::NB; ++t) bacc[t] *= al;
             m_ref = m_new;
         }
         float p[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            p[e] = exp2f(sv[e] - m_ref);
+            p[e] = __builtin_amdgcn_exp2f(sv[e] - m_ref);
             l_part += p[e];
         }
         uint32_t pp[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) pp[k] = cvt_pk_h(p[2 * k], p[2 * k + 1]);
 
-        // -- the LDS data of this tile must have landed (the next tile's loads
-        //    may still be in flight)
-        // (the caller waits before calling compute)
-
-        // -- P' = P * V block scale for the rows of this lane row (8*lq + e)
-        uint32_t ps[C::NB][4];
-        if constexpr (C::V_SCALE) {
-            const uint16_t* vs = reinterpret_cast<const uint16_t*>(vsb) + (8 * lq) * C::NB;
-#pragma unroll
-            for (int kb = 0; kb < C::NB; ++kb)
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const uint32_t sp = (uint32_t)vs[(2 * k) * C::NB + kb] |
-                                        ((uint32_t)vs[(2 * k + 1) * C::NB + kb] << 16);
-                    ps[kb][k] = pk_mul_h(pp[k], sp);
-                }
-        }
+        // P' for block kb: p times the V scale of each of this lane row's
+        // rows 8*lq + e (eight contiguous fp16 values of the transposed tile)
+        auto pscaled = [&](int kb) -> half8 {
+            const u32x4 sv4 = *reinterpret_cast<const u32x4*>(vst + kb * TT + 8 * lq);
+            return make_half8(pk_mul_h(pp[0], sv4[0]), pk_mul_h(pp[1], sv4[1]),
+                              pk_mul_h(pp[2], sv4[2]), pk_mul_h(pp[3], sv4[3]));
+        };
+        const half8 voff = __builtin_bit_cast(half8, u32x4{C::VOFF_BITS, C::VOFF_BITS, C::VOFF_BITS,
+                                                           C::VOFF_BITS});
 
         // -- PV: O^T tile t (16 value columns) += V^T(16 x 32 rows) * P'^T
         const LDS_AS uint8_t* vl = (const LDS_AS uint8_t*)vb;
         if constexpr (TV == T_Q4) {
-            // one transposed read gives two column tiles (chunks 2c2, 2c2+1);
-            // lane r of the row group addresses row 8*lq + pi(r&7), chunk 2c2 + (r>>3)
+            // one transposed read gives the two column tiles of block c2
+            // (chunks 2*c2 and 2*c2+1); lane r of the row group addresses row
+            // 8*lq + pi(r&7), chunk 2*c2 + (r>>3), pi = [0,2,4,6,1,3,5,7] so the
+            // nibble pairs come out in row order
             const int r = ln;
             const int rr = r & 7;
             const int trow = 8 * lq + ((rr < 4) ? 2 * rr : 2 * (rr - 4) + 1);
+            const LDS_AS uint8_t* tbase = vl + trow * C::RBV + 8 * (r >> 3);
 #pragma unroll
-            for (int c2 = 0; c2 < C::NDT / 2; ++c2) {
-                const int chunk = 2 * c2 + (r >> 3);
-                const int2v w = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
-                    (LDS_AS int2v*)(vl + trow * C::RBV + 8 * chunk));
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int t = 2 * c2 + h;           // column tile = chunk
-                    const int kb = t >> 1;              // its block
-                    const half8 av = q4_dword_to_half8((uint32_t)w[h]);
-                    const half8 bv = make_half8(ps[kb][0], ps[kb][1], ps[kb][2], ps[kb][3]);
-                    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, oacc[t], 0, 0, 0);
-                }
+            for (int c2 = 0; c2 < C::NB; ++c2) {
+                const int2v w = __builtin_amdgcn_ds_read_tr4_b64_v2i32((LDS_AS int2v*)(tbase + 16 * c2));
+                const half8 bv = pscaled(c2);
+                oacc[2 * c2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(q4_sub8((uint32_t)w[0]), bv,
+                                                                     oacc[2 * c2], 0, 0, 0);
+                oacc[2 * c2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(q4_sub8((uint32_t)w[1]), bv,
+                                                                         oacc[2 * c2 + 1], 0, 0, 0);
+                bacc[c2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(voff, bv, bacc[c2], 0, 0, 0);
             }
         } else if constexpr (TV == T_Q8) {
-            // column tile t = chunks 2t, 2t+1; lane r addresses row 8*lq + r/2, chunk 2t + (r&1)
+            // column tile t = chunks 2t, 2t+1; lane r addresses row 8*lq + r/2,
+            // chunk 2t + (r&1)
             const int r = ln;
-            const int trow = 8 * lq + (r >> 1);
+            const LDS_AS uint8_t* tbase = vl + (8 * lq + (r >> 1)) * C::RBV + 8 * (r & 1);
 #pragma unroll
-            for (int t = 0; t < C::NDT; ++t) {
-                const int2v w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (LDS_AS int2v*)(vl + trow * C::RBV + 8 * (2 * t + (r & 1))));
-                const half8 av = q8_dwords_to_half8((uint32_t)w[0], (uint32_t)w[1]);
-                const int kb = t >> 1;
-                const half8 bv = make_half8(ps[kb][0], ps[kb][1], ps[kb][2], ps[kb][3]);
-                oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, oacc[t], 0, 0, 0);
+            for (int kb = 0; kb < C::NB; ++kb) {
+                const half8 bv = pscaled(kb);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int t = 2 * kb + h;
+                    const int2v w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS int2v*)(tbase + 16 * t));
+                    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(q8_sub8((uint32_t)w[0], (uint32_t)w[1]),
+                                                                    bv, oacc[t], 0, 0, 0);
+                }
+                bacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(voff, bv, bacc[kb], 0, 0, 0);
             }
         } else {
-            // column tile t = chunks 4t..4t+3 (4 halves each); two reads of 4 rows;
-            // lane r addresses row 8*lq + 4*R + r/4, chunk 4t + (r&3)
+            // column tile t = chunks 4t..4t+3 (4 halves each); two reads of 4
+            // rows; lane r addresses row 8*lq + 4*R + r/4, chunk 4t + (r&3)
             const int r = ln;
             const half8 bv = make_half8(pp[0], pp[1], pp[2], pp[3]);
+            const LDS_AS uint8_t* tbase = vl + (8 * lq + (r >> 2)) * C::RBV + 8 * (r & 3);
 #pragma unroll
             for (int t = 0; t < C::NDT; ++t) {
                 uint32_t d[4];
 #pragma unroll
                 for (int R = 0; R < 2; ++R) {
-                    const int trow = 8 * lq + 4 * R + (r >> 2);
                     const short4v w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (LDS_AS short4v*)(vl + trow * C::RBV + 8 * (4 * t + (r & 3))));
+                        (LDS_AS short4v*)(tbase + 4 * R * C::RBV + 32 * t));
                     const u32x2 u = __builtin_bit_cast(u32x2, w);
                     d[2 * R] = u[0];
                     d[2 * R + 1] = u[1];
                 }
-                const half8 av = make_half8(d[0], d[1], d[2], d[3]);
-                oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, oacc[t], 0, 0, 0);
+                oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(make_half8(d[0], d[1], d[2], d[3]), bv,
+                                                                oacc[t], 0, 0, 0);
             }
         }
     };
 
-    // ---- main loop over this wave's tiles, double-buffered
-    uint32_t kA[2][C::KDW], kB[2][C::KDW];
+    // ---- main loop over this wave's tiles (it, it+4, ...).  At the top of an
+    //      iteration the K rows of tile `it` are in kr, its V rows and scales
+    //      in LDS, and the V/scale loads of the next tile are in flight in
+    //      vr/sr.  The next tile's K loads are issued as soon as the QK
+    //      products are done; its V rows go to LDS after this tile's PV (a
+    //      wave's LDS reads and writes are performed in order, so one buffer
+    //      suffices).
+    uint32_t kr[2][C::KDW];
+    uint32_t vr[C::V_DW];
+    uint32_t sr[C::S_DW];
     int it = wave;
-    if (it < ntiles) issue(it, kA, 0);
-    while (it < ntiles) {
+    if (it < ntiles) {
+        issue_k(it, kr);
+        issue_vs(it, vr, sr);
+        stage(vr, sr);
+        if (it + WAVES < ntiles) issue_vs(it + WAVES, vr, sr);
+    }
+    for (; it < ntiles; it += WAVES) {
         const int nx = it + WAVES;
+        compute(it, kr, nx);
         if (nx < ntiles) {
-            wait_lgkm0();
-            issue(nx, kB, 1);
-            wait_vmcnt<C::TILE_VM>();
-        } else {
-            wait_vmcnt<0>();
+            stage(vr, sr);
+            if (nx + WAVES < ntiles) issue_vs(nx + WAVES, vr, sr);
         }
-        compute(it, kA, 0);
-        it = nx;
-        if (it >= ntiles) break;
-        const int nx2 = it + WAVES;
-        if (nx2 < ntiles) {
-            wait_lgkm0();
-            issue(nx2, kA, 0);
-            wait_vmcnt<C::TILE_VM>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        compute(it, kB, 1);
-        it = nx2;
     }
 
     // ---- merge the four waves: (m, l, O) per head through LDS
     const float l_head = xsum4(l_part);
     __syncthreads();
-    float* mw = reinterpret_cast<float*>(smem);           // [WAVES][16]
+    const size_t merge_bytes = sizeof(float) * ((size_t)WAVES * 32 + (size_t)WAVES * G * D);
+    uint8_t* marea = merge_bytes <= sizeof(lds_a) ? lds_a : lds_merge_dyn;
+    float* mw = reinterpret_cast<float*>(marea);          // [WAVES][16]
     float* lw = mw + WAVES * 16;                          // [WAVES][16]
     float* ow = lw + WAVES * 16;                          // [WAVES][G][D]
     if (lq == 0) {
@@ -510,7 +561,9 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
                 int d;
                 if constexpr (TV == T_Q4) d = 32 * (t >> 1) + 8 * (t & 1) + (m >> 1) + 16 * (m & 1);
                 else d = 16 * t + m;
-                ow[(wave * G + ln) * D + d] = oacc[t][i];
+                float o = oacc[t][i];
+                if constexpr (C::V_SCALE) o = (o - bacc[t >> 1][i]) * TWO24;
+                ow[(wave * G + ln) * D + d] = o;
             }
     }
     __syncthreads();
@@ -526,21 +579,70 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
             lsum += f * lw[w * 16 + n];
             o += f * ow[(w * G + n) * D + d];
         }
-        po[n * ho_stride + d] = o / lsum;
-        if (d == 0) pl[(int64_t)n * a.max_splits] = (M + log2f(lsum)) * 0.69314718055994531f;
+        const float ov = o / lsum;
+        const float lv = (M + log2f(lsum)) * 0.69314718055994531f;
+        if (fused) {
+            // written through to memory, so the merging workgroup (on any
+            // XCD) reads them after its acquire without an L2 writeback here
+            __hip_atomic_store(po + n * ho_stride + d, ov, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            if (d == 0)
+                __hip_atomic_store(pl + (int64_t)n * a.max_splits, lv, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM);
+        } else {
+            po[n * ho_stride + d] = ov;
+            if (d == 0) pl[(int64_t)n * a.max_splits] = lv;
+        }
+    }
+
+    // ---- fused decode step: the last of the (sequence, KV head)'s non-empty
+    //      splits to finish merges all of them for the G heads of this KV head.
+    //      Release: every thread's partial stores (system scope, written
+    //      through) are complete before the arrival count; acquire: the last
+    //      workgroup invalidates its L2 view before reading the partials.
+    if (fused) {
+        __shared__ int is_last;
+        __builtin_amdgcn_s_waitcnt(VMCNT0);
+        __syncthreads();
+        if (tid == 0) {
+            const int S_b = (L + a.split_tokens - 1) / a.split_tokens;
+            uint32_t* ctr = a.counters + (int64_t)b * a.Hkv + g;
+            const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            is_last = prev == (uint32_t)(S_b - 1);
+            if (is_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (is_last) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            const int S_b = (L + a.split_tokens - 1) / a.split_tokens;
+            const int64_t bh0 = (int64_t)b * a.Hq + h0;
+            void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh0 * D)
+                                  : (void*)(reinterpret_cast<float*>(a.out) + bh0 * D);
+            combine_group<D / 64>(a.part_lse + bh0 * a.max_splits, a.max_splits,
+                                  a.part_o + bh0 * a.max_splits * D, (int64_t)a.max_splits * D, G, S_b,
+                                  D, a.out_f16, out, a.lse_out ? a.lse_out + bh0 : nullptr,
+                                  reinterpret_cast<float*>(lds_a), (int)(sizeof(lds_a) / sizeof(float)));
+        }
     }
 }
 
 template <int TK, int TV, int D>
 constexpr bool cfg_valid() { return Cfg<TK, TV, D>::VALID; }
 
+// Dynamic LDS of a launch: the merge area, when it does not fit in the
+// static stage array.
+template <int TK, int TV, int D>
+size_t dyn_lds_bytes(int G)
+{
+    using C = Cfg<TK, TV, D>;
+    const size_t merge = sizeof(float) * ((size_t)WAVES * 32 + (size_t)WAVES * G * D);
+    return merge <= (size_t)WAVES * C::BUF ? 0 : merge;
+}
+
 template <int TK, int TV, int D>
 size_t lds_bytes(int G)
 {
     using C = Cfg<TK, TV, D>;
-    const size_t stage = (size_t)WAVES * C::WAVE_LDS;
-    const size_t merge = sizeof(float) * ((size_t)WAVES * 32 + (size_t)WAVES * G * D);
-    return stage > merge ? stage : merge;
+    return (size_t)WAVES * C::BUF + dyn_lds_bytes<TK, TV, D>(G);
 }
 
 template <int TK, int TV, int D>
@@ -550,14 +652,14 @@ hipError_t launch3(const DecodeArgs& a, hipStream_t s)
         return hipErrorInvalidConfiguration;
     } else {
         dim3 grid(a.max_splits, a.Hkv, a.B);
-        const size_t lds = lds_bytes<TK, TV, D>(a.G);
-        if (lds > 64 * 1024) {
+        const size_t dyn = dyn_lds_bytes<TK, TV, D>(a.G);
+        if (lds_bytes<TK, TV, D>(a.G) > 64 * 1024) {
             const hipError_t e = hipFuncSetAttribute(
                 reinterpret_cast<const void*>(&decode_mfma_kernel<TK, TV, D>),
-                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL((decode_mfma_kernel<TK, TV, D>), grid, dim3(NT), lds, s, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<TK, TV, D>), grid, dim3(NT), dyn, s, a);
         return hipGetLastError();
     }
 }
@@ -582,6 +684,24 @@ hipError_t launch1(const DecodeArgs& a, hipStream_t s)
     }
 }
 
+template <int TK, int TV>
+bool supports2(const DecodeArgs& a)
+{
+    if (a.D == 128) return cfg_valid<TK, TV, 128>() && lds_bytes<TK, TV, 128>(a.G) <= 160 * 1024;
+    if (a.D == 256) return cfg_valid<TK, TV, 256>() && lds_bytes<TK, TV, 256>(a.G) <= 160 * 1024;
+    return false;
+}
+
+template <int TK>
+bool supports1(const DecodeArgs& a)
+{
+    switch (a.tv) {
+    case T_F16: return supports2<TK, T_F16>(a);
+    case T_Q8: return supports2<TK, T_Q8>(a);
+    default: return supports2<TK, T_Q4>(a);
+    }
+}
+
 }  // namespace
 
 bool decode_mfma_supports(const DecodeArgs& a)
@@ -590,22 +710,16 @@ bool decode_mfma_supports(const DecodeArgs& a)
     // spilling; it stays on the vector-ALU kernel
     if (a.D != 128 && a.D != 256) return false;
     if (a.G < 1 || a.G > 16) return false;
-    // LDS: staging buffers of the four waves, or the merge area if larger
-    size_t need = 0;
-    switch (a.tk * 3 + a.tv) {
-#define KVQ_CASE(TKV, TVV)                                                               \
-    case TKV * 3 + TVV:                                                                  \
-        if (a.D == 128) { if (!cfg_valid<TKV, TVV, 128>()) return false; need = lds_bytes<TKV, TVV, 128>(a.G); } \
-        else if (a.D == 256) { if (!cfg_valid<TKV, TVV, 256>()) return false; need = lds_bytes<TKV, TVV, 256>(a.G); } \
-        else { return false; } \
-        break;
-        KVQ_CASE(0, 0) KVQ_CASE(0, 1) KVQ_CASE(0, 2)
-        KVQ_CASE(1, 0) KVQ_CASE(1, 1) KVQ_CASE(1, 2)
-        KVQ_CASE(2, 0) KVQ_CASE(2, 1) KVQ_CASE(2, 2)
-#undef KVQ_CASE
-    default: return false;
+    // rows read are below max_seq_len; their offsets inside one (sequence,
+    // KV head) plane are computed in 32 bits
+    const int64_t rows = a.max_seq_len;
+    if (rows * (int64_t)data_row_bytes(a.tk, a.D) >= (1LL << 31)) return false;
+    if (rows * (int64_t)data_row_bytes(a.tv, a.D) >= (1LL << 31)) return false;
+    switch (a.tk) {
+    case T_F16: return supports1<T_F16>(a);
+    case T_Q8: return supports1<T_Q8>(a);
+    default: return supports1<T_Q4>(a);
     }
-    return need <= 160 * 1024;
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s)

@@ -15,7 +15,8 @@ struct AppendArgs {
     int tk, tv;
     const uint16_t* k_new;
     const uint16_t* v_new;
-    const int32_t* positions;
+    const int32_t* positions;  // first row per sequence; or null: seq_lens[b] - n_new
+    const int32_t* seq_lens;
     int B, n_new, Hkv, D;
 };
 
@@ -29,6 +30,16 @@ struct DecodeArgs {
     int max_seq_len, split_tokens, max_splits;
     float* part_o;
     float* part_lse;
+    // fused decode step only (null otherwise): the new K/V row of every
+    // (sequence, KV head), [B][Hkv][D] fp16, written at row seq_lens[b] - 1 by
+    // the workgroup whose split holds that row; and the per-(sequence, KV head)
+    // arrival counters with which the last workgroup merges the splits.
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    uint32_t* counters;
+    bool out_f16;
+    void* out;
+    float* lse_out;
 };
 
 struct CombineArgs {

@@ -1,5 +1,6 @@
-"""Helpers for the GPU parity tests: build caches through the HIP library, run
-the decode path through the C ABI, and compare with the CPU oracle."""
+"""Helpers for the GPU parity tests: caches quantised by the CPU oracle and
+uploaded (so every oracle input is the oracle's own), the decode path run
+through the C ABI, and the comparison with the oracle."""
 from __future__ import annotations
 
 import math
@@ -10,6 +11,7 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
+from oracle import oracle as O  # noqa: E402
 from quantised_kv_long_amd import cache as C  # noqa: E402
 from quantised_kv_long_amd import synth  # noqa: E402
 
@@ -37,24 +39,48 @@ def to_host_u16(x: torch.Tensor) -> np.ndarray:
     return x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def fill_pair(tk, tv, k_f16, v_f16, capacity=None, stream=None):
-    B, Hkv, L, D = k_f16.shape
+def oracle_quantize(t, x_u16: np.ndarray, nthreads: int | None = None):
+    """The oracle's quantiser over (..., D) fp16 bits, with the leading axis cut
+    into chunks run on threads (ctypes releases the GIL; the arithmetic is the
+    oracle's, row by row)."""
+    from concurrent.futures import ThreadPoolExecutor
+    x = np.ascontiguousarray(x_u16)
+    n = x.shape[0]
+    nt = max(1, min(nthreads or oracle_threads(), n))
+    cuts = np.linspace(0, n, nt + 1).astype(int)
+    with ThreadPoolExecutor(nt) as ex:
+        parts = list(ex.map(lambda i: O.quantize(t, x[cuts[i]:cuts[i + 1]]), range(nt)))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
+def oracle_planes(t, x_u16: np.ndarray, capacity: int | None = None):
+    """Planes of rows x (B, Hkv, L, D) fp16 bits quantised by the oracle, padded
+    with zero rows to `capacity`: (type name, data, scales) on the host."""
+    B, Hkv, L, D = x_u16.shape
     cap = capacity or L
-    kc = C.CachePlanes.alloc(tk, B, Hkv, cap, D)
-    vc = C.CachePlanes.alloc(tv, B, Hkv, cap, D)
-    pos = torch.zeros(B, dtype=torch.int32, device=k_f16.device)
-    C.append(kc, vc, k_f16.permute(0, 2, 1, 3).contiguous(), v_f16.permute(0, 2, 1, 3).contiguous(),
-             pos, L, stream)
+    name = t if isinstance(t, str) else {0: "f16", 1: "q8_0", 2: "q4_0"}[t]
+    data, sc = oracle_quantize(name, x_u16.reshape(B * Hkv, L, D))
+    rb = data.shape[-1]
+    d = np.zeros((B, Hkv, cap, rb), np.uint8)
+    s = np.zeros((B, Hkv, cap, D // 32 if name != "f16" else 0), np.uint16)
+    d[:, :, :L] = data.reshape(B, Hkv, L, rb)
+    s[:, :, :L] = sc.reshape(B, Hkv, L, -1)
+    return (name, d, s)
+
+
+def fill_pair(tk, tv, k_f16, v_f16, capacity=None):
+    """Device cache planes holding the oracle's quantisation of k, v (B, Hkv, L,
+    D) fp16; each carries its host copy as `.oracle` for the oracle side."""
+    kh, vh = to_host_u16(k_f16), to_host_u16(v_f16)
+    kc = upload_oracle_planes(*oracle_planes(tk, kh, capacity))
+    vc = upload_oracle_planes(*oracle_planes(tv, vh, capacity))
     return kc, vc
 
 
 def planes_to_oracle(p: C.CachePlanes):
-    """(type name, data uint8 (B,Hkv,C,rb), scales uint16 (B,Hkv,C,nb)) on the host."""
-    name = {0: "f16", 1: "q8_0", 2: "q4_0"}[p.type]
-    data = p.data.cpu().numpy()
-    sc = p.scales.cpu().numpy().view(np.uint16) if p.scales is not None else np.zeros(
-        p.data.shape[:3] + (0,), np.uint16)
-    return (name, data, sc)
+    """The oracle-side (type name, data, scales) of planes built by fill_pair:
+    the oracle's own bytes, never bytes written by the library."""
+    return p.oracle
 
 
 def upload_oracle_planes(name: str, data: np.ndarray, scales: np.ndarray) -> C.CachePlanes:
@@ -64,7 +90,16 @@ def upload_oracle_planes(name: str, data: np.ndarray, scales: np.ndarray) -> C.C
     p.data.copy_(torch.from_numpy(np.ascontiguousarray(data)))
     if p.scales is not None:
         p.scales.copy_(torch.from_numpy(np.ascontiguousarray(scales).view(np.int16)))
+    p.oracle = (name, data, scales)
     return p
+
+
+def download_planes(p: C.CachePlanes):
+    """What the library holds in a cache on the device (for byte comparisons)."""
+    data = p.data.cpu().numpy()
+    sc = p.scales.cpu().numpy().view(np.uint16) if p.scales is not None else np.zeros(
+        p.data.shape[:3] + (0,), np.uint16)
+    return data, sc
 
 
 def run_decode(kc, vc, q, lens, split_tokens, variant="auto", scale=None, out_f16=False):

@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kvq_quantize_append", "kvq_decode_attn", "kvq_combine", "kvq_decode_attn_variant",
-              "kvq_data_row_bytes", "kvq_scale_row_bytes", "kvq_status_string"):
+              "kvq_decode_step", "kvq_data_row_bytes", "kvq_scale_row_bytes", "kvq_status_string"):
         assert n in names
 
 
@@ -186,6 +186,38 @@ def test_combine_validation(lib):
     assert combine(lib, out=A + 1, ot=0) == -4
     assert combine(lib, out=A + 8, ot=3) == -4
     assert combine(lib, lse=A + 2) == -4
+
+
+def step(lib, k=None, v=None, kn=A, vn=A, q=A, lens=A, B=1, Hq=40, Hkv=8, D=128, scale=0.088,
+         max_len=100, split=64, max_splits=2, po=A, pl=A, ctr=A, ot=0, out=A, lse=None):
+    k = k if k is not None else plane()
+    v = v if v is not None else plane()
+    return lib.kvq_decode_step(ctypes.byref(k), ctypes.byref(v), kn, vn, q, lens, B, Hq, Hkv, D,
+                               scale, max_len, split, max_splits, po, pl, ctr, ot, out, lse, None)
+
+
+@nogpu
+def test_decode_step_validation(lib):
+    # the decode arguments are checked exactly as kvq_decode_attn checks them
+    assert step(lib, q=None) == -1
+    assert step(lib, po=None) == -1
+    assert step(lib, Hq=41) == -2
+    assert step(lib, D=1024) == -2
+    assert step(lib, k=plane(t=5)) == -3
+    assert step(lib, max_len=101) == -5
+    assert step(lib, split=100) == -6
+    # and the step's own arguments
+    assert step(lib, kn=None) == -1
+    assert step(lib, vn=None) == -1
+    assert step(lib, ctr=None) == -1
+    assert step(lib, out=None) == -1
+    assert step(lib, ot=1) == -3
+    assert step(lib, ot=2) == -3
+    assert step(lib, kn=A + 2) == -4
+    assert step(lib, vn=A + 8) == -4
+    assert step(lib, ctr=A + 2) == -4
+    assert step(lib, out=A + 8) == -4
+    assert step(lib, lse=A + 2) == -4
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
