@@ -4,8 +4,8 @@
 One step = the whole hot path for every layer of the workload: quantise-on-write
 of one new token per sequence, split-KV decode attention over every row and
 the exact log-sum-exp combine, on inputs already resident in HBM.  The timed
-path is kvq_decode_step (one launch per layer where the matrix-core kernel
-covers the shape); the same step as three calls (kvq_quantize_append,
+path is kvq_decode_step (two launches per layer where the matrix-core kernel
+covers the shape: attention with the new row's write, then the merge); the same step as three calls (kvq_quantize_append,
 kvq_decode_attn, kvq_combine) and the attention launch alone are timed beside
 it and reported per arm.  The default workload is the 48-layer stack at 65536 rows
 (40 query / 8 KV heads, head_dim 128) with the f16, q8_0K/q4_0V and q4_0/q4_0
@@ -114,7 +114,6 @@ class Arm:
         vcode = _lib.VARIANTS[variant]
         scale = 1.0 / math.sqrt(wl.D)
         part = self.part
-        ctr = part.counters(wl.Hkv)
         self.calls = []
         for L in self.layers:
             kd, vd = L["kc"].desc(), L["vc"].desc()
@@ -123,7 +122,7 @@ class Arm:
                 step=(ctypes.byref(kd), ctypes.byref(vd), L["knew"].data_ptr(), L["vnew"].data_ptr(),
                       L["q"].data_ptr(), self.lens_t.data_ptr(), wl.B, wl.Hq, wl.Hkv, wl.D, scale,
                       self.max_len, part.split_tokens, part.max_splits, part.o.data_ptr(),
-                      part.lse.data_ptr(), ctr.data_ptr(), 0, self.out.data_ptr(), None),
+                      part.lse.data_ptr(), 0, self.out.data_ptr(), None),
                 append=(ctypes.byref(kd), ctypes.byref(vd), L["knew"].data_ptr(), L["vnew"].data_ptr(),
                         self.pos.data_ptr(), wl.B, 1, wl.Hkv, wl.D, self.max_len),
                 decode=(ctypes.byref(kd), ctypes.byref(vd), L["q"].data_ptr(), self.lens_t.data_ptr(),

@@ -117,6 +117,8 @@ const char* kvq_status_string(int status);
  *         d = fp16_rne(s / -8); code_i = clamp(round_half_away(x_i / d),
  *         -8, 7) + 8; all codes 8 when d == 0.
  *   f16 : the bits are copied unchanged.
+ * Inputs of the quantised types must be finite: a block holding an infinity
+ * or a NaN gets unspecified codes (the method defines none).
  *
  *   k_cache, v_cache : plane descriptors (host memory, read during the call).
  *   k_new, v_new     : device, [B][n_new][Hkv][D] binary16.
@@ -207,20 +209,16 @@ int kvq_combine(const float* part_o, const float* part_lse, const int32_t* seq_l
  *
  * Results equal kvq_quantize_append (one new row per sequence, written at row
  * seq_lens[b] - 1) followed by kvq_decode_attn and kvq_combine with the same
- * arguments: the cache rows are bit-identical, and out / lse_out agree within
- * floating-point rounding.  Where the matrix-core kernel covers the shape
- * (D = 128 or 256) this is one kernel launch: the workgroup whose split holds
- * row seq_lens[b] - 1 writes that row before reading it, and the last
- * workgroup of each (sequence, KV head) to finish merges the splits of its
- * query heads.  Other shapes run the three kernels in order.
+ * arguments: the cache rows are bit-identical, the split partials are the
+ * same, and out / lse_out agree within floating-point rounding.  Where the
+ * matrix-core kernel covers the shape (D = 128 or 256) the step is two kernel
+ * launches: the attention kernel's workgroup whose split holds row
+ * seq_lens[b] - 1 writes that row before it reads it, then the merge runs.
+ * Other shapes run the three kernels in order.
  *
  *   k_new, v_new : device, [B][Hkv][D] binary16: the new token's K and V rows.
  *   seq_lens     : device, [B] int32: lengths *including* the new token,
  *                  1 <= L_b <= max_seq_len <= capacity.
- *   counters     : device, [B][Hkv] uint32 arrival counters, all zero before
- *                  the first call; every call leaves them zero when it has
- *                  completed.  Calls that may run concurrently (different
- *                  streams) need separate counters and partial buffers.
  *   out_type     : KVQ_F16 or KVQ_OUT_F32.
  *   out          : device, [B][Hq][D] of out_type, 16-byte aligned.
  *   lse_out      : device, [B][Hq] fp32 (natural-log LSE of the scores), or
@@ -232,7 +230,7 @@ int kvq_decode_step(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache
                     const void* k_new, const void* v_new, const void* q, const int32_t* seq_lens,
                     int B, int Hq, int Hkv, int D, float softmax_scale, int max_seq_len,
                     int split_tokens, int max_splits, float* part_o, float* part_lse,
-                    uint32_t* counters, int out_type, void* out, float* lse_out, void* stream);
+                    int out_type, void* out, float* lse_out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -79,7 +79,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_combine.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, P, P, P]
     lib.kvq_combine.restype = i32
     lib.kvq_decode_step.argtypes = [DP, DP, P, P, P, P, i32, i32, i32, i32, f32, i32, i32, i32, P, P,
-                                    P, i32, P, P, P]
+                                    i32, P, P, P]
     lib.kvq_decode_step.restype = i32
     _lib = lib
     return lib
@@ -169,12 +169,12 @@ def kvq_combine(part_o, part_lse, seq_lens, B: int, Hq: int, D: int, split_token
 
 def kvq_decode_step(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, k_new, v_new, q, seq_lens,
                     B: int, Hq: int, Hkv: int, D: int, softmax_scale: float, max_seq_len: int,
-                    split_tokens: int, max_splits: int, part_o, part_lse, counters, out_type, out,
+                    split_tokens: int, max_splits: int, part_o, part_lse, out_type, out,
                     lse_out=None, stream=None) -> int:
     ot = OUT_F32 if out_type in ("f32", OUT_F32) else _tcode(out_type)
     rc = load().kvq_decode_step(ctypes.byref(k_cache), ctypes.byref(v_cache), _ptr(k_new),
                                 _ptr(v_new), _ptr(q), _ptr(seq_lens), B, Hq, Hkv, D,
                                 float(softmax_scale), max_seq_len, split_tokens, max_splits,
-                                _ptr(part_o), _ptr(part_lse), _ptr(counters), ot, _ptr(out),
+                                _ptr(part_o), _ptr(part_lse), ot, _ptr(out),
                                 _ptr(lse_out), _stream(stream))
     return _check("kvq_decode_step", rc)

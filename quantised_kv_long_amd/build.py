@@ -35,6 +35,10 @@ HIP_FLAGS = [
     "-fno-fast-math",
     # LDS tiles are written and read through different pointer types
     "-fno-strict-aliasing",
+    # matrix-core results and accumulators in ordinary VGPRs (the VGPR form of
+    # v_mfma): no accumulator-register copies around every use, and the
+    # head_dim-128 decode kernels fit in 256 registers (two waves per SIMD)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -60,15 +60,6 @@ class Partials:
         self.max_splits = max(1, math.ceil(max_seq_len / split_tokens))
         self.o = torch.empty((B, Hq, self.max_splits, D), dtype=torch.float32, device=device)
         self.lse = torch.empty((B, Hq, self.max_splits), dtype=torch.float32, device=device)
-        self._counters = None
-
-    def counters(self, Hkv: int) -> torch.Tensor:
-        """Arrival counters of kvq_decode_step, [B][Hkv] uint32 (held as int32),
-        zeroed once here; each completed step leaves them zero."""
-        B = self.o.shape[0]
-        if self._counters is None or self._counters.shape != (B, Hkv):
-            self._counters = torch.zeros((B, Hkv), dtype=torch.int32, device=self.o.device)
-        return self._counters
 
 
 def append(kc: CachePlanes, vc: CachePlanes, k_new: torch.Tensor, v_new: torch.Tensor,
@@ -105,4 +96,4 @@ def decode_step(kc: CachePlanes, vc: CachePlanes, k_new: torch.Tensor, v_new: to
     ot = "f16" if out.dtype == torch.float16 else "f32"
     return _lib.kvq_decode_step(kc.desc(), vc.desc(), k_new, v_new, q, seq_lens, B, Hq, kc.Hkv, D,
                                 softmax_scale, max_seq_len, part.split_tokens, part.max_splits,
-                                part.o, part.lse, part.counters(kc.Hkv), ot, out, lse_out, stream)
+                                part.o, part.lse, ot, out, lse_out, stream)

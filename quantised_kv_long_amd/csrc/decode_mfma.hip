@@ -41,7 +41,6 @@
 // partial per (head, split).
 #include <math.h>
 
-#include "kvq_combine.hpp"
 #include "kvq_internal.hpp"
 #include "kvq_quant.hpp"
 
@@ -162,11 +161,11 @@ struct Cfg {
     static constexpr int VS_OFF = V_BYTES + S_BYTES * K_SCALE;
     static constexpr int BUF = V_BYTES + S_BYTES * (K_SCALE + V_SCALE);
     static constexpr int NDT = D / 16;                                 // PV output tiles
+    static constexpr bool DEEP = D == 128;                             // two register sets
     static constexpr float KOFF = TK == T_Q4 ? 8.0f : (TK == T_Q8 ? 128.0f : 0.0f);
     static constexpr uint32_t VOFF_BITS = TV == T_Q4 ? 0x00080008u : 0x00800080u;
     static constexpr bool VALID = V_BYTES % 1024 == 0 && S_BYTES % 256 == 0 && V_DW <= 32 &&
-                                  WAVES * BUF <= 64 * 1024 &&
-                                  4 * CMB_GROUP_LDS_MIN(16) <= WAVES * BUF;
+                                  WAVES * BUF <= 64 * 1024;
 };
 
 template <int TK, int TV, int D>
@@ -187,7 +186,6 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
     const int t_end = min(t_begin + a.split_tokens, L);
     const int h0 = g * G;
     const int64_t ho_stride = (int64_t)a.max_splits * D;
-    const bool fused = a.counters != nullptr;
     float* po = a.part_o + (((int64_t)b * a.Hq + h0) * a.max_splits + s) * D;
     float* pl = a.part_lse + ((int64_t)b * a.Hq + h0) * a.max_splits + s;
 
@@ -204,22 +202,23 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
     const uint8_t* vdata = a.v.data + vrow0 * C::RBV;
     const uint8_t* vscl = reinterpret_cast<const uint8_t*>(a.v.scales + vrow0 * C::NB);
 
-    // ---- fused decode step: the workgroup whose split holds row L-1 first
-    //      quantises the new K and V rows of its KV head into that row (the
-    //      same block quantiser as kvq_quantize_append), then makes them
-    //      visible to its own loads
+    // ---- decode step with the new token: the workgroup whose split holds
+    //      row L-1 first quantises the new K and V rows of its KV head into
+    //      that row (the same block quantiser as kvq_quantize_append), then
+    //      makes them visible to its own loads
     if (a.k_new != nullptr && t_end == L) {
-        if (tid < 2 * C::NB) {
-            const bool isv = tid >= C::NB;
-            const int blk = isv ? tid - C::NB : tid;
+        // 2*NB blocks (K then V), one aligned half-wave of 32 lanes per block
+        for (int blk2 = tid >> 5; blk2 < 2 * C::NB; blk2 += NT / 32) {
+            const bool isv = blk2 >= C::NB;
+            const int blk = isv ? blk2 - C::NB : blk2;
             const uint16_t* src = (isv ? a.v_new : a.k_new) + ((int64_t)b * a.Hkv + g) * D + 32 * blk;
             const int64_t row = (isv ? vrow0 : krow0) + (L - 1);
             if (isv) {
-                quantize_block<TV>(src, a.v.data + row * C::RBV + blk * rb(TV, 32),
-                                   a.v.scales + row * C::NB + blk);
+                quantize_block_lanes<TV>(src, a.v.data + row * C::RBV + blk * rb(TV, 32),
+                                         a.v.scales + row * C::NB + blk, tid & 31);
             } else {
-                quantize_block<TK>(src, a.k.data + row * C::RBK + blk * rb(TK, 32),
-                                   a.k.scales + row * C::NB + blk);
+                quantize_block_lanes<TK>(src, a.k.data + row * C::RBK + blk * rb(TK, 32),
+                                         a.k.scales + row * C::NB + blk, tid & 31);
             }
         }
         // the row is read back only by this workgroup, whose loads of that
@@ -411,14 +410,22 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
 
         // -- online softmax (log2 domain)
         float sv[8];
-        const bool tail = t0 + TT > t_end;
+        const bool tail = t0 + TT > t_end;   // the split's last tile: rows past its end drop out
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float x = sacc[j][i] * cK;
-                sv[4 * j + i] = (tail && t0 + 8 * lq + 4 * j + i >= t_end) ? -INFINITY : x;
+            for (int i = 0; i < 4; ++i) sv[4 * j + i] = sacc[j][i] * cK;
+        if constexpr (C::DEEP) {
+            if (tail) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (t0 + 8 * lq + e >= t_end) sv[e] = -INFINITY;
             }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (tail && t0 + 8 * lq + e >= t_end) sv[e] = -INFINITY;
+        }
         float mx = sv[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
@@ -514,29 +521,64 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
         }
     };
 
-    // ---- main loop over this wave's tiles (it, it+4, ...).  At the top of an
-    //      iteration the K rows of tile `it` are in kr, its V rows and scales
-    //      in LDS, and the V/scale loads of the next tile are in flight in
-    //      vr/sr.  The next tile's K loads are issued as soon as the QK
-    //      products are done; its V rows go to LDS after this tile's PV (a
-    //      wave's LDS reads and writes are performed in order, so one buffer
-    //      suffices).
-    uint32_t kr[2][C::KDW];
-    uint32_t vr[C::V_DW];
-    uint32_t sr[C::S_DW];
+    // ---- main loop over this wave's tiles (it, it+W, ...).  For head_dim
+    //      128 it is unrolled by two with two register sets A/B so that loads
+    //      run far ahead:
+    //      at the top of tile `it` its K rows are in (or on their way to) one
+    //      set, the next tile's K rows are in flight in the other; its V rows
+    //      and scales are in LDS, and the V/scale rows of the next two tiles
+    //      are in flight in vr/sr of both sets.  K of tile it+2W is issued as
+    //      soon as tile it's QK products are done (into the registers they
+    //      free); V of tile it+W goes to LDS after tile it's PV (a wave's LDS
+    //      reads and writes are performed in order, so one buffer suffices),
+    //      and V of tile it+3W is issued into the registers that frees.
+    constexpr int W = WAVES;
     int it = wave;
-    if (it < ntiles) {
-        issue_k(it, kr);
-        issue_vs(it, vr, sr);
-        stage(vr, sr);
-        if (it + WAVES < ntiles) issue_vs(it + WAVES, vr, sr);
-    }
-    for (; it < ntiles; it += WAVES) {
-        const int nx = it + WAVES;
-        compute(it, kr, nx);
-        if (nx < ntiles) {
+    if constexpr (C::DEEP) {
+        uint32_t krA[2][C::KDW], krB[2][C::KDW];
+        uint32_t vrA[C::V_DW], vrB[C::V_DW];
+        uint32_t srA[C::S_DW], srB[C::S_DW];
+        if (it < ntiles) {
+            issue_k(it, krA);
+            issue_vs(it, vrA, srA);
+            if (it + W < ntiles) {
+                issue_k(it + W, krB);
+                issue_vs(it + W, vrB, srB);
+            }
+            stage(vrA, srA);
+            if (it + 2 * W < ntiles) issue_vs(it + 2 * W, vrA, srA);
+        }
+        while (it < ntiles) {
+            compute(it, krA, it + 2 * W);
+            if (it + W >= ntiles) break;
+            stage(vrB, srB);
+            if (it + 3 * W < ntiles) issue_vs(it + 3 * W, vrB, srB);
+            it += W;
+
+            compute(it, krB, it + 2 * W);
+            if (it + W >= ntiles) break;
+            stage(vrA, srA);
+            if (it + 3 * W < ntiles) issue_vs(it + 3 * W, vrA, srA);
+            it += W;
+        }
+    } else {
+        // one register set (head_dim 256 has no room for two): K of the next
+        // tile is issued after this tile's QK, V one tile ahead
+        uint32_t kr[2][C::KDW];
+        uint32_t vr[C::V_DW];
+        uint32_t sr[C::S_DW];
+        if (it < ntiles) {
+            issue_k(it, kr);
+            issue_vs(it, vr, sr);
             stage(vr, sr);
-            if (nx + WAVES < ntiles) issue_vs(nx + WAVES, vr, sr);
+            if (it + W < ntiles) issue_vs(it + W, vr, sr);
+        }
+        for (; it < ntiles; it += W) {
+            compute(it, kr, it + W);
+            if (it + W < ntiles) {
+                stage(vr, sr);
+                if (it + 2 * W < ntiles) issue_vs(it + 2 * W, vr, sr);
+            }
         }
     }
 
@@ -579,50 +621,10 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
             lsum += f * lw[w * 16 + n];
             o += f * ow[(w * G + n) * D + d];
         }
-        const float ov = o / lsum;
-        const float lv = (M + log2f(lsum)) * 0.69314718055994531f;
-        if (fused) {
-            // written through to memory, so the merging workgroup (on any
-            // XCD) reads them after its acquire without an L2 writeback here
-            __hip_atomic_store(po + n * ho_stride + d, ov, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-            if (d == 0)
-                __hip_atomic_store(pl + (int64_t)n * a.max_splits, lv, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_SYSTEM);
-        } else {
-            po[n * ho_stride + d] = ov;
-            if (d == 0) pl[(int64_t)n * a.max_splits] = lv;
-        }
+        po[n * ho_stride + d] = o / lsum;
+        if (d == 0) pl[(int64_t)n * a.max_splits] = (M + log2f(lsum)) * 0.69314718055994531f;
     }
 
-    // ---- fused decode step: the last of the (sequence, KV head)'s non-empty
-    //      splits to finish merges all of them for the G heads of this KV head.
-    //      Release: every thread's partial stores (system scope, written
-    //      through) are complete before the arrival count; acquire: the last
-    //      workgroup invalidates its L2 view before reading the partials.
-    if (fused) {
-        __shared__ int is_last;
-        __builtin_amdgcn_s_waitcnt(VMCNT0);
-        __syncthreads();
-        if (tid == 0) {
-            const int S_b = (L + a.split_tokens - 1) / a.split_tokens;
-            uint32_t* ctr = a.counters + (int64_t)b * a.Hkv + g;
-            const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            is_last = prev == (uint32_t)(S_b - 1);
-            if (is_last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        if (is_last) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            const int S_b = (L + a.split_tokens - 1) / a.split_tokens;
-            const int64_t bh0 = (int64_t)b * a.Hq + h0;
-            void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh0 * D)
-                                  : (void*)(reinterpret_cast<float*>(a.out) + bh0 * D);
-            combine_group<D / 64>(a.part_lse + bh0 * a.max_splits, a.max_splits,
-                                  a.part_o + bh0 * a.max_splits * D, (int64_t)a.max_splits * D, G, S_b,
-                                  D, a.out_f16, out, a.lse_out ? a.lse_out + bh0 : nullptr,
-                                  reinterpret_cast<float*>(lds_a), (int)(sizeof(lds_a) / sizeof(float)));
-        }
-    }
 }
 
 template <int TK, int TV, int D>

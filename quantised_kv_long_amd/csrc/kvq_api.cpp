@@ -88,10 +88,6 @@ kvq::DecodeArgs decode_args(const kvq_plane_desc* k_cache, const kvq_plane_desc*
     a.part_lse = part_lse;
     a.k_new = nullptr;
     a.v_new = nullptr;
-    a.counters = nullptr;
-    a.out_f16 = false;
-    a.out = nullptr;
-    a.lse_out = nullptr;
     return a;
 }
 
@@ -221,16 +217,16 @@ int kvq_combine(const float* part_o, const float* part_lse, const int32_t* seq_l
 int kvq_decode_step(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache, const void* k_new,
                     const void* v_new, const void* q, const int32_t* seq_lens, int B, int Hq, int Hkv,
                     int D, float softmax_scale, int max_seq_len, int split_tokens, int max_splits,
-                    float* part_o, float* part_lse, uint32_t* counters, int out_type, void* out,
-                    float* lse_out, void* stream)
+                    float* part_o, float* part_lse, int out_type, void* out, float* lse_out,
+                    void* stream)
 {
     const int rc = validate_decode(k_cache, v_cache, q, seq_lens, B, Hq, Hkv, D, softmax_scale,
                                    max_seq_len, split_tokens, max_splits, part_o, part_lse);
     if (rc != KVQ_OK) return rc;
-    if (!k_new || !v_new || !counters || !out) return KVQ_ERR_NULL;
+    if (!k_new || !v_new || !out) return KVQ_ERR_NULL;
     if (out_type != KVQ_F16 && out_type != KVQ_OUT_F32) return KVQ_ERR_TYPE;
     if (B > 65535 || Hq > 65535) return KVQ_ERR_SHAPE;
-    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(counters, 4) || !aligned(out, 16) ||
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16) ||
         (lse_out && !aligned(lse_out, 4)))
         return KVQ_ERR_ALIGN;
 
@@ -238,32 +234,29 @@ int kvq_decode_step(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache
                                     max_seq_len, split_tokens, max_splits, part_o, part_lse);
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
+    hipError_t e;
     if (kvq::decode_mfma_supports(a)) {
+        // the attention kernel writes the new row itself
         a.k_new = static_cast<const uint16_t*>(k_new);
         a.v_new = static_cast<const uint16_t*>(v_new);
-        a.counters = counters;
-        a.out_f16 = out_type == KVQ_F16;
-        a.out = out;
-        a.lse_out = lse_out;
-        return finish(kvq::launch_decode_mfma(a, s));
+        e = kvq::launch_decode_mfma(a, s);
+    } else {
+        kvq::AppendArgs ap;
+        ap.k = a.k;
+        ap.v = a.v;
+        ap.tk = a.tk;
+        ap.tv = a.tv;
+        ap.k_new = static_cast<const uint16_t*>(k_new);
+        ap.v_new = static_cast<const uint16_t*>(v_new);
+        ap.positions = nullptr;  // row seq_lens[b] - 1
+        ap.seq_lens = seq_lens;
+        ap.B = B;
+        ap.n_new = 1;
+        ap.Hkv = Hkv;
+        ap.D = D;
+        e = kvq::launch_quantize_append(ap, s);
+        if (e == hipSuccess) e = kvq::launch_decode_valu(a, s);
     }
-
-    kvq::AppendArgs ap;
-    ap.k = a.k;
-    ap.v = a.v;
-    ap.tk = a.tk;
-    ap.tv = a.tv;
-    ap.k_new = static_cast<const uint16_t*>(k_new);
-    ap.v_new = static_cast<const uint16_t*>(v_new);
-    ap.positions = nullptr;  // row seq_lens[b] - 1
-    ap.seq_lens = seq_lens;
-    ap.B = B;
-    ap.n_new = 1;
-    ap.Hkv = Hkv;
-    ap.D = D;
-    hipError_t e = kvq::launch_quantize_append(ap, s);
-    if (e != hipSuccess) return KVQ_ERR_LAUNCH;
-    e = kvq::launch_decode_valu(a, s);
     if (e != hipSuccess) return KVQ_ERR_LAUNCH;
 
     kvq::CombineArgs c;

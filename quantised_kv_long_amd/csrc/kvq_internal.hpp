@@ -30,16 +30,11 @@ struct DecodeArgs {
     int max_seq_len, split_tokens, max_splits;
     float* part_o;
     float* part_lse;
-    // fused decode step only (null otherwise): the new K/V row of every
-    // (sequence, KV head), [B][Hkv][D] fp16, written at row seq_lens[b] - 1 by
-    // the workgroup whose split holds that row; and the per-(sequence, KV head)
-    // arrival counters with which the last workgroup merges the splits.
+    // decode step only (null otherwise): the new K/V row of every (sequence,
+    // KV head), [B][Hkv][D] fp16, written at row seq_lens[b] - 1 by the
+    // workgroup whose split holds that row, before it reads it
     const uint16_t* k_new;
     const uint16_t* v_new;
-    uint32_t* counters;
-    bool out_f16;
-    void* out;
-    float* lse_out;
 };
 
 struct CombineArgs {

@@ -102,5 +102,73 @@ __device__ __forceinline__ void quantize_block(const uint16_t* __restrict__ src,
     }
 }
 
+// The same block quantiser with one lane per value: the 32 lanes of an
+// aligned half-wave (j = lane & 31) quantise the block at src together, with
+// the block maximum found by cross-lane exchanges.  Every lane performs the
+// same float operations on its value as quantize_block does, so the bytes are
+// identical.  All 32 lanes of the half-wave must call it together.
+template <int T>
+__device__ __forceinline__ void quantize_block_lanes(const uint16_t* __restrict__ src,
+                                                     uint8_t* __restrict__ dst,
+                                                     uint16_t* __restrict__ sdst, int j)
+{
+    if constexpr (T == T_F16) {
+        if (j < 4) reinterpret_cast<uint4*>(dst)[j] = reinterpret_cast<const uint4*>(src)[j];
+        return;
+    } else {
+        const float x = h2f(src[j]);
+        if constexpr (T == T_Q8) {
+            float amax = fmaxf(0.0f, fabsf(x));   // as the sequential fold from 0 (NaN drops out)
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+            const uint16_t d16 = f2h_rne(amax / 127.0f);
+            const float d = h2f(d16);
+            uint32_t c = 0;
+            if (d != 0.0f) {
+                float r = roundf(x / d);
+                r = fminf(fmaxf(r, -127.0f), 127.0f);
+                c = (uint32_t)(uint8_t)(int8_t)(int)r;
+            }
+            const uint32_t w = c | (__shfl_down(c, 1, 32) << 8) | (__shfl_down(c, 2, 32) << 16) |
+                               (__shfl_down(c, 3, 32) << 24);
+            if ((j & 3) == 0) *reinterpret_cast<uint32_t*>(dst + j) = w;
+            if (j == 0) *sdst = d16;
+        } else {
+            // first value of largest magnitude: a value is a candidate when
+            // its magnitude exceeds 0 (NaN never is); larger magnitude wins,
+            // then the lower index.  No candidate: s = +0.
+            const float ax = fabsf(x);
+            float a = ax > 0.0f ? ax : 0.0f;
+            int idx = a > 0.0f ? j : 32;
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1) {
+                const float a2 = __shfl_xor(a, off, 32);
+                const int i2 = __shfl_xor(idx, off, 32);
+                if (a2 > a || (a2 == a && i2 < idx)) {
+                    a = a2;
+                    idx = i2;
+                }
+            }
+            const float xs = __shfl(x, idx & 31, 32);
+            const float smax = idx < 32 ? xs : 0.0f;
+            const uint16_t mag16 = f2h_rne(fabsf(smax) * 0.125f);
+            const uint16_t d16 = (uint16_t)(mag16 | (smax < 0.0f ? 0 : 0x8000));
+            const float d = h2f(d16);
+            uint32_t n = 8;
+            if (d != 0.0f) {
+                float r = roundf(x / d);
+                r = fminf(fmaxf(r, -8.0f), 7.0f);
+                n = (uint32_t)((int)r + 8);
+            }
+            // byte j (< 16) holds element j (low nibble) and element j+16
+            const uint32_t byte = n | (__shfl_down(n, 16, 32) << 4);
+            const uint32_t w = (byte & 0xff) | ((__shfl_down(byte, 1, 32) & 0xff) << 8) |
+                               ((__shfl_down(byte, 2, 32) & 0xff) << 16) |
+                               ((__shfl_down(byte, 3, 32) & 0xff) << 24);
+            if (j < 16 && (j & 3) == 0) *reinterpret_cast<uint32_t*>(dst + j) = w;
+            if (j == 0) *sdst = d16;
+        }
+    }
+}
 
 }  // namespace kvq

@@ -119,13 +119,13 @@ WORKLOADS = {
         "48-layer decode stack: 40 query / 8 KV heads, head_dim 128, ctx 65536, batch 1; per "
         "layer append one token then attend; N(0,1)",
         layers=48, B=1, Hq=40, Hkv=8, D=128, ctx=65536,
-        arms=[("f16", "f16"), ("q8_0", "q4_0"), ("q4_0", "q4_0")], seed=1003, split_tokens=512),
+        arms=[("f16", "f16"), ("q8_0", "q4_0"), ("q4_0", "q4_0")], seed=1003, split_tokens=1024),
     "long_d128_ctx256k": Workload(
         "long_d128_ctx256k",
         "one layer, 40 query / 8 KV heads, head_dim 128, ctx 262144, batch 1; keys N(0,1) with "
         "one planted needle row of cosine 0.9 to the group's first query head",
         layers=1, B=1, Hq=40, Hkv=8, D=128, ctx=262144, arms=[("q8_0", "q4_0"), ("q4_0", "q4_0")],
-        seed=1004, split_tokens=2048, needle=True),
+        seed=1004, split_tokens=4096, needle=True),
     "batch16_ragged": Workload(
         "batch16_ragged",
         "16 sequences, ctx uniform in [16384, 131072], 40 query / 8 KV heads, head_dim 128; "

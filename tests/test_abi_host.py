@@ -189,11 +189,11 @@ def test_combine_validation(lib):
 
 
 def step(lib, k=None, v=None, kn=A, vn=A, q=A, lens=A, B=1, Hq=40, Hkv=8, D=128, scale=0.088,
-         max_len=100, split=64, max_splits=2, po=A, pl=A, ctr=A, ot=0, out=A, lse=None):
+         max_len=100, split=64, max_splits=2, po=A, pl=A, ot=0, out=A, lse=None):
     k = k if k is not None else plane()
     v = v if v is not None else plane()
     return lib.kvq_decode_step(ctypes.byref(k), ctypes.byref(v), kn, vn, q, lens, B, Hq, Hkv, D,
-                               scale, max_len, split, max_splits, po, pl, ctr, ot, out, lse, None)
+                               scale, max_len, split, max_splits, po, pl, ot, out, lse, None)
 
 
 @nogpu
@@ -209,13 +209,11 @@ def test_decode_step_validation(lib):
     # and the step's own arguments
     assert step(lib, kn=None) == -1
     assert step(lib, vn=None) == -1
-    assert step(lib, ctr=None) == -1
     assert step(lib, out=None) == -1
     assert step(lib, ot=1) == -3
     assert step(lib, ot=2) == -3
     assert step(lib, kn=A + 2) == -4
     assert step(lib, vn=A + 8) == -4
-    assert step(lib, ctr=A + 2) == -4
     assert step(lib, out=A + 8) == -4
     assert step(lib, lse=A + 2) == -4
 
