@@ -33,6 +33,38 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attn KV GB/s (stored bytes) and % of MI355X HBM peak; µs/step at 64k–256k"
 HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+# sources of the attention kernel: a traffic record taken from the counters is
+# used only while these are unchanged
+KERNEL_SOURCES = ["decode_mfma.hip", "kvq_device.hpp", "kvq_internal.hpp", "kvq_quant.hpp"]
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantised_kv_long_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_record(workload: str, tk: str, tv: str):
+    """Measured HBM bytes per launch of the attention kernel for this workload
+    and arm, from a committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE per dispatch, scaled by the calibration on a copy of known
+    size), or None when there is none for the current kernel sources."""
+    import glob
+    import re
+    sha = kernel_sources_sha256()
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*.md"))):
+        for line in open(path, encoding="utf-8"):
+            if not line.startswith("traffic-record:"):
+                continue
+            kv = dict(re.findall(r"(\w+)=(\S+)", line))
+            if (kv.get("workload") == workload and kv.get("arm") == f"{tk}/{tv}"
+                    and kv.get("sources_sha256") == sha):
+                return int(kv["fetch_bytes"]), int(kv["write_bytes"]), os.path.basename(path)
+    return None
 
 
 def parse():
@@ -309,6 +341,17 @@ def main():
     if "f16/f16" in results and "q8_0/q4_0" in results:
         ratios["q8q4_over_f16_speedup"] = round(results["f16/f16"]["us_per_step"] /
                                                 results["q8_0/q4_0"]["us_per_step"], 3)
+    dec_us = h["decode_only_us_per_launch"]
+    achieved = head_arm.stored_bytes_layer / (dec_us * 1e-6) / 1e9
+    rec = traffic_record(wl.name, headline[0], headline[1])
+    traffic = None
+    if rec is not None:
+        traffic = round((rec[0] + rec[1]) / (dec_us * 1e-6) / 1e9, 1)
+        log(f"traffic from {rec[2]}: {rec[0] + rec[1]} bytes per launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "decode_mfma_kernel", "avg_launch_us": dec_us,
+                "algorithmic_bytes_per_launch": head_arm.stored_bytes_layer}
     line = {
         "metric": METRIC,
         "value": h["GBps"],
@@ -326,13 +369,10 @@ def main():
                    "layers": wl.layers, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
                    "head_dim": wl.D, "ctx": wl.ctx, "split_tokens": split_tokens,
                    "path": "kvq_decode_step", "graph": not args.no_graph},
-        # the step is one launch per layer: its average launch duration is the
-        # step time over the layers (gaps between graph-replayed launches included)
-        "roofline": {"bound": "hbm", "achieved": round(h["GBps"], 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(h["GBps"] / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "decode_mfma_kernel (kvq_decode_step)",
-                     "avg_launch_us": h["step_us_per_layer"],
-                     "algorithmic_bytes_per_launch": head_arm.stored_bytes_layer},
+        # the dominant kernel is the split-KV attention kernel: its average
+        # launch duration is measured with HIP events around graph replays of
+        # that launch alone (one per layer, back to back)
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "arms": results,
         "ratios": ratios,

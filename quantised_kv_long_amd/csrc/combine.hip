@@ -19,8 +19,14 @@ __global__ void __launch_bounds__(CMB_NT) combine_kernel(CombineArgs a)
     const int64_t bh = (int64_t)b * a.Hq + h;
     void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh * a.D)
                           : (void*)(reinterpret_cast<float*>(a.out) + bh * a.D);
-    combine_rows(a.part_lse + bh * a.max_splits, a.part_o + bh * a.max_splits * a.D, S, a.D,
-                 a.out_f16, out, a.lse_out ? a.lse_out + bh : nullptr, sm);
+    const float* pl = a.part_lse + bh * a.max_splits;
+    const float* po = a.part_o + bh * a.max_splits * a.D;
+    float* lse = a.lse_out ? a.lse_out + bh : nullptr;
+    // one batch of loads covers S <= 8 * (256 / (D / 4)) splits with U = 8
+    if (S <= 8 * (CMB_NT / (a.D / 4)))
+        combine_rows<8>(pl, po, S, a.D, a.out_f16, out, lse, sm);
+    else
+        combine_rows<16>(pl, po, S, a.D, a.out_f16, out, lse, sm);
 }
 
 }  // namespace

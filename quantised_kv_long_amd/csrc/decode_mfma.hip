@@ -23,9 +23,10 @@
 //     values of one 32-value block, B = the GQA group's Q (16 columns, G
 //     used).  One MFMA per block; its fp32 result is multiplied by the row's
 //     block scale (exact products, fp32 sums).  K goes straight from HBM to
-//     registers with coalesced 16-byte loads; a 4x4 exchange between the four
-//     16-lane rows (v_permlane32_swap / v_permlane16_swap) turns "lane row q
-//     holds block q" into "lane row q holds a quarter of every block".
+//     registers with coalesced 16-byte loads; for q8_0 / q4_0 a 4x4 exchange
+//     between the four 16-lane rows (v_permlane32_swap / v_permlane16_swap)
+//     turns "lane row q holds block q" into "lane row q holds a quarter of
+//     every block" (f16 rows are loaded in that layout directly).
 //   online softmax in fp32, log2 domain; the running maximum is only moved
 //     when a score exceeds it by more than 2^8 (exact either way: every
 //     partial sum is kept relative to the same reference), so rescaling the
@@ -161,15 +162,30 @@ struct Cfg {
     static constexpr int VS_OFF = V_BYTES + S_BYTES * K_SCALE;
     static constexpr int BUF = V_BYTES + S_BYTES * (K_SCALE + V_SCALE);
     static constexpr int NDT = D / 16;                                 // PV output tiles
-    static constexpr bool DEEP = D == 128;                             // two register sets
+    // register sets of the load ring: two for head_dim 128 (a third, where
+    // it fits in 256 registers, measured slower), one for head_dim 256
+    static constexpr int NSET = D == 128 ? 2 : 1;
     static constexpr float KOFF = TK == T_Q4 ? 8.0f : (TK == T_Q8 ? 128.0f : 0.0f);
     static constexpr uint32_t VOFF_BITS = TV == T_Q4 ? 0x00080008u : 0x00800080u;
     static constexpr bool VALID = V_BYTES % 1024 == 0 && S_BYTES % 256 == 0 && V_DW <= 32 &&
                                   WAVES * BUF <= 64 * 1024;
 };
 
+// Bytes of the four-wave merge area: per wave and head the running max, sum
+// and weight, the V offset sums per block, the corrections, and the G x D
+// accumulators of every wave.
 template <int TK, int TV, int D>
-__global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
+__host__ __device__ constexpr size_t merge_lds_bytes(int G)
+{
+    return sizeof(float) * ((size_t)WAVES * 16 * 3 + (size_t)WAVES * 16 * (D / 32) + 16 * (D / 32) +
+                            (size_t)WAVES * G * D);
+}
+
+// head_dim 128 is built for two waves per SIMD (at most 256 registers);
+// head_dim 256 needs more and runs one
+template <int TK, int TV, int D>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1)))
+decode_mfma_kernel(DecodeArgs a)
 {
     using C = Cfg<TK, TV, D>;
     // One LDS buffer per wave: the V rows of the current tile, then the K and
@@ -229,26 +245,36 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
     }
 
     // ---- Q as the B operand of S^T = K Q^T: column ln = head, lane row lq
+    //      holds k-slots 8*lq .. 8*lq+7 of each block, in the element order
+    //      the K codes arrive in (q8_0 / f16: elements 8*lq .. 8*lq+7; q4_0:
+    //      4*lq + {0, 2, 16, 18, 1, 3, 17, 19}, the nibble order of one dword)
     half8 qop[C::NB];
     floatx4 kbias[C::NB];
     {
         const uint16_t* qh = a.q + ((int64_t)b * a.Hq + h0 + min(ln, G - 1)) * D;
+        const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
         for (int kb = 0; kb < C::NB; ++kb) {
+            uint32_t w[4];
+            if constexpr (TK == T_Q4) {
+                const u32x2 ra = *reinterpret_cast<const u32x2*>(qh + 32 * kb + 4 * lq);
+                const u32x2 rb = *reinterpret_cast<const u32x2*>(qh + 32 * kb + 4 * lq + 16);
+                w[0] = __builtin_amdgcn_perm((uint32_t)ra[1], (uint32_t)ra[0], 0x05040100u);
+                w[1] = __builtin_amdgcn_perm((uint32_t)rb[1], (uint32_t)rb[0], 0x05040100u);
+                w[2] = __builtin_amdgcn_perm((uint32_t)ra[1], (uint32_t)ra[0], 0x07060302u);
+                w[3] = __builtin_amdgcn_perm((uint32_t)rb[1], (uint32_t)rb[0], 0x07060302u);
+            } else {
+                const u32x4 r = *reinterpret_cast<const u32x4*>(qh + 32 * kb + 8 * lq);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) w[c] = (uint32_t)r[c];
+            }
             float part = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                int el;
-                if constexpr (TK == T_Q4) {
-                    const int p = e >> 1, hi = e & 1, nib = p + 4 * hi;
-                    el = 4 * lq + (nib >> 1) + 16 * (nib & 1);
-                } else {
-                    el = 8 * lq + e;
-                }
-                const _Float16 qv = __builtin_bit_cast(_Float16, qh[32 * kb + el]);
-                qop[kb][e] = ln < G ? qv : (_Float16)0.0f;
-                part += (float)qop[kb][e];
+            for (int c = 0; c < 4; ++c) {
+                if (ln >= G) w[c] = 0;
+                part = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, w[c]), one2, part, false);
             }
+            qop[kb] = make_half8(w[0], w[1], w[2], w[3]);
             // the accumulator's start removes the code offset exactly once
             const float bias = -C::KOFF * TWOM24 * xsum4(part);
             kbias[kb] = floatx4{bias, bias, bias, bias};
@@ -270,49 +296,98 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
     const int ntiles = (t_end - t_begin + TT - 1) / TT;
     // K row of subtile j read by this lane (tile-relative): rows of the A
     // operand are ordered so that the score layout gives lane row lq the rows
-    // 8*lq .. 8*lq+7 of the tile
+    // 8*lq .. 8*lq+7 of the tile.  Lane (ln, lq) needs k-slots 8*lq .. 8*lq+7
+    // of every block: its quarter lq of the block (QB bytes).
+    //   f16 (QB = 16): each lane loads its quarters directly, 16 bytes each.
+    //   q8_0 / q4_0: 16-byte loads stay coalesced: lane row lq loads the whole
+    //   of block 4*bg + lq (BB bytes), and a 4x4 exchange between lane rows
+    //   (xpose4) then gives each lane row its quarter of every block.
+    constexpr int QB = 4 * C::KU;                  // bytes of a block quarter
+    constexpr int BB = C::RBK / C::NB;             // bytes of a block
+    constexpr bool KDIRECT = C::KU == 4;
     const int krow_rel0 = 8 * (ln >> 2) + (ln & 3);
-    const int kpiece = lq * (16 * C::KU);
+    const uint32_t kpart = (uint32_t)(lq * (KDIRECT ? QB : BB));
+    const uint32_t klane0 = (uint32_t)(krow_rel0 * C::RBK) + kpart;
+    const uint32_t klane1 = (uint32_t)((krow_rel0 + 4) * C::RBK) + kpart;
+
+    // one K row's share of this lane (p: the row start plus kpart)
+    auto load_k_row = [&](const uint8_t* p, uint32_t (&x)[C::KDW]) {
+        if constexpr (KDIRECT) {
+#pragma unroll
+            for (int kb = 0; kb < C::NB; ++kb) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(p + kb * BB);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) x[4 * kb + c] = v[c];
+            }
+        } else {
+#pragma unroll
+            for (int bg = 0; bg < C::NBG; ++bg)
+#pragma unroll
+                for (int u = 0; u < C::KU; ++u) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(p + bg * 4 * BB + 16 * u);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) x[(bg * C::KU + u) * 4 + c] = v[c];
+                }
+        }
+    };
 
     // ---- global loads of tile `it` into registers: K rows in the MFMA layout
     //      (issue_k), and the V rows and scale rows (issue_vs) that stage()
-    //      then copies to this wave's LDS buffer
+    //      then copies to this wave's LDS buffer.  A tile whose rows all lie
+    //      below L is one contiguous range per plane, addressed as a uniform
+    //      tile base plus a per-lane offset; only a split's last tile clamps
+    //      its rows to L - 1 (rows past L are masked out of the softmax).
     auto issue_k = [&](int it, uint32_t (&kr)[2][C::KDW]) {
         const int t0 = t_begin + it * TT;
+        if (t0 + TT <= L) {
+            const uint8_t* base = kdata + (uint32_t)(t0 * C::RBK);
+            load_k_row(base + klane0, kr[0]);
+            load_k_row(base + klane1, kr[1]);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int tok = min(t0 + krow_rel0 + 4 * j, L - 1);
-            const uint8_t* row = kdata + (uint32_t)(tok * C::RBK) + kpiece;
-#pragma unroll
-            for (int bg = 0; bg < C::NBG; ++bg) {
-#pragma unroll
-                for (int u = 0; u < C::KU; ++u) {
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(row + bg * (C::RBK / C::NBG) + 16 * u);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) kr[j][(bg * C::KU + u) * 4 + c] = v[c];
-                }
+            for (int j = 0; j < 2; ++j) {
+                const int tok = min(t0 + krow_rel0 + 4 * j, L - 1);
+                load_k_row(kdata + (uint32_t)(tok * C::RBK) + kpart, kr[j]);
             }
         }
     };
     auto issue_vs = [&](int it, uint32_t (&vr)[C::V_DW], uint32_t (&sr)[C::S_DW]) {
         const int t0 = t_begin + it * TT;
+        if (t0 + TT <= L) {
+            const uint8_t* vbase = vdata + (uint32_t)(t0 * C::RBV) + 16 * lane;
 #pragma unroll
-        for (int k = 0; k < C::V_LOADS; ++k) {
-            const int c16 = k * 64 + lane;
-            const int tok = min(t0 + c16 / (C::RBV / 16), L - 1);
-            const u32x4 v = *reinterpret_cast<const u32x4*>(
-                vdata + (uint32_t)(tok * C::RBV) + 16 * (c16 % (C::RBV / 16)));
+            for (int k = 0; k < C::V_LOADS; ++k) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(vbase + 1024 * k);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) vr[4 * k + c] = v[c];
-        }
+                for (int c = 0; c < 4; ++c) vr[4 * k + c] = v[c];
+            }
+            const uint32_t soff = (uint32_t)(t0 * (2 * C::NB)) + 4 * lane;
 #pragma unroll
-        for (int k = 0; k < C::S_LOADS; ++k) {
-            const int c4 = k * 64 + lane;
-            const int tok = min(t0 + c4 / (C::NB / 2), L - 1);
-            const uint32_t off = (uint32_t)(tok * (2 * C::NB)) + 4 * (c4 % (C::NB / 2));
-            if constexpr (C::K_SCALE) sr[k] = *reinterpret_cast<const uint32_t*>(kscl + off);
-            if constexpr (C::V_SCALE)
-                sr[C::K_SCALE * C::S_LOADS + k] = *reinterpret_cast<const uint32_t*>(vscl + off);
+            for (int k = 0; k < C::S_LOADS; ++k) {
+                if constexpr (C::K_SCALE) sr[k] = *reinterpret_cast<const uint32_t*>(kscl + soff + 256 * k);
+                if constexpr (C::V_SCALE)
+                    sr[C::K_SCALE * C::S_LOADS + k] =
+                        *reinterpret_cast<const uint32_t*>(vscl + soff + 256 * k);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < C::V_LOADS; ++k) {
+                const int c16 = k * 64 + lane;
+                const int tok = min(t0 + c16 / (C::RBV / 16), L - 1);
+                const u32x4 v = *reinterpret_cast<const u32x4*>(
+                    vdata + (uint32_t)(tok * C::RBV) + 16 * (c16 % (C::RBV / 16)));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) vr[4 * k + c] = v[c];
+            }
+#pragma unroll
+            for (int k = 0; k < C::S_LOADS; ++k) {
+                const int c4 = k * 64 + lane;
+                const int tok = min(t0 + c4 / (C::NB / 2), L - 1);
+                const uint32_t off = (uint32_t)(tok * (2 * C::NB)) + 4 * (c4 % (C::NB / 2));
+                if constexpr (C::K_SCALE) sr[k] = *reinterpret_cast<const uint32_t*>(kscl + off);
+                if constexpr (C::V_SCALE)
+                    sr[C::K_SCALE * C::S_LOADS + k] = *reinterpret_cast<const uint32_t*>(vscl + off);
+            }
         }
     };
 
@@ -357,17 +432,18 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             uint32_t* x = kr[j];
-            // exchange: lane row lq loaded all of block (4*bg + lq), dword
-            // delta at x[bg*4*KU + delta]; quarter w of a block is dwords
-            // [w*KU, (w+1)*KU).  Afterwards lane row lq holds quarter lq of
-            // block 4*bg + w at x[bg*4*KU + w*KU + v].
+            if constexpr (!KDIRECT) {
+                // lane row lq loaded all of block 4*bg + lq (dwords bg*4*KU +
+                // [0, 4*KU)); afterwards it holds quarter lq of block 4*bg + w
+                // at x[bg*4*KU + w*KU + v]
 #pragma unroll
-            for (int bg = 0; bg < C::NBG; ++bg) {
-                uint32_t* base = x + bg * 4 * C::KU;
+                for (int bg = 0; bg < C::NBG; ++bg) {
+                    uint32_t* base = x + bg * 4 * C::KU;
 #pragma unroll
-                for (int u = 0; u < C::KU; ++u)
-                    xpose4(base[0 * C::KU + u], base[1 * C::KU + u], base[2 * C::KU + u],
-                           base[3 * C::KU + u]);
+                    for (int u = 0; u < C::KU; ++u)
+                        xpose4(base[0 * C::KU + u], base[1 * C::KU + u], base[2 * C::KU + u],
+                               base[3 * C::KU + u]);
+                }
             }
             floatx4 cb[C::NB];
 #pragma unroll
@@ -415,7 +491,7 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) sv[4 * j + i] = sacc[j][i] * cK;
-        if constexpr (C::DEEP) {
+        if constexpr (C::NSET > 1) {
             if (tail) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
@@ -521,80 +597,72 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
         }
     };
 
-    // ---- main loop over this wave's tiles (it, it+W, ...).  For head_dim
-    //      128 it is unrolled by two with two register sets A/B so that loads
-    //      run far ahead:
-    //      at the top of tile `it` its K rows are in (or on their way to) one
-    //      set, the next tile's K rows are in flight in the other; its V rows
-    //      and scales are in LDS, and the V/scale rows of the next two tiles
-    //      are in flight in vr/sr of both sets.  K of tile it+2W is issued as
-    //      soon as tile it's QK products are done (into the registers they
-    //      free); V of tile it+W goes to LDS after tile it's PV (a wave's LDS
-    //      reads and writes are performed in order, so one buffer suffices),
-    //      and V of tile it+3W is issued into the registers that frees.
+    // ---- main loop over this wave's tiles (it, it+W, ...), with a ring of
+    //      NS register sets so that loads run ahead: K of tile it+NS*W is
+    //      issued as soon as tile it's QK products are done (into the
+    //      registers they free); after tile it's PV the V rows and scales of
+    //      tile it+W go to LDS (a wave's LDS reads and writes are performed in
+    //      order, so one buffer suffices) and V of tile it+(NS+1)*W is issued
+    //      into the registers that frees.
     constexpr int W = WAVES;
+    constexpr int NS = C::NSET;
     int it = wave;
-    if constexpr (C::DEEP) {
-        uint32_t krA[2][C::KDW], krB[2][C::KDW];
-        uint32_t vrA[C::V_DW], vrB[C::V_DW];
-        uint32_t srA[C::S_DW], srB[C::S_DW];
-        if (it < ntiles) {
-            issue_k(it, krA);
-            issue_vs(it, vrA, srA);
-            if (it + W < ntiles) {
-                issue_k(it + W, krB);
-                issue_vs(it + W, vrB, srB);
+    uint32_t krs[NS][2][C::KDW];
+    uint32_t vrs[NS][C::V_DW];
+    uint32_t srs[NS][C::S_DW];
+    if (it < ntiles) {
+#pragma unroll
+        for (int x = 0; x < NS; ++x)
+            if (it + x * W < ntiles) {
+                issue_k(it + x * W, krs[x]);
+                issue_vs(it + x * W, vrs[x], srs[x]);
             }
-            stage(vrA, srA);
-            if (it + 2 * W < ntiles) issue_vs(it + 2 * W, vrA, srA);
-        }
-        while (it < ntiles) {
-            compute(it, krA, it + 2 * W);
-            if (it + W >= ntiles) break;
-            stage(vrB, srB);
-            if (it + 3 * W < ntiles) issue_vs(it + 3 * W, vrB, srB);
-            it += W;
-
-            compute(it, krB, it + 2 * W);
-            if (it + W >= ntiles) break;
-            stage(vrA, srA);
-            if (it + 3 * W < ntiles) issue_vs(it + 3 * W, vrA, srA);
-            it += W;
-        }
-    } else {
-        // one register set (head_dim 256 has no room for two): K of the next
-        // tile is issued after this tile's QK, V one tile ahead
-        uint32_t kr[2][C::KDW];
-        uint32_t vr[C::V_DW];
-        uint32_t sr[C::S_DW];
-        if (it < ntiles) {
-            issue_k(it, kr);
-            issue_vs(it, vr, sr);
-            stage(vr, sr);
-            if (it + W < ntiles) issue_vs(it + W, vr, sr);
-        }
-        for (; it < ntiles; it += W) {
-            compute(it, kr, it + W);
-            if (it + W < ntiles) {
-                stage(vr, sr);
-                if (it + 2 * W < ntiles) issue_vs(it + 2 * W, vr, sr);
+        stage(vrs[0], srs[0]);
+        if (it + NS * W < ntiles) issue_vs(it + NS * W, vrs[0], srs[0]);
+    }
+    // tile it uses K set x; V of tile it is in LDS, V of the next tile in set
+    // (x + 1) % NS
+    bool done = it >= ntiles;
+    while (!done) {
+#pragma unroll
+        for (int x = 0; x < NS; ++x) {
+            if (!done) {
+                compute(it, krs[x], it + NS * W);
+                if (it + W >= ntiles) {
+                    done = true;
+                } else {
+                    const int y = (x + 1) % NS;
+                    stage(vrs[y], srs[y]);
+                    if (it + (NS + 1) * W < ntiles) issue_vs(it + (NS + 1) * W, vrs[y], srs[y]);
+                    it += W;
+                }
             }
         }
     }
 
-    // ---- merge the four waves: (m, l, O) per head through LDS
+    // ---- merge the four waves: (m, l, O) per head through LDS.  Each lane
+    //      stores its raw accumulators; one thread per head then forms the
+    //      waves' weights (and the V code-offset correction per block), and
+    //      every output column is a four-term weighted sum.
     const float l_head = xsum4(l_part);
     __syncthreads();
-    const size_t merge_bytes = sizeof(float) * ((size_t)WAVES * 32 + (size_t)WAVES * G * D);
-    uint8_t* marea = merge_bytes <= sizeof(lds_a) ? lds_a : lds_merge_dyn;
-    float* mw = reinterpret_cast<float*>(marea);          // [WAVES][16]
-    float* lw = mw + WAVES * 16;                          // [WAVES][16]
-    float* ow = lw + WAVES * 16;                          // [WAVES][G][D]
+    uint8_t* marea = merge_lds_bytes<TK, TV, D>(G) <= sizeof(lds_a) ? lds_a : lds_merge_dyn;
+    float* mw = reinterpret_cast<float*>(marea);          // [WAVES][16]   running max
+    float* lw = mw + WAVES * 16;                          // [WAVES][16]   running sum
+    float* fw = lw + WAVES * 16;                          // [WAVES][16]   merge weights
+    float* bw = fw + WAVES * 16;                          // [WAVES][16][NB] V offset sums
+    float* corr = bw + WAVES * 16 * C::NB;                // [16][NB]      corrections
+    float* ow = corr + 16 * C::NB;                        // [WAVES][G][D] accumulators
     if (lq == 0) {
         mw[wave * 16 + ln] = m_ref;
         lw[wave * 16 + ln] = l_head;
+        if constexpr (C::V_SCALE) {
+#pragma unroll
+            for (int kb = 0; kb < C::NB; ++kb) bw[(wave * 16 + ln) * C::NB + kb] = bacc[kb][0];
+        }
     }
     if (ln < G) {
+        float* orow = ow + (wave * G + ln) * D;
 #pragma unroll
         for (int t = 0; t < C::NDT; ++t)
 #pragma unroll
@@ -603,28 +671,58 @@ __global__ void __launch_bounds__(NT) decode_mfma_kernel(DecodeArgs a)
                 int d;
                 if constexpr (TV == T_Q4) d = 32 * (t >> 1) + 8 * (t & 1) + (m >> 1) + 16 * (m & 1);
                 else d = 16 * t + m;
-                float o = oacc[t][i];
-                if constexpr (C::V_SCALE) o = (o - bacc[t >> 1][i]) * TWO24;
-                ow[(wave * G + ln) * D + d] = o;
+                orow[d] = oacc[t][i];
             }
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += NT) {
-        const int n = idx / D, d = idx % D;
+    if (tid < G) {
+        const int n = tid;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mw[w * 16 + n]);
-        float lsum = 0.0f, o = 0.0f;
+        float f[WAVES], lsum = 0.0f;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
-            const float f = exp2f(mw[w * 16 + n] - M);   // exp2(-inf) = 0 for idle waves
-            lsum += f * lw[w * 16 + n];
-            o += f * ow[(w * G + n) * D + d];
+            f[w] = exp2f(mw[w * 16 + n] - M);     // exp2(-inf) = 0 for idle waves
+            lsum += f[w] * lw[w * 16 + n];
         }
-        po[n * ho_stride + d] = o / lsum;
-        if (d == 0) pl[(int64_t)n * a.max_splits] = (M + log2f(lsum)) * 0.69314718055994531f;
+        // quantised V: O = (acc - offset sum) * 2^24
+        const float inv = (C::V_SCALE ? TWO24 : 1.0f) / lsum;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) fw[w * 16 + n] = f[w] * inv;
+        if constexpr (C::V_SCALE) {
+#pragma unroll
+            for (int kb = 0; kb < C::NB; ++kb) {
+                float c = 0.0f;
+#pragma unroll
+                for (int w = 0; w < WAVES; ++w) c += f[w] * inv * bw[(w * 16 + n) * C::NB + kb];
+                corr[n * C::NB + kb] = c;
+            }
+        }
+        pl[(int64_t)n * a.max_splits] = (M + log2f(lsum)) * 0.69314718055994531f;
     }
-
+    __syncthreads();
+    for (int idx = tid; idx < G * (D / 4); idx += NT) {
+        const int n = idx / (D / 4), c4 = idx % (D / 4);
+        float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+            const float f = fw[w * 16 + n];
+            const float4 v = reinterpret_cast<const float4*>(ow + (w * G + n) * D)[c4];
+            o.x = fmaf(f, v.x, o.x);
+            o.y = fmaf(f, v.y, o.y);
+            o.z = fmaf(f, v.z, o.z);
+            o.w = fmaf(f, v.w, o.w);
+        }
+        if constexpr (C::V_SCALE) {
+            const float c = corr[n * C::NB + c4 / 8];
+            o.x -= c;
+            o.y -= c;
+            o.z -= c;
+            o.w -= c;
+        }
+        reinterpret_cast<float4*>(po + n * ho_stride)[c4] = o;
+    }
 }
 
 template <int TK, int TV, int D>
@@ -636,7 +734,7 @@ template <int TK, int TV, int D>
 size_t dyn_lds_bytes(int G)
 {
     using C = Cfg<TK, TV, D>;
-    const size_t merge = sizeof(float) * ((size_t)WAVES * 32 + (size_t)WAVES * G * D);
+    const size_t merge = merge_lds_bytes<TK, TV, D>(G);
     return merge <= (size_t)WAVES * C::BUF ? 0 : merge;
 }
 

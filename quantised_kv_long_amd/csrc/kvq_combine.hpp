@@ -7,9 +7,9 @@
 //   LSE = ln sum_s exp(lse_s),   out = sum_s exp(lse_s - LSE) * o_s .
 // Each thread owns four adjacent columns (one 16-byte load per split row) and
 // a residue class r of the splits (s = r, r + R, ...).  It issues the loads of
-// up to CMB_UNROLL of its splits at once (lse values and rows together) and
+// up to U (8 or 16) of its splits at once (lse values and rows together) and
 // folds them into a running (max m, sum l, weighted row a) -- the same online
-// softmax as within a split -- so a merge of up to R * CMB_UNROLL splits costs
+// softmax as within a split -- so a merge of up to R * U splits costs
 // one memory round trip.  The R running triples of a column are then merged
 // through LDS:  M = max m_r,  l = sum exp(m_r - M) l_r,  a = sum exp(m_r - M) a_r,
 // out = a / l,  LSE = M + ln l.
@@ -22,7 +22,7 @@
 namespace kvq {
 
 constexpr int CMB_NT = 256;        // threads of the calling workgroup
-constexpr int CMB_UNROLL = 16;     // splits in flight per thread
+constexpr float CMB_LOG2E = 1.4426950408889634f;
 
 struct CombineLds {
     float m[CMB_NT];
@@ -33,7 +33,10 @@ struct CombineLds {
 // pl: the S partial lse values; po: the S partial rows of D floats (16-byte
 // aligned); writes D outputs at out (fp16 or fp32) and, if lse_dst is not
 // NULL, the merged lse.  Splits with lse = -inf carry no weight; S == 0 (or all
-// splits empty) gives out = 0, lse = -inf.
+// splits empty) gives out = 0, lse = -inf.  U splits are loaded per batch.
+// Weights are exp2((lse - m) * log2 e) on the hardware exp2: the relative
+// error of a weight is a few fp32 ulps times |lse - m|.
+template <int U>
 __device__ __forceinline__ void combine_rows(const float* pl, const float* po, int S, int D,
                                              bool out_f16, void* out, float* lse_dst, CombineLds& sm)
 {
@@ -45,11 +48,11 @@ __device__ __forceinline__ void combine_rows(const float* pl, const float* po, i
 
     float m = -INFINITY, l = 0.0f;
     float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int s0 = r; s0 < S; s0 += R * CMB_UNROLL) {
-        float ls[CMB_UNROLL];
-        float4 v[CMB_UNROLL];
+    for (int s0 = r; s0 < S; s0 += R * U) {
+        float ls[U];
+        float4 v[U];
 #pragma unroll
-        for (int u = 0; u < CMB_UNROLL; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int sp = s0 + u * R;
             if (sp < S) {
                 ls[u] = pl[sp];
@@ -61,9 +64,9 @@ __device__ __forceinline__ void combine_rows(const float* pl, const float* po, i
         }
         float bm = ls[0];
 #pragma unroll
-        for (int u = 1; u < CMB_UNROLL; ++u) bm = fmaxf(bm, ls[u]);
+        for (int u = 1; u < U; ++u) bm = fmaxf(bm, ls[u]);
         if (bm > m) {                      // move the reference (m = -inf: nothing to scale)
-            const float f = m == -INFINITY ? 0.0f : expf(m - bm);
+            const float f = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m - bm) * CMB_LOG2E);
             l *= f;
             a.x *= f;
             a.y *= f;
@@ -72,8 +75,8 @@ __device__ __forceinline__ void combine_rows(const float* pl, const float* po, i
             m = bm;
         }
 #pragma unroll
-        for (int u = 0; u < CMB_UNROLL; ++u) {
-            const float w = ls[u] == -INFINITY ? 0.0f : expf(ls[u] - m);
+        for (int u = 0; u < U; ++u) {
+            const float w = ls[u] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((ls[u] - m) * CMB_LOG2E);
             l += w;
             a.x += w * v[u].x;
             a.y += w * v[u].y;
@@ -95,7 +98,7 @@ __device__ __forceinline__ void combine_rows(const float* pl, const float* po, i
         if (M != -INFINITY) {
             for (int k = 0; k < R; ++k) {
                 const float mk = sm.m[k * D4 + tid];
-                const float f = mk == -INFINITY ? 0.0f : expf(mk - M);
+                const float f = mk == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((mk - M) * CMB_LOG2E);
                 const float4 ak = sm.a[k * D4 + tid];
                 L += f * sm.l[k * D4 + tid];
                 A.x += f * ak.x;
