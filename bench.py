@@ -79,6 +79,9 @@ def parse():
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline (0 disables it)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only copy MIB MiB device to device once (a plain copy kernel of known "
+                        "size, for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     p.add_argument("--replicas", type=int, default=0,
                    help="cache copies rotated per step so the working set exceeds the 256 MB "
                         "last-level cache (0 = automatic)")
@@ -190,7 +193,9 @@ MODES = ("step", "three", "decode")
 
 def time_arm(arm, steps, warmup, use_graph, variant):
     """ms per step for every mode, timed with HIP events on the stream the
-    launches go to (graphs are replayed on torch's current stream)."""
+    launches go to.  With graphs, the K timed steps of a mode are captured as
+    one graph (step i uses cache replica i mod R) and replayed once, so launch
+    gaps between graph replays do not enter the per-launch times."""
     import torch
 
     arm.prepare_calls(variant)
@@ -202,32 +207,28 @@ def time_arm(arm, steps, warmup, use_graph, variant):
             arm.step(sh, i % R, mode)
     torch.cuda.synchronize()
 
-    graphs = {m: [] for m in MODES}
+    graphs = {}
     if use_graph:
         for m in MODES:
-            for r in range(R):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    arm.step(torch.cuda.current_stream().cuda_stream, r, m)
-                graphs[m].append(g)
-            for g in graphs[m]:
-                g.replay()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cs = torch.cuda.current_stream().cuda_stream
+                for i in range(steps):
+                    arm.step(cs, i % R, m)
+            graphs[m] = g
+            g.replay()                     # untimed: first replay of the new graph
         torch.cuda.synchronize()
-
-    def run(k, mode):
-        for i in range(k):
-            r = i % R
-            if use_graph:
-                graphs[mode][r].replay()
-            else:
-                arm.step(sh, r, mode)
 
     ms = {}
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for mode in MODES:
         torch.cuda.synchronize()
         e0.record(stream)
-        run(steps, mode)
+        if use_graph:
+            graphs[mode].replay()
+        else:
+            for i in range(steps):
+                arm.step(sh, i % R, mode)
         e1.record(stream)
         torch.cuda.synchronize()
         ms[mode] = e0.elapsed_time(e1) / steps
@@ -285,6 +286,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
 
     import quantised_kv_long_amd as kvq
     from quantised_kv_long_amd import synth
