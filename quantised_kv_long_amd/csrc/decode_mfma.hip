@@ -250,7 +250,8 @@ decode_mfma_kernel(DecodeArgs a)
     //      4*lq + {0, 2, 16, 18, 1, 3, 17, 19}, the nibble order of one dword)
     half8 qop[C::NB];
     floatx4 kbias[C::NB];
-    {
+    // (run after the first tiles' loads are issued, so they overlap)
+    auto init_q = [&]() {
         const uint16_t* qh = a.q + ((int64_t)b * a.Hq + h0 + min(ln, G - 1)) * D;
         const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
@@ -279,7 +280,8 @@ decode_mfma_kernel(DecodeArgs a)
             const float bias = -C::KOFF * TWOM24 * xsum4(part);
             kbias[kb] = floatx4{bias, bias, bias, bias};
         }
-    }
+    };
+
     // scores: fp32 MFMA sums times block scale, then softmax scale * log2(e)
     // (and 2^24 for the subnormal codes)
     const float cK = a.scale_log2 * (C::K_SCALE ? TWO24 : 1.0f);
@@ -617,6 +619,9 @@ decode_mfma_kernel(DecodeArgs a)
                 issue_k(it + x * W, krs[x]);
                 issue_vs(it + x * W, vrs[x], srs[x]);
             }
+    }
+    init_q();
+    if (it < ntiles) {
         stage(vrs[0], srs[0]);
         if (it + NS * W < ntiles) issue_vs(it + NS * W, vrs[0], srs[0]);
     }
