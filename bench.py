@@ -232,7 +232,75 @@ def time_arm(arm, steps, warmup, use_graph, variant):
         e1.record(stream)
         torch.cuda.synchronize()
         ms[mode] = e0.elapsed_time(e1) / steps
-    return ms
+
+    # distribution of single steps (mode "step"): one graph per replica, each
+    # step replayed and timed on its own (graph launch overhead included)
+    samples = []
+    if use_graph:
+        one = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                arm.step(torch.cuda.current_stream().cuda_stream, r, "step")
+            one.append(g)
+            g.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            one[i % R].replay()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        samples = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    return ms, samples
+
+
+def percentile(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    k = (len(xs) - 1) * q
+    lo, hi = int(k), min(int(k) + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
+
+
+def probe_read_bandwidth(nbytes=4 << 30, reps=4):
+    """Achievable streaming-read rate of this GPU's HBM: the plain read kernel
+    of libkvq_probe.so over a buffer far larger than the last-level cache, best
+    over a few grid sizes.  None when the probe library is not built (it is not
+    part of the decode path)."""
+    import ctypes
+
+    import torch
+
+    from quantised_kv_long_amd import build as B
+
+    if not os.path.exists(B.PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.kvq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p]
+    lib.kvq_probe_stream_read.restype = ctypes.c_int
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    grids = (4096, 8192, 16384)
+    sink = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    best = 0.0
+    for blocks in grids:
+        for i in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = lib.kvq_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks,
+                                           stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            assert rc == 0, rc
+            if i:
+                best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return best
 
 
 def cpu_baseline(arm, budget_s):
@@ -320,7 +388,7 @@ def main():
         log(f"arm {tk}/{tv}: building {wl.layers} layer(s) x {reps} replica(s)")
         arm = Arm(wl, tk, tv, split_tokens, reps, dev)
         log(f"arm {tk}/{tv}: timing {args.steps} steps")
-        ms = time_arm(arm, args.steps, args.warmup, not args.no_graph, args.variant)
+        ms, samples = time_arm(arm, args.steps, args.warmup, not args.no_graph, args.variant)
         per_launch = {m: ms[m] / wl.layers for m in MODES}
         results[f"{tk}/{tv}"] = {
             "us_per_step": round(ms["step"] * 1e3, 2),
@@ -333,6 +401,9 @@ def main():
             "decode_only_GBps": round(arm.stored_bytes_layer / (per_launch["decode"] * 1e-3) / 1e9, 1),
             "replicas": reps,
         }
+        if samples:
+            results[f"{tk}/{tv}"]["single_step_us_p10_p50_p90"] = [
+                round(percentile(samples, q), 2) for q in (0.1, 0.5, 0.9)]
         log(f"arm {tk}/{tv}: {results[f'{tk}/{tv}']}")
         if (tk, tv) == headline:
             head_arm = arm
@@ -349,6 +420,11 @@ def main():
     if "q4_0/q4_0" in results and "q8_0/q4_0" in results:
         ratios["q4q4_over_q8q4_speedup"] = round(results["q8_0/q4_0"]["us_per_step"] /
                                                  results["q4_0/q4_0"]["us_per_step"], 3)
+        a, b = results["q8_0/q4_0"], results["q4_0/q4_0"]
+        if "single_step_us_p10_p50_p90" in a and "single_step_us_p10_p50_p90" in b:
+            pa, pb = a["single_step_us_p10_p50_p90"], b["single_step_us_p10_p50_p90"]
+            ratios["q4q4_over_q8q4_median_single_step"] = round(pa[1] / pb[1], 3)
+            ratios["q4q4_p90_below_q8q4_p10"] = pb[2] < pa[0]
     if "f16/f16" in results and "q8_0/q4_0" in results:
         ratios["q8q4_over_f16_speedup"] = round(results["f16/f16"]["us_per_step"] /
                                                 results["q8_0/q4_0"]["us_per_step"], 3)
@@ -359,10 +435,15 @@ def main():
     if rec is not None:
         traffic = round((rec[0] + rec[1]) / (dec_us * 1e-6) / 1e9, 1)
         log(f"traffic from {rec[2]}: {rec[0] + rec[1]} bytes per launch")
+    probe = probe_read_bandwidth()
+    probe = round(probe, 1) if probe else None
+    log(f"probe read bandwidth {probe} GB/s")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "decode_mfma_kernel", "avg_launch_us": dec_us,
-                "algorithmic_bytes_per_launch": head_arm.stored_bytes_layer}
+                "algorithmic_bytes_per_launch": head_arm.stored_bytes_layer,
+                "probe_read_GBps": probe,
+                "frac_of_probe": round(achieved / probe, 4) if probe else None}
     line = {
         "metric": METRIC,
         "value": h["GBps"],

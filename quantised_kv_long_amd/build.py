@@ -46,8 +46,12 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
-    cmd = [HIPCC, *HIP_FLAGS, *(extra or []), f"-I{INCLUDE}", f"-I{CSRC}", *sources(), "-o", out + ".tmp"]
+PROBE_SRC = os.path.join(PKG, "probe", "stream_read.hip")
+PROBE_LIB = os.path.join(PKG, "libkvq_probe.so")
+
+
+def _hipcc(srcs: list[str], out: str, extra: list[str] | None, verbose: bool) -> str:
+    cmd = [HIPCC, *HIP_FLAGS, *(extra or []), f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,5 +64,17 @@ def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False)
     return out
 
 
+def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
+    """The decode-path library: every csrc/*.hip and *.cpp."""
+    return _hipcc(sources(), out, extra, verbose)
+
+
+def build_probe(out: str = PROBE_LIB, verbose: bool = False) -> str:
+    """The streaming-read probe the benchmark measures the achievable HBM
+    read bandwidth with (not part of the decode path)."""
+    return _hipcc([PROBE_SRC], out, None, verbose)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe(verbose=True))

@@ -167,7 +167,7 @@ struct Cfg {
     static constexpr int NSET = D == 128 ? 2 : 1;
     static constexpr float KOFF = TK == T_Q4 ? 8.0f : (TK == T_Q8 ? 128.0f : 0.0f);
     static constexpr uint32_t VOFF_BITS = TV == T_Q4 ? 0x00080008u : 0x00800080u;
-    static constexpr bool VALID = V_BYTES % 1024 == 0 && S_BYTES % 256 == 0 && V_DW <= 32 &&
+    static constexpr bool VALID = V_BYTES % 1024 == 0 && S_BYTES % 256 == 0 && V_DW <= (D == 128 ? 32 : 64) &&
                                   WAVES * BUF <= 64 * 1024;
 };
 

@@ -254,9 +254,9 @@ def test_workload_hybrid_d256_ctx32k(variant, tk, tv):
 @pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("tk,tv", [("f16", "f16"), ("q8_0", "q4_0"), ("q4_0", "q4_0")])
 def test_workload_stack48_layers_sampled(variant, tk, tv):
-    """Layers 0 and 47 of the 48-layer stack (each layer is an independent
+    """Layers 0, 23 and 47 of the 48-layer stack (each layer is an independent
     65536-row cache; every output of those layers is checked)."""
-    for layer in (0, 47):
+    for layer in (0, 23, 47):
         workload_case("stack48_d128_ctx64k", tk, tv, variant, layer=layer)
 
 
