@@ -144,30 +144,41 @@ __device__ __forceinline__ float xsum4(float v)
 
 template <int TK, int TV, int D>
 struct Cfg {
-    static constexpr int NB = D / 32;               // blocks per row
-    static constexpr int NBG = D / 128;             // groups of 4 blocks
-    static constexpr int RBK = rb(TK, D);
-    static constexpr int RBV = rb(TV, D);
+    // head_dim 512: the four waves of a workgroup walk the same tiles, each
+    // owning one 128-column slice of the head dimension (partial scores are
+    // summed through LDS); otherwise each wave walks its own tiles over the
+    // full head dimension
+    static constexpr int DS = D == 512 ? 4 : 1;    // waves sharing a tile
+    static constexpr int DW = D / DS;              // head-dim slice of a wave
+    static constexpr int NB = DW / 32;             // blocks per slice
+    static constexpr int NBG = DW / 128;           // groups of 4 blocks
+    static constexpr int NB_ROW = D / 32;          // blocks per row
+    static constexpr int RBK = rb(TK, DW);         // bytes of a row's slice
+    static constexpr int RBV = rb(TV, DW);
+    static constexpr int RBK_ROW = rb(TK, D);      // bytes of a row (row stride)
+    static constexpr int RBV_ROW = rb(TV, D);
     static constexpr int KU = TK == T_Q4 ? 1 : (TK == T_Q8 ? 2 : 4);   // dwords per lane per block
     static constexpr int KDW = 4 * KU * NBG;                           // K dwords per lane per subtile
-    static constexpr int V_BYTES = TT * RBV;                           // V tile bytes
+    static constexpr int V_BYTES = TT * RBV;                           // V tile bytes (slice)
     static constexpr int V_LOADS = V_BYTES / 1024;                     // 16-byte loads per lane
     static constexpr int V_DW = 4 * V_LOADS;
     static constexpr int K_SCALE = TK != T_F16;
     static constexpr int V_SCALE = TV != T_F16;
-    static constexpr int S_BYTES = TT * 2 * NB;                        // one scale tile
+    static constexpr int S_BYTES = TT * 2 * NB;                        // one scale tile (slice)
     static constexpr int S_LOADS = S_BYTES / 256;                      // 4-byte loads per lane
     static constexpr int S_DW = (K_SCALE + V_SCALE) * S_LOADS > 0 ? (K_SCALE + V_SCALE) * S_LOADS : 1;
     static constexpr int KS_OFF = V_BYTES;
     static constexpr int VS_OFF = V_BYTES + S_BYTES * K_SCALE;
     static constexpr int BUF = V_BYTES + S_BYTES * (K_SCALE + V_SCALE);
-    static constexpr int NDT = D / 16;                                 // PV output tiles
-    // register sets of the load ring: two for head_dim 128 (a third, where
-    // it fits in 256 registers, measured slower), one for head_dim 256
-    static constexpr int NSET = D == 128 ? 2 : 1;
+    static constexpr int NDT = DW / 16;                                // PV output tiles
+    // register sets of the load ring: two for 128-column slices (a third,
+    // where it fits in 256 registers, measured slower), one for 256 and for
+    // f16 rows of a 512-wide head (their registers do not fit twice)
+    static constexpr int NSET = DW == 128 && (DS == 1 || (TK != T_F16 && TV != T_F16)) ? 2 : 1;
+    static constexpr int SX_FLOATS = DS > 1 ? 2 * WAVES * 64 * 8 : 1;  // partial-score exchange
     static constexpr float KOFF = TK == T_Q4 ? 8.0f : (TK == T_Q8 ? 128.0f : 0.0f);
     static constexpr uint32_t VOFF_BITS = TV == T_Q4 ? 0x00080008u : 0x00800080u;
-    static constexpr bool VALID = V_BYTES % 1024 == 0 && S_BYTES % 256 == 0 && V_DW <= (D == 128 ? 32 : 64) &&
+    static constexpr bool VALID = V_BYTES % 1024 == 0 && S_BYTES % 256 == 0 && V_DW <= (DW == 128 ? 32 : 64) &&
                                   WAVES * BUF <= 64 * 1024;
 };
 
@@ -177,20 +188,22 @@ struct Cfg {
 template <int TK, int TV, int D>
 __host__ __device__ constexpr size_t merge_lds_bytes(int G)
 {
-    return sizeof(float) * ((size_t)WAVES * 16 * 3 + (size_t)WAVES * 16 * (D / 32) + 16 * (D / 32) +
-                            (size_t)WAVES * G * D);
+    return Cfg<TK, TV, D>::DS > 1 ? 0
+                                  : sizeof(float) * ((size_t)WAVES * 16 * 3 + (size_t)WAVES * 16 * (D / 32) +
+                                                     16 * (D / 32) + (size_t)WAVES * G * D);
 }
 
-// head_dim 128 is built for two waves per SIMD (at most 256 registers);
-// head_dim 256 needs more and runs one
+// 128-column slices are built for two waves per SIMD (at most 256
+// registers); head_dim 256 needs more and runs one
 template <int TK, int TV, int D>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1)))
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 decode_mfma_kernel(DecodeArgs a)
 {
     using C = Cfg<TK, TV, D>;
     // One LDS buffer per wave: the V rows of the current tile, then the K and
     // V scale tiles, transposed to [block][row].
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[WAVES * C::BUF];
+    __shared__ __attribute__((aligned(16))) float lds_sx[C::SX_FLOATS];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
 
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -213,28 +226,29 @@ decode_mfma_kernel(DecodeArgs a)
 
     const int64_t krow0 = (int64_t)b * a.k.seq_stride + (int64_t)g * a.k.head_stride;
     const int64_t vrow0 = (int64_t)b * a.v.seq_stride + (int64_t)g * a.v.head_stride;
-    const uint8_t* kdata = a.k.data + krow0 * C::RBK;
-    const uint8_t* kscl = reinterpret_cast<const uint8_t*>(a.k.scales + krow0 * C::NB);
-    const uint8_t* vdata = a.v.data + vrow0 * C::RBV;
-    const uint8_t* vscl = reinterpret_cast<const uint8_t*>(a.v.scales + vrow0 * C::NB);
+    const int wsl = C::DS > 1 ? wave : 0;          // this wave's head-dim slice
+    const uint8_t* kdata = a.k.data + krow0 * C::RBK_ROW + wsl * C::RBK;
+    const uint8_t* kscl = reinterpret_cast<const uint8_t*>(a.k.scales + krow0 * C::NB_ROW + wsl * C::NB);
+    const uint8_t* vdata = a.v.data + vrow0 * C::RBV_ROW + wsl * C::RBV;
+    const uint8_t* vscl = reinterpret_cast<const uint8_t*>(a.v.scales + vrow0 * C::NB_ROW + wsl * C::NB);
 
     // ---- decode step with the new token: the workgroup whose split holds
     //      row L-1 first quantises the new K and V rows of its KV head into
     //      that row (the same block quantiser as kvq_quantize_append), then
     //      makes them visible to its own loads
     if (a.k_new != nullptr && t_end == L) {
-        // 2*NB blocks (K then V), one aligned half-wave of 32 lanes per block
-        for (int blk2 = tid >> 5; blk2 < 2 * C::NB; blk2 += NT / 32) {
-            const bool isv = blk2 >= C::NB;
-            const int blk = isv ? blk2 - C::NB : blk2;
+        // 2*NB_ROW blocks (K then V), one aligned half-wave of 32 lanes per block
+        for (int blk2 = tid >> 5; blk2 < 2 * C::NB_ROW; blk2 += NT / 32) {
+            const bool isv = blk2 >= C::NB_ROW;
+            const int blk = isv ? blk2 - C::NB_ROW : blk2;
             const uint16_t* src = (isv ? a.v_new : a.k_new) + ((int64_t)b * a.Hkv + g) * D + 32 * blk;
             const int64_t row = (isv ? vrow0 : krow0) + (L - 1);
             if (isv) {
-                quantize_block_lanes<TV>(src, a.v.data + row * C::RBV + blk * rb(TV, 32),
-                                         a.v.scales + row * C::NB + blk, tid & 31);
+                quantize_block_lanes<TV>(src, a.v.data + row * C::RBV_ROW + blk * rb(TV, 32),
+                                         a.v.scales + row * C::NB_ROW + blk, tid & 31);
             } else {
-                quantize_block_lanes<TK>(src, a.k.data + row * C::RBK + blk * rb(TK, 32),
-                                         a.k.scales + row * C::NB + blk, tid & 31);
+                quantize_block_lanes<TK>(src, a.k.data + row * C::RBK_ROW + blk * rb(TK, 32),
+                                         a.k.scales + row * C::NB_ROW + blk, tid & 31);
             }
         }
         // the row is read back only by this workgroup, whose loads of that
@@ -252,7 +266,7 @@ decode_mfma_kernel(DecodeArgs a)
     floatx4 kbias[C::NB];
     // (run after the first tiles' loads are issued, so they overlap)
     auto init_q = [&]() {
-        const uint16_t* qh = a.q + ((int64_t)b * a.Hq + h0 + min(ln, G - 1)) * D;
+        const uint16_t* qh = a.q + ((int64_t)b * a.Hq + h0 + min(ln, G - 1)) * D + wsl * C::DW;
         const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
         for (int kb = 0; kb < C::NB; ++kb) {
@@ -309,8 +323,22 @@ decode_mfma_kernel(DecodeArgs a)
     constexpr bool KDIRECT = C::KU == 4;
     const int krow_rel0 = 8 * (ln >> 2) + (ln & 3);
     const uint32_t kpart = (uint32_t)(lq * (KDIRECT ? QB : BB));
-    const uint32_t klane0 = (uint32_t)(krow_rel0 * C::RBK) + kpart;
-    const uint32_t klane1 = (uint32_t)((krow_rel0 + 4) * C::RBK) + kpart;
+    const uint32_t klane0 = (uint32_t)(krow_rel0 * C::RBK_ROW) + kpart;
+    const uint32_t klane1 = (uint32_t)((krow_rel0 + 4) * C::RBK_ROW) + kpart;
+    // V row chunks and scale words of a tile: 16-byte chunk k*64 + lane of the
+    // slice is row c16 / (RBV/16), column c16 % (RBV/16); scale word k*64 +
+    // lane is row c4 / (NB/2), word c4 % (NB/2)
+    // (whole rows, DS == 1: one contiguous tile, offsets 16*c16 and 4*c4)
+    auto voff = [&](int k) -> uint32_t {
+        const int c16 = k * 64 + lane;
+        if constexpr (C::DS == 1) return (uint32_t)(16 * lane + 1024 * k);
+        else return (uint32_t)((c16 / (C::RBV / 16)) * C::RBV_ROW + 16 * (c16 % (C::RBV / 16)));
+    };
+    auto soff = [&](int k) -> uint32_t {
+        const int c4 = k * 64 + lane;
+        if constexpr (C::DS == 1) return (uint32_t)(4 * lane + 256 * k);
+        else return (uint32_t)((c4 / (C::NB / 2)) * (2 * C::NB_ROW) + 4 * (c4 % (C::NB / 2)));
+    };
 
     // one K row's share of this lane (p: the row start plus kpart)
     auto load_k_row = [&](const uint8_t* p, uint32_t (&x)[C::KDW]) {
@@ -342,34 +370,34 @@ decode_mfma_kernel(DecodeArgs a)
     auto issue_k = [&](int it, uint32_t (&kr)[2][C::KDW]) {
         const int t0 = t_begin + it * TT;
         if (t0 + TT <= L) {
-            const uint8_t* base = kdata + (uint32_t)(t0 * C::RBK);
+            const uint8_t* base = kdata + (uint32_t)(t0 * C::RBK_ROW);
             load_k_row(base + klane0, kr[0]);
             load_k_row(base + klane1, kr[1]);
         } else {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int tok = min(t0 + krow_rel0 + 4 * j, L - 1);
-                load_k_row(kdata + (uint32_t)(tok * C::RBK) + kpart, kr[j]);
+                load_k_row(kdata + (uint32_t)(tok * C::RBK_ROW) + kpart, kr[j]);
             }
         }
     };
     auto issue_vs = [&](int it, uint32_t (&vr)[C::V_DW], uint32_t (&sr)[C::S_DW]) {
         const int t0 = t_begin + it * TT;
         if (t0 + TT <= L) {
-            const uint8_t* vbase = vdata + (uint32_t)(t0 * C::RBV) + 16 * lane;
+            const uint8_t* vbase = vdata + (uint32_t)(t0 * C::RBV_ROW);
 #pragma unroll
             for (int k = 0; k < C::V_LOADS; ++k) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(vbase + 1024 * k);
+                const u32x4 v = *reinterpret_cast<const u32x4*>(vbase + voff(k));
 #pragma unroll
                 for (int c = 0; c < 4; ++c) vr[4 * k + c] = v[c];
             }
-            const uint32_t soff = (uint32_t)(t0 * (2 * C::NB)) + 4 * lane;
+            const uint32_t sbase = (uint32_t)(t0 * (2 * C::NB_ROW));
 #pragma unroll
             for (int k = 0; k < C::S_LOADS; ++k) {
-                if constexpr (C::K_SCALE) sr[k] = *reinterpret_cast<const uint32_t*>(kscl + soff + 256 * k);
+                if constexpr (C::K_SCALE) sr[k] = *reinterpret_cast<const uint32_t*>(kscl + sbase + soff(k));
                 if constexpr (C::V_SCALE)
                     sr[C::K_SCALE * C::S_LOADS + k] =
-                        *reinterpret_cast<const uint32_t*>(vscl + soff + 256 * k);
+                        *reinterpret_cast<const uint32_t*>(vscl + sbase + soff(k));
             }
         } else {
 #pragma unroll
@@ -377,7 +405,7 @@ decode_mfma_kernel(DecodeArgs a)
                 const int c16 = k * 64 + lane;
                 const int tok = min(t0 + c16 / (C::RBV / 16), L - 1);
                 const u32x4 v = *reinterpret_cast<const u32x4*>(
-                    vdata + (uint32_t)(tok * C::RBV) + 16 * (c16 % (C::RBV / 16)));
+                    vdata + (uint32_t)(tok * C::RBV_ROW) + 16 * (c16 % (C::RBV / 16)));
 #pragma unroll
                 for (int c = 0; c < 4; ++c) vr[4 * k + c] = v[c];
             }
@@ -385,7 +413,7 @@ decode_mfma_kernel(DecodeArgs a)
             for (int k = 0; k < C::S_LOADS; ++k) {
                 const int c4 = k * 64 + lane;
                 const int tok = min(t0 + c4 / (C::NB / 2), L - 1);
-                const uint32_t off = (uint32_t)(tok * (2 * C::NB)) + 4 * (c4 % (C::NB / 2));
+                const uint32_t off = (uint32_t)(tok * (2 * C::NB_ROW)) + 4 * (c4 % (C::NB / 2));
                 if constexpr (C::K_SCALE) sr[k] = *reinterpret_cast<const uint32_t*>(kscl + off);
                 if constexpr (C::V_SCALE)
                     sr[C::K_SCALE * C::S_LOADS + k] = *reinterpret_cast<const uint32_t*>(vscl + off);
@@ -485,6 +513,25 @@ decode_mfma_kernel(DecodeArgs a)
         }
         // the K registers are free: start loading the next tile's K rows
         if (next_it < ntiles) issue_k(next_it, kr);
+
+        if constexpr (C::DS > 1) {
+            // each wave holds the scores over its head-dim slice: sum the
+            // four in a fixed order, so every wave gets the same bits (one
+            // barrier per tile; the two halves of lds_sx alternate by tile)
+            float* mine = lds_sx + ((it & 1) * WAVES + wave) * 512 + lane * 8;
+            *reinterpret_cast<floatx4*>(mine) = sacc[0];
+            *reinterpret_cast<floatx4*>(mine + 4) = sacc[1];
+            __syncthreads();
+            floatx4 f0 = {0.0f, 0.0f, 0.0f, 0.0f}, f1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) {
+                const float* theirs = lds_sx + ((it & 1) * WAVES + w) * 512 + lane * 8;
+                f0 += *reinterpret_cast<const floatx4*>(theirs);
+                f1 += *reinterpret_cast<const floatx4*>(theirs + 4);
+            }
+            sacc[0] = f0;
+            sacc[1] = f1;
+        }
 
         // -- online softmax (log2 domain)
         float sv[8];
@@ -606,9 +653,10 @@ decode_mfma_kernel(DecodeArgs a)
     //      tile it+W go to LDS (a wave's LDS reads and writes are performed in
     //      order, so one buffer suffices) and V of tile it+(NS+1)*W is issued
     //      into the registers that frees.
-    constexpr int W = WAVES;
+    // (a 512-wide head: all waves walk every tile, each over its slice)
+    constexpr int W = C::DS > 1 ? 1 : WAVES;
     constexpr int NS = C::NSET;
-    int it = wave;
+    int it = C::DS > 1 ? 0 : wave;
     uint32_t krs[NS][2][C::KDW];
     uint32_t vrs[NS][C::V_DW];
     uint32_t srs[NS][C::S_DW];
@@ -643,6 +691,30 @@ decode_mfma_kernel(DecodeArgs a)
                 }
             }
         }
+    }
+
+    if constexpr (C::DS > 1) {
+        // every wave holds the same (m, l) and its own slice of O: write it
+        const float l_head = xsum4(l_part);
+        if (ln < G) {
+            const float inv = (C::V_SCALE ? TWO24 : 1.0f) / l_head;
+            float* prow = po + ln * ho_stride + wsl * C::DW;
+#pragma unroll
+            for (int t = 0; t < C::NDT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = 4 * lq + i;
+                    int d;
+                    if constexpr (TV == T_Q4) d = 32 * (t >> 1) + 8 * (t & 1) + (m >> 1) + 16 * (m & 1);
+                    else d = 16 * t + m;
+                    float o = oacc[t][i];
+                    if constexpr (C::V_SCALE) o -= bacc[t >> 1][i];
+                    prow[d] = o * inv;
+                }
+            if (wave == 0 && lq == 0)
+                pl[(int64_t)ln * a.max_splits] = (m_ref + log2f(l_head)) * 0.69314718055994531f;
+        }
+        return;
     }
 
     // ---- merge the four waves: (m, l, O) per head through LDS.  Each lane
@@ -747,7 +819,7 @@ template <int TK, int TV, int D>
 size_t lds_bytes(int G)
 {
     using C = Cfg<TK, TV, D>;
-    return (size_t)WAVES * C::BUF + dyn_lds_bytes<TK, TV, D>(G);
+    return (size_t)WAVES * C::BUF + sizeof(float) * C::SX_FLOATS + dyn_lds_bytes<TK, TV, D>(G);
 }
 
 template <int TK, int TV, int D>
@@ -775,6 +847,7 @@ hipError_t launch2(const DecodeArgs& a, hipStream_t s)
     switch (a.D) {
     case 128: return launch3<TK, TV, 128>(a, s);
     case 256: return launch3<TK, TV, 256>(a, s);
+    case 512: return launch3<TK, TV, 512>(a, s);
     default: return hipErrorInvalidConfiguration;
     }
 }
@@ -794,6 +867,7 @@ bool supports2(const DecodeArgs& a)
 {
     if (a.D == 128) return cfg_valid<TK, TV, 128>() && lds_bytes<TK, TV, 128>(a.G) <= 160 * 1024;
     if (a.D == 256) return cfg_valid<TK, TV, 256>() && lds_bytes<TK, TV, 256>(a.G) <= 160 * 1024;
+    if (a.D == 512) return cfg_valid<TK, TV, 512>() && lds_bytes<TK, TV, 512>(a.G) <= 160 * 1024;
     return false;
 }
 
@@ -811,9 +885,7 @@ bool supports1(const DecodeArgs& a)
 
 bool decode_mfma_supports(const DecodeArgs& a)
 {
-    // head_dim 512 needs more registers than the kernel can hold without
-    // spilling; it stays on the vector-ALU kernel
-    if (a.D != 128 && a.D != 256) return false;
+    if (a.D != 128 && a.D != 256 && a.D != 512) return false;
     if (a.G < 1 || a.G > 16) return false;
     // rows read are below max_seq_len; their offsets inside one (sequence,
     // KV head) plane are computed in 32 bits
