@@ -98,6 +98,44 @@ size_t kvq_data_row_bytes(int type, int head_dim);
 /* Bytes of one scale-plane row: 0 (f16), D/16 (q8_0, q4_0); 0 when invalid. */
 size_t kvq_scale_row_bytes(int type, int head_dim);
 
+/*
+ * KV tier ladder (HAL #582 section 5 P1, the automatic KV tier at start-up:
+ * pick the least compression whose whole cache stays resident).
+ *
+ * Tiers, from least to most compressing (K type / V type):
+ *   KVQ_TIER_F16     f16 / f16
+ *   KVQ_TIER_Q8_Q8   q8_0 / q8_0
+ *   KVQ_TIER_Q8_Q4   q8_0 / q4_0
+ *   KVQ_TIER_Q51_Q4  q5_1 / q4_0   (the last resort; q5_1 blocks are 24 bytes
+ *                    per 32 values -- a size this library counts but does not
+ *                    store: kvq_tier_types reports KVQ_ERR_TYPE for it)
+ */
+enum { KVQ_TIER_F16 = 0, KVQ_TIER_Q8_Q8 = 1, KVQ_TIER_Q8_Q4 = 2, KVQ_TIER_Q51_Q4 = 3 };
+
+/*
+ * Bytes of a whole cache of the tier: n_layers * Hkv * n_ctx rows of K and of
+ * V (f16: 2*D bytes a row; q8_0: 34*D/32; q4_0: 18*D/32; q5_1: 24*D/32).
+ * -1 for an unknown tier or non-positive sizes, or D % 32 != 0.
+ */
+int64_t kvq_tier_cache_bytes(int tier, int64_t n_ctx, int n_layers, int Hkv, int D);
+
+/*
+ * The tier chosen for a context of n_ctx tokens: the first of the ladder
+ * (least compressing) whose whole cache fits the budget
+ *   budget = min(free_bytes, vram_target_bytes if > 0) - resident_bytes - 1.5 GiB
+ * (the compute reserve), or KVQ_TIER_Q51_Q4 when none fits.  Writes the budget
+ * and the chosen tier's cache bytes if the pointers are not NULL.  Returns the
+ * tier, or KVQ_ERR_SHAPE for non-positive sizes, negative byte counts or
+ * D % 32 != 0.  Host-only; no HIP call.
+ */
+int kvq_select_kv_tier(int64_t n_ctx, int n_layers, int Hkv, int D, int64_t free_bytes,
+                       int64_t resident_bytes, int64_t vram_target_bytes, int64_t* budget_bytes,
+                       int64_t* cache_bytes);
+
+/* K and V storage types of a tier; KVQ_ERR_TYPE for KVQ_TIER_Q51_Q4 and
+ * unknown tiers (types not written). */
+int kvq_tier_types(int tier, int* type_k, int* type_v);
+
 /* Static, human-readable name of a status code. */
 const char* kvq_status_string(int status);
 
@@ -134,6 +172,30 @@ int kvq_quantize_append(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_c
                         int B, int n_new, int Hkv, int D, int max_end, void* stream);
 
 /*
+ * Quantise rows of fp16 cache planes into a cache (HAL #582 section 5 P2, the
+ * position-axis mixed cache: recent tokens stay fp16 in a rolling window and
+ * are quantised once, in batches, when they leave it for the compressed
+ * tail).  For every sequence b < B, row r < counts[b] and KV head g < Hkv,
+ * converts row r of KV head g of sequence b of the fp16 planes k_src / v_src
+ * with the block quantiser of kvq_quantize_append and stores it at row
+ * positions[b] + r of k_cache / v_cache.
+ *
+ *   k_src, v_src : plane descriptors of type KVQ_F16 (host memory, read
+ *                  during the call); rows [0, max_rows) must be addressable.
+ *   counts       : device, [B] int32, 0 <= counts[b] <= max_rows.
+ *   positions    : device, [B] int32, first row written per sequence.
+ *   max_end      : host, max over b of positions[b] + counts[b]; must not
+ *                  exceed either cache's capacity (KVQ_ERR_CAPACITY).
+ *   Sources and destinations must not overlap.  B == 0 or max_rows == 0
+ *   (with valid Hkv and D) enqueues nothing and returns KVQ_OK.
+ *   KVQ_ERR_TYPE if a source plane is not fp16.
+ */
+int kvq_quantize_rows(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache,
+                      const kvq_plane_desc* k_src, const kvq_plane_desc* v_src,
+                      const int32_t* counts, const int32_t* positions, int B, int max_rows,
+                      int Hkv, int D, int max_end, void* stream);
+
+/*
  * Split-KV decode attention (HAL #582 section 3b finding 2 and section 5 P0:
  * a reader that streams the stored blocks and dequantises them in registers;
  * section 5 P2: regions merged exactly by log-sum-exp).
@@ -149,7 +211,8 @@ int kvq_quantize_append(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_c
  * dequantised rows (code * scale, exactly).
  *
  *   q              : device, [B][Hq][D] binary16.
- *   seq_lens       : device, [B] int32, 1 <= L_b <= max_seq_len <= capacity.
+ *   seq_lens       : device, [B] int32, 0 <= L_b <= max_seq_len <= capacity
+ *                    (L_b = 0: every split of b is empty).
  *   max_seq_len    : host, an upper bound of every L_b.
  *   split_tokens   : host, a positive multiple of KVQ_SPLIT_GRANULE.
  *   max_splits     : host, >= ceil(max_seq_len / split_tokens).
@@ -162,6 +225,31 @@ int kvq_decode_attn(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache
                     const void* q, const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
                     float softmax_scale, int max_seq_len, int split_tokens, int max_splits,
                     float* part_o, float* part_lse, void* stream);
+
+/*
+ * Decode attention for n_q query tokens per sequence at once (the
+ * speculative-decoding verify step: n_q draft tokens checked in one pass; the
+ * pages gate their quantised decode route on n_q <= 16).  The last n_q rows of
+ * each sequence are the query tokens' own K/V rows (appended before the
+ * call), and token i (0-based) attends causally over rows
+ * [0, L_b - n_q + 1 + i).  Query token i, head h reads KV head h / (Hq / Hkv);
+ * every (token, head) is one column of the matrix-core tile, so
+ * n_q * (Hq / Hkv) <= 16 and the K/V stream is read once for all of them.
+ *
+ *   q        : device, [B][n_q][Hq][D] binary16.
+ *   seq_lens : device, [B] int32, n_q <= L_b <= max_seq_len <= capacity.
+ *   part_o   : device, [B][n_q * Hq][max_splits][D] fp32 (row i*Hq + h for
+ *              token i, head h); part_lse [B][n_q * Hq][max_splits].  A
+ *              split with no row a token sees is written empty for it.
+ *   The partials merge with kvq_combine called with n_q * Hq heads, giving
+ *   out [B][n_q][Hq][D].  Other arguments as for kvq_decode_attn.
+ *   KVQ_ERR_SHAPE if n_q < 1, n_q * Hq / Hkv > 16, or the matrix-core kernel
+ *   does not cover D (128, 256, 512) and the types.
+ */
+int kvq_decode_attn_multi(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache,
+                          const void* q, const int32_t* seq_lens, int B, int n_q, int Hq, int Hkv,
+                          int D, float softmax_scale, int max_seq_len, int split_tokens,
+                          int max_splits, float* part_o, float* part_lse, void* stream);
 
 /* Kernel family for kvq_decode_attn_variant. */
 enum {
@@ -201,6 +289,28 @@ int kvq_combine(const float* part_o, const float* part_lse, const int32_t* seq_l
                 float* lse_out, void* stream);
 
 /*
+ * Exact log-sum-exp merge of the partials of several regions (HAL #582
+ * section 5 P2 read path: each region of a mixed cache -- the fp16 window and
+ * the compressed tail -- runs its own typed attention launch, and the regions
+ * are merged by an exact online-softmax combine).  Region i was written by
+ * kvq_decode_attn with lengths seq_lens[i], split_tokens[i] and
+ * max_splits[i]; for each (b, h) the merge runs over the S_b,i =
+ * ceil(seq_lens[i][b] / split_tokens[i]) splits of every region, as
+ * kvq_combine does over one region.  The result is the attention over the
+ * union of the regions' rows.
+ *
+ *   n_regions    : 1 .. 4.
+ *   part_o, part_lse, seq_lens, split_tokens, max_splits : host arrays of
+ *                  n_regions entries; the pointers are device pointers laid
+ *                  out as for kvq_combine.
+ *   out_type, out, lse_out : as for kvq_combine.
+ */
+int kvq_combine_regions(int n_regions, const float* const* part_o, const float* const* part_lse,
+                        const int32_t* const* seq_lens, const int* split_tokens,
+                        const int* max_splits, int B, int Hq, int D, int out_type, void* out,
+                        float* lse_out, void* stream);
+
+/*
  * One decode step of one layer in a single call: quantise-on-write of the new
  * token, split-KV attention over every row including the new one, and the
  * exact log-sum-exp merge (HAL #582 section 5 P2: the write path quantises a
@@ -211,8 +321,8 @@ int kvq_combine(const float* part_o, const float* part_lse, const int32_t* seq_l
  * seq_lens[b] - 1) followed by kvq_decode_attn and kvq_combine with the same
  * arguments: the cache rows are bit-identical, the split partials are the
  * same, and out / lse_out agree within floating-point rounding.  Where the
- * matrix-core kernel covers the shape (D = 128 or 256) the step is two kernel
- * launches: the attention kernel's workgroup whose split holds row
+ * matrix-core kernel covers the shape (D = 128, 256 or 512) the step is two
+ * kernel launches: the attention kernel's workgroup whose split holds row
  * seq_lens[b] - 1 writes that row before it reads it, then the merge runs.
  * Other shapes run the three kernels in order.
  *

@@ -198,3 +198,43 @@ def combine(part_o: np.ndarray, part_lse: np.ndarray, lib=None):
     if rc != 0:
         raise ValueError("kvo_combine failed")
     return out, lse
+
+
+def attend_regions(q_f16, regions, Hkv: int, scale: float, lib=None):
+    """fp64 decode attention over the union of the rows of several caches (the
+    regions of a mixed cache, HAL #582 section 5 P2: an fp16 window of recent
+    tokens and a quantised tail).  ``regions``: list of (kc, vc, seq_lens) with
+    kc / vc as for ``attend``; region i contributes its rows [0, seq_lens[b]).
+    Every row is dequantised exactly (``dequantize``) and the scores of all
+    regions' rows share one softmax, by the plain definition:
+        s_t = scale * q . k_t,  p_t = exp(s_t - max s),  o = sum p_t v_t / sum p_t,
+        lse = max s + ln sum p_t  (no rows: o = 0, lse = -inf).
+    Returns (out (B, Hq, D) float64, lse (B, Hq) float64)."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q_f16).view(np.uint16)
+    B, Hq, D = q.shape
+    G = Hq // Hkv
+    qv = q.view(np.float16).astype(np.float64)
+    deq = []
+    for kc, vc, lens in regions:
+        lens = [int(x) for x in lens]
+        n = max(lens) if lens else 0
+        k = dequantize(kc[0], kc[1][:, :, :n], kc[2][:, :, :n], D, lib)
+        v = dequantize(vc[0], vc[1][:, :, :n], vc[2][:, :, :n], D, lib)
+        deq.append((k, v, lens))
+    out = np.zeros((B, Hq, D), np.float64)
+    lse = np.full((B, Hq), -np.inf, np.float64)
+    for b in range(B):
+        for g in range(Hkv):
+            K = np.concatenate([k[b, g, :lens[b]] for k, _, lens in deq], axis=0)
+            V = np.concatenate([v[b, g, :lens[b]] for _, v, lens in deq], axis=0)
+            if K.shape[0] == 0:
+                continue
+            for h in range(g * G, (g + 1) * G):
+                s = scale * (K @ qv[b, h])
+                m = s.max()
+                p = np.exp(s - m)
+                l = p.sum()
+                out[b, h] = (p @ V) / l
+                lse[b, h] = m + np.log(l)
+    return out, lse

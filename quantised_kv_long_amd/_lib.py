@@ -67,10 +67,27 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_data_row_bytes.restype = ctypes.c_size_t
     lib.kvq_scale_row_bytes.argtypes = [i32, i32]
     lib.kvq_scale_row_bytes.restype = ctypes.c_size_t
+    i64 = ctypes.c_int64
+    lib.kvq_tier_cache_bytes.argtypes = [i32, i64, i32, i32, i32]
+    lib.kvq_tier_cache_bytes.restype = i64
+    lib.kvq_select_kv_tier.argtypes = [i64, i32, i32, i32, i64, i64, i64, ctypes.POINTER(i64),
+                                       ctypes.POINTER(i64)]
+    lib.kvq_select_kv_tier.restype = i32
+    lib.kvq_tier_types.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.kvq_tier_types.restype = i32
     lib.kvq_status_string.argtypes = [i32]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_quantize_append.argtypes = [DP, DP, P, P, P, i32, i32, i32, i32, i32, P]
     lib.kvq_quantize_append.restype = i32
+    lib.kvq_quantize_rows.argtypes = [DP, DP, DP, DP, P, P, i32, i32, i32, i32, i32, P]
+    lib.kvq_quantize_rows.restype = i32
+    lib.kvq_combine_regions.argtypes = [i32, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P),
+                                        ctypes.POINTER(i32), ctypes.POINTER(i32), i32, i32, i32, i32,
+                                        P, P, P]
+    lib.kvq_combine_regions.restype = i32
+    lib.kvq_decode_attn_multi.argtypes = [DP, DP, P, P, i32, i32, i32, i32, i32, f32, i32, i32, i32,
+                                          P, P, P]
+    lib.kvq_decode_attn_multi.restype = i32
     lib.kvq_decode_attn.argtypes = [DP, DP, P, P, i32, i32, i32, i32, f32, i32, i32, i32, P, P, P]
     lib.kvq_decode_attn.restype = i32
     lib.kvq_decode_attn_variant.argtypes = [DP, DP, P, P, i32, i32, i32, i32, f32, i32, i32, i32,
@@ -125,6 +142,30 @@ def kvq_scale_row_bytes(t, head_dim: int) -> int:
     return int(load().kvq_scale_row_bytes(_tcode(t), head_dim))
 
 
+TIERS = {0: ("f16", "f16"), 1: ("q8_0", "q8_0"), 2: ("q8_0", "q4_0"), 3: ("q5_1", "q4_0")}
+
+
+def kvq_tier_cache_bytes(tier: int, n_ctx: int, n_layers: int, Hkv: int, D: int) -> int:
+    return int(load().kvq_tier_cache_bytes(tier, n_ctx, n_layers, Hkv, D))
+
+
+def kvq_select_kv_tier(n_ctx: int, n_layers: int, Hkv: int, D: int, free_bytes: int,
+                       resident_bytes: int, vram_target_bytes: int = 0):
+    """Returns (tier, budget bytes, cache bytes of the tier)."""
+    budget, cache = ctypes.c_int64(), ctypes.c_int64()
+    rc = load().kvq_select_kv_tier(n_ctx, n_layers, Hkv, D, free_bytes, resident_bytes,
+                                   vram_target_bytes, ctypes.byref(budget), ctypes.byref(cache))
+    if rc < 0:
+        _check("kvq_select_kv_tier", rc)
+    return rc, budget.value, cache.value
+
+
+def kvq_tier_types(tier: int):
+    tk, tv = ctypes.c_int(), ctypes.c_int()
+    _check("kvq_tier_types", load().kvq_tier_types(tier, ctypes.byref(tk), ctypes.byref(tv)))
+    return tk.value, tv.value
+
+
 def kvq_status_string(status: int) -> str:
     return load().kvq_status_string(status).decode()
 
@@ -137,6 +178,15 @@ def kvq_quantize_append(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, k_new,
     return _check("kvq_quantize_append", rc)
 
 
+def kvq_quantize_rows(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, k_src: kvq_plane_desc,
+                      v_src: kvq_plane_desc, counts, positions, B: int, max_rows: int, Hkv: int, D: int,
+                      max_end: int, stream=None) -> int:
+    rc = load().kvq_quantize_rows(ctypes.byref(k_cache), ctypes.byref(v_cache), ctypes.byref(k_src),
+                                  ctypes.byref(v_src), _ptr(counts), _ptr(positions), B, max_rows, Hkv,
+                                  D, max_end, _stream(stream))
+    return _check("kvq_quantize_rows", rc)
+
+
 def kvq_decode_attn(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, q, seq_lens, B: int, Hq: int,
                     Hkv: int, D: int, softmax_scale: float, max_seq_len: int, split_tokens: int,
                     max_splits: int, part_o, part_lse, stream=None) -> int:
@@ -145,6 +195,17 @@ def kvq_decode_attn(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, q, seq_len
                                 split_tokens, max_splits, _ptr(part_o), _ptr(part_lse),
                                 _stream(stream))
     return _check("kvq_decode_attn", rc)
+
+
+def kvq_decode_attn_multi(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, q, seq_lens, B: int,
+                          n_q: int, Hq: int, Hkv: int, D: int, softmax_scale: float,
+                          max_seq_len: int, split_tokens: int, max_splits: int, part_o, part_lse,
+                          stream=None) -> int:
+    rc = load().kvq_decode_attn_multi(ctypes.byref(k_cache), ctypes.byref(v_cache), _ptr(q),
+                                      _ptr(seq_lens), B, n_q, Hq, Hkv, D, float(softmax_scale),
+                                      max_seq_len, split_tokens, max_splits, _ptr(part_o),
+                                      _ptr(part_lse), _stream(stream))
+    return _check("kvq_decode_attn_multi", rc)
 
 
 def kvq_decode_attn_variant(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, q, seq_lens, B: int,
@@ -165,6 +226,23 @@ def kvq_combine(part_o, part_lse, seq_lens, B: int, Hq: int, D: int, split_token
     rc = load().kvq_combine(_ptr(part_o), _ptr(part_lse), _ptr(seq_lens), B, Hq, D, split_tokens,
                             max_splits, ot, _ptr(out), _ptr(lse_out), _stream(stream))
     return _check("kvq_combine", rc)
+
+
+def kvq_combine_regions(part_o, part_lse, seq_lens, split_tokens, max_splits, B: int, Hq: int,
+                        D: int, out_type, out, lse_out=None, stream=None) -> int:
+    """Each of part_o, part_lse, seq_lens, split_tokens, max_splits is a list with
+    one entry per region."""
+    n = len(part_o)
+    if not (len(part_lse) == len(seq_lens) == len(split_tokens) == len(max_splits) == n):
+        raise ValueError("one entry per region in every list")
+    P = ctypes.c_void_p
+    arr = lambda xs: (P * max(n, 1))(*[_ptr(x) for x in xs])
+    ints = lambda xs: (ctypes.c_int * max(n, 1))(*[int(x) for x in xs])
+    ot = OUT_F32 if out_type in ("f32", OUT_F32) else _tcode(out_type)
+    rc = load().kvq_combine_regions(n, arr(part_o), arr(part_lse), arr(seq_lens), ints(split_tokens),
+                                    ints(max_splits), B, Hq, D, ot, _ptr(out), _ptr(lse_out),
+                                    _stream(stream))
+    return _check("kvq_combine_regions", rc)
 
 
 def kvq_decode_step(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, k_new, v_new, q, seq_lens,

@@ -70,6 +70,35 @@ def append(kc: CachePlanes, vc: CachePlanes, k_new: torch.Tensor, v_new: torch.T
                                     D, max_end, stream)
 
 
+def quantize_rows(kc: CachePlanes, vc: CachePlanes, k_src: CachePlanes, v_src: CachePlanes,
+                  counts: torch.Tensor, positions: torch.Tensor, max_rows: int, max_end: int,
+                  stream=None):
+    """kvq_quantize_rows: rows [0, counts[b]) of the fp16 planes k_src / v_src
+    into rows positions[b] + r of kc / vc."""
+    return _lib.kvq_quantize_rows(kc.desc(), vc.desc(), k_src.desc(), v_src.desc(), counts, positions,
+                                  kc.B, max_rows, kc.Hkv, kc.D, max_end, stream)
+
+
+def combine_regions(parts, seq_lens, out: torch.Tensor, lse_out=None, stream=None):
+    """kvq_combine_regions over the Partials of several regions (one seq_lens
+    tensor per region) into ``out`` (B, Hq, D) fp16 or fp32."""
+    B, Hq, D = out.shape
+    ot = "f16" if out.dtype == torch.float16 else "f32"
+    return _lib.kvq_combine_regions([p.o for p in parts], [p.lse for p in parts], list(seq_lens),
+                                    [p.split_tokens for p in parts], [p.max_splits for p in parts],
+                                    B, Hq, D, ot, out, lse_out, stream)
+
+
+def decode_multi(kc: CachePlanes, vc: CachePlanes, q: torch.Tensor, seq_lens: torch.Tensor,
+                 max_seq_len: int, part: "Partials", softmax_scale: float, stream=None):
+    """kvq_decode_attn_multi: q (B, n_q, Hq, D) fp16; ``part`` built for n_q * Hq
+    heads."""
+    B, n_q, Hq, D = q.shape
+    return _lib.kvq_decode_attn_multi(kc.desc(), vc.desc(), q, seq_lens, B, n_q, Hq, kc.Hkv, D,
+                                      softmax_scale, max_seq_len, part.split_tokens,
+                                      part.max_splits, part.o, part.lse, stream)
+
+
 def decode(kc: CachePlanes, vc: CachePlanes, q: torch.Tensor, seq_lens: torch.Tensor,
            max_seq_len: int, part: Partials, softmax_scale: float, variant="auto", stream=None):
     """kvq_decode_attn_variant on torch tensors: q (B, Hq, D) fp16."""

@@ -29,7 +29,35 @@ __global__ void __launch_bounds__(CMB_NT) combine_kernel(CombineArgs a)
         combine_rows<16>(pl, po, S, a.D, a.out_f16, out, lse, sm);
 }
 
+// The same merge over the partials of several regions (HAL #582 section 5
+// P2: each region of a mixed cache, the fp16 window and the quantised tail,
+// has its own typed attention launch; their partials are merged exactly).
+__global__ void __launch_bounds__(CMB_NT) combine_regions_kernel(CombineRegionsArgs a)
+{
+    __shared__ CombineLds sm;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int64_t bh = (int64_t)b * a.Hq + h;
+    void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh * a.D)
+                          : (void*)(reinterpret_cast<float*>(a.out) + bh * a.D);
+    CombineState st = combine_init();
+    for (int i = 0; i < a.n; ++i) {
+        const int L = a.seq_lens[i][b];
+        const int S = L > 0 ? min((L + a.split_tokens[i] - 1) / a.split_tokens[i], a.max_splits[i]) : 0;
+        const float* pl = a.part_lse[i] + bh * a.max_splits[i];
+        const float* po = a.part_o[i] + bh * a.max_splits[i] * a.D;
+        combine_fold<8>(pl, po, S, a.D, st);
+    }
+    combine_finish(st, a.D, a.out_f16, out, a.lse_out ? a.lse_out + bh : nullptr, sm);
+}
+
 }  // namespace
+
+hipError_t launch_combine_regions(const CombineRegionsArgs& a, hipStream_t s)
+{
+    dim3 grid(a.Hq, a.B);
+    hipLaunchKernelGGL(combine_regions_kernel, grid, dim3(CMB_NT), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s)
 {

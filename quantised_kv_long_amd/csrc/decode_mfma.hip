@@ -182,20 +182,22 @@ struct Cfg {
                                   WAVES * BUF <= 64 * 1024;
 };
 
-// Bytes of the four-wave merge area: per wave and head the running max, sum
-// and weight, the V offset sums per block, the corrections, and the G x D
-// accumulators of every wave.
+// Bytes of the four-wave merge area: per wave and score column the running
+// max, sum and weight, the V offset sums per block, the corrections, and the
+// nc x D accumulators of every wave (nc = query tokens x heads per KV head).
 template <int TK, int TV, int D>
-__host__ __device__ constexpr size_t merge_lds_bytes(int G)
+__host__ __device__ constexpr size_t merge_lds_bytes(int nc)
 {
     return Cfg<TK, TV, D>::DS > 1 ? 0
                                   : sizeof(float) * ((size_t)WAVES * 16 * 3 + (size_t)WAVES * 16 * (D / 32) +
-                                                     16 * (D / 32) + (size_t)WAVES * G * D);
+                                                     16 * (D / 32) + (size_t)WAVES * nc * D);
 }
 
 // 128-column slices are built for two waves per SIMD (at most 256
 // registers); head_dim 256 needs more and runs one
-template <int TK, int TV, int D>
+// MQ: several query tokens per sequence (a.nq > 1); a separate instance, so
+// that the single-token kernels carry none of its per-column index arithmetic
+template <int TK, int TV, int D, bool MQ>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 decode_mfma_kernel(DecodeArgs a)
 {
@@ -210,17 +212,24 @@ decode_mfma_kernel(DecodeArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, lq = lane >> 4;       // column / lane row of the 16x16 layouts
     const int G = a.G;
+    // score columns: NQ query tokens x G heads; column c is token c / G (the
+    // last NQ rows of the sequence are the query tokens: token i sees rows
+    // [0, L - NQ + 1 + i)) and head h0 + c % G
+    const int NQ = MQ ? a.nq : 1, NC = NQ * G;
     const int L = a.seq_lens[b];
     const int t_begin = s * a.split_tokens;
     const int t_end = min(t_begin + a.split_tokens, L);
     const int h0 = g * G;
     const int64_t ho_stride = (int64_t)a.max_splits * D;
-    float* po = a.part_o + (((int64_t)b * a.Hq + h0) * a.max_splits + s) * D;
-    float* pl = a.part_lse + ((int64_t)b * a.Hq + h0) * a.max_splits + s;
+    const int64_t HQT = (int64_t)NQ * a.Hq;        // rows of the partials' head axis
+    float* po = a.part_o + (((int64_t)b * HQT + h0) * a.max_splits + s) * D;
+    float* pl = a.part_lse + ((int64_t)b * HQT + h0) * a.max_splits + s;
+    // partial row of column c, relative to (b, h0)
+    auto crow = [&](int c) -> int64_t { return MQ ? (int64_t)(c / G) * a.Hq + c % G : (int64_t)c; };
 
     if (t_begin >= t_end) {
-        for (int i = tid; i < G * D; i += NT) po[(i / D) * ho_stride + (i % D)] = 0.0f;
-        if (tid < G) pl[(int64_t)tid * a.max_splits] = -INFINITY;
+        for (int i = tid; i < NC * D; i += NT) po[crow(i / D) * ho_stride + (i % D)] = 0.0f;
+        if (tid < NC) pl[crow(tid) * a.max_splits] = -INFINITY;
         return;
     }
 
@@ -236,7 +245,7 @@ decode_mfma_kernel(DecodeArgs a)
     //      row L-1 first quantises the new K and V rows of its KV head into
     //      that row (the same block quantiser as kvq_quantize_append), then
     //      makes them visible to its own loads
-    if (a.k_new != nullptr && t_end == L) {
+    if (a.k_new != nullptr && t_end == L) {   // (single query token)
         // 2*NB_ROW blocks (K then V), one aligned half-wave of 32 lanes per block
         for (int blk2 = tid >> 5; blk2 < 2 * C::NB_ROW; blk2 += NT / 32) {
             const bool isv = blk2 >= C::NB_ROW;
@@ -266,7 +275,9 @@ decode_mfma_kernel(DecodeArgs a)
     floatx4 kbias[C::NB];
     // (run after the first tiles' loads are issued, so they overlap)
     auto init_q = [&]() {
-        const uint16_t* qh = a.q + ((int64_t)b * a.Hq + h0 + min(ln, G - 1)) * D + wsl * C::DW;
+        const int c = min(ln, NC - 1);
+        const uint16_t* qh = MQ ? a.q + (((int64_t)b * NQ + c / G) * a.Hq + h0 + c % G) * D + wsl * C::DW
+                                : a.q + ((int64_t)b * a.Hq + h0 + c) * D + wsl * C::DW;
         const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
         for (int kb = 0; kb < C::NB; ++kb) {
@@ -286,7 +297,7 @@ decode_mfma_kernel(DecodeArgs a)
             float part = 0.0f;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                if (ln >= G) w[c] = 0;
+                if (ln >= NC) w[c] = 0;
                 part = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, w[c]), one2, part, false);
             }
             qop[kb] = make_half8(w[0], w[1], w[2], w[3]);
@@ -307,7 +318,15 @@ decode_mfma_kernel(DecodeArgs a)
     for (int i = 0; i < C::NDT; ++i) oacc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < C::NB; ++i) bacc[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_ref = -INFINITY, l_part = 0.0f;
+    // running maximum starts at a finite floor: a column can see no row at all
+    // in a wave (a query token's causal limit lies before the wave's tiles),
+    // and its weights must then be exp2(-inf - floor) = 0, not NaN
+    constexpr float M_FLOOR = -1.0e30f;
+    float m_ref = MQ ? M_FLOOR : -INFINITY, l_part = 0.0f;
+    // rows this lane's column sees: [0, c_end), the split's end included;
+    // below t_lim every column sees every row of the split
+    const int c_end = MQ ? min(t_end, L - NQ + 1 + min(ln, NC - 1) / G) : t_end;
+    const int t_lim = MQ ? min(t_end, L - NQ + 1) : t_end;
 
     const int ntiles = (t_end - t_begin + TT - 1) / TT;
     // K row of subtile j read by this lane (tile-relative): rows of the A
@@ -535,7 +554,9 @@ decode_mfma_kernel(DecodeArgs a)
 
         // -- online softmax (log2 domain)
         float sv[8];
-        const bool tail = t0 + TT > t_end;   // the split's last tile: rows past its end drop out
+        // the split's last tile, or a tile holding query tokens' rows: rows
+        // past the split's end or the column's causal limit drop out
+        const bool tail = t0 + TT > t_lim;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -544,12 +565,12 @@ decode_mfma_kernel(DecodeArgs a)
             if (tail) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    if (t0 + 8 * lq + e >= t_end) sv[e] = -INFINITY;
+                    if (t0 + 8 * lq + e >= c_end) sv[e] = -INFINITY;
             }
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (tail && t0 + 8 * lq + e >= t_end) sv[e] = -INFINITY;
+                if (tail && t0 + 8 * lq + e >= c_end) sv[e] = -INFINITY;
         }
         float mx = sv[0];
 #pragma unroll
@@ -696,23 +717,33 @@ decode_mfma_kernel(DecodeArgs a)
     if constexpr (C::DS > 1) {
         // every wave holds the same (m, l) and its own slice of O: write it
         const float l_head = xsum4(l_part);
-        if (ln < G) {
-            const float inv = (C::V_SCALE ? TWO24 : 1.0f) / l_head;
-            float* prow = po + ln * ho_stride + wsl * C::DW;
+        if (ln < NC) {
+            // (a column that saw no row: l = 0, o = 0, lse = -inf)
+            const float inv = l_head > 0.0f ? (C::V_SCALE ? TWO24 : 1.0f) / l_head : 0.0f;
+            float* prow = po + crow(ln) * ho_stride + wsl * C::DW;
 #pragma unroll
-            for (int t = 0; t < C::NDT; ++t)
+            for (int t = 0; t < C::NDT; ++t) {
+                float o[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int m = 4 * lq + i;
-                    int d;
-                    if constexpr (TV == T_Q4) d = 32 * (t >> 1) + 8 * (t & 1) + (m >> 1) + 16 * (m & 1);
-                    else d = 16 * t + m;
-                    float o = oacc[t][i];
-                    if constexpr (C::V_SCALE) o -= bacc[t >> 1][i];
-                    prow[d] = o * inv;
+                    o[i] = oacc[t][i];
+                    if constexpr (C::V_SCALE) o[i] -= bacc[t >> 1][i];
+                    o[i] *= inv;
                 }
+                // register i holds output row m = 4*lq + i of the tile: for
+                // q4_0 V column 32*(t/2) + 8*(t%2) + m/2 + 16*(m%2), i.e. two
+                // adjacent pairs 16 apart; otherwise column 16*t + m, four
+                // adjacent values
+                if constexpr (TV == T_Q4) {
+                    float* d0 = prow + 32 * (t >> 1) + 8 * (t & 1) + 2 * lq;
+                    *reinterpret_cast<float2*>(d0) = make_float2(o[0], o[2]);
+                    *reinterpret_cast<float2*>(d0 + 16) = make_float2(o[1], o[3]);
+                } else {
+                    *reinterpret_cast<float4*>(prow + 16 * t + 4 * lq) = make_float4(o[0], o[1], o[2], o[3]);
+                }
+            }
             if (wave == 0 && lq == 0)
-                pl[(int64_t)ln * a.max_splits] = (m_ref + log2f(l_head)) * 0.69314718055994531f;
+                pl[crow(ln) * a.max_splits] = (m_ref + log2f(l_head)) * 0.69314718055994531f;
         }
         return;
     }
@@ -723,13 +754,13 @@ decode_mfma_kernel(DecodeArgs a)
     //      every output column is a four-term weighted sum.
     const float l_head = xsum4(l_part);
     __syncthreads();
-    uint8_t* marea = merge_lds_bytes<TK, TV, D>(G) <= sizeof(lds_a) ? lds_a : lds_merge_dyn;
+    uint8_t* marea = merge_lds_bytes<TK, TV, D>(NC) <= sizeof(lds_a) ? lds_a : lds_merge_dyn;
     float* mw = reinterpret_cast<float*>(marea);          // [WAVES][16]   running max
     float* lw = mw + WAVES * 16;                          // [WAVES][16]   running sum
     float* fw = lw + WAVES * 16;                          // [WAVES][16]   merge weights
     float* bw = fw + WAVES * 16;                          // [WAVES][16][NB] V offset sums
     float* corr = bw + WAVES * 16 * C::NB;                // [16][NB]      corrections
-    float* ow = corr + 16 * C::NB;                        // [WAVES][G][D] accumulators
+    float* ow = corr + 16 * C::NB;                        // [WAVES][NC][D] accumulators
     if (lq == 0) {
         mw[wave * 16 + ln] = m_ref;
         lw[wave * 16 + ln] = l_head;
@@ -738,8 +769,8 @@ decode_mfma_kernel(DecodeArgs a)
             for (int kb = 0; kb < C::NB; ++kb) bw[(wave * 16 + ln) * C::NB + kb] = bacc[kb][0];
         }
     }
-    if (ln < G) {
-        float* orow = ow + (wave * G + ln) * D;
+    if (ln < NC) {
+        float* orow = ow + (wave * NC + ln) * D;
 #pragma unroll
         for (int t = 0; t < C::NDT; ++t)
 #pragma unroll
@@ -752,7 +783,7 @@ decode_mfma_kernel(DecodeArgs a)
             }
     }
     __syncthreads();
-    if (tid < G) {
+    if (tid < NC) {
         const int n = tid;
         float M = -INFINITY;
 #pragma unroll
@@ -760,11 +791,12 @@ decode_mfma_kernel(DecodeArgs a)
         float f[WAVES], lsum = 0.0f;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
-            f[w] = exp2f(mw[w * 16 + n] - M);     // exp2(-inf) = 0 for idle waves
+            f[w] = exp2f(mw[w * 16 + n] - M);     // 0 for waves that saw no row (m at the floor)
             lsum += f[w] * lw[w * 16 + n];
         }
-        // quantised V: O = (acc - offset sum) * 2^24
-        const float inv = (C::V_SCALE ? TWO24 : 1.0f) / lsum;
+        // quantised V: O = (acc - offset sum) * 2^24 (no row at all: o = 0,
+        // lse = -inf)
+        const float inv = lsum > 0.0f ? (C::V_SCALE ? TWO24 : 1.0f) / lsum : 0.0f;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) fw[w * 16 + n] = f[w] * inv;
         if constexpr (C::V_SCALE) {
@@ -776,16 +808,16 @@ decode_mfma_kernel(DecodeArgs a)
                 corr[n * C::NB + kb] = c;
             }
         }
-        pl[(int64_t)n * a.max_splits] = (M + log2f(lsum)) * 0.69314718055994531f;
+        pl[crow(n) * a.max_splits] = (M + log2f(lsum)) * 0.69314718055994531f;
     }
     __syncthreads();
-    for (int idx = tid; idx < G * (D / 4); idx += NT) {
+    for (int idx = tid; idx < NC * (D / 4); idx += NT) {
         const int n = idx / (D / 4), c4 = idx % (D / 4);
         float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
             const float f = fw[w * 16 + n];
-            const float4 v = reinterpret_cast<const float4*>(ow + (w * G + n) * D)[c4];
+            const float4 v = reinterpret_cast<const float4*>(ow + (w * NC + n) * D)[c4];
             o.x = fmaf(f, v.x, o.x);
             o.y = fmaf(f, v.y, o.y);
             o.z = fmaf(f, v.z, o.z);
@@ -798,7 +830,7 @@ decode_mfma_kernel(DecodeArgs a)
             o.z -= c;
             o.w -= c;
         }
-        reinterpret_cast<float4*>(po + n * ho_stride)[c4] = o;
+        reinterpret_cast<float4*>(po + crow(n) * ho_stride)[c4] = o;
     }
 }
 
@@ -808,18 +840,34 @@ constexpr bool cfg_valid() { return Cfg<TK, TV, D>::VALID; }
 // Dynamic LDS of a launch: the merge area, when it does not fit in the
 // static stage array.
 template <int TK, int TV, int D>
-size_t dyn_lds_bytes(int G)
+size_t dyn_lds_bytes(int nc)
 {
     using C = Cfg<TK, TV, D>;
-    const size_t merge = merge_lds_bytes<TK, TV, D>(G);
+    const size_t merge = merge_lds_bytes<TK, TV, D>(nc);
     return merge <= (size_t)WAVES * C::BUF ? 0 : merge;
 }
 
 template <int TK, int TV, int D>
-size_t lds_bytes(int G)
+size_t lds_bytes(int nc)
 {
     using C = Cfg<TK, TV, D>;
-    return (size_t)WAVES * C::BUF + sizeof(float) * C::SX_FLOATS + dyn_lds_bytes<TK, TV, D>(G);
+    return (size_t)WAVES * C::BUF + sizeof(float) * C::SX_FLOATS + dyn_lds_bytes<TK, TV, D>(nc);
+}
+
+template <int TK, int TV, int D, bool MQ>
+hipError_t launch4(const DecodeArgs& a, hipStream_t s)
+{
+    dim3 grid(a.max_splits, a.Hkv, a.B);
+    const int nc = a.nq * a.G;
+    const size_t dyn = dyn_lds_bytes<TK, TV, D>(nc);
+    if (lds_bytes<TK, TV, D>(nc) > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&decode_mfma_kernel<TK, TV, D, MQ>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((decode_mfma_kernel<TK, TV, D, MQ>), grid, dim3(NT), dyn, s, a);
+    return hipGetLastError();
 }
 
 template <int TK, int TV, int D>
@@ -828,16 +876,7 @@ hipError_t launch3(const DecodeArgs& a, hipStream_t s)
     if constexpr (!Cfg<TK, TV, D>::VALID) {
         return hipErrorInvalidConfiguration;
     } else {
-        dim3 grid(a.max_splits, a.Hkv, a.B);
-        const size_t dyn = dyn_lds_bytes<TK, TV, D>(a.G);
-        if (lds_bytes<TK, TV, D>(a.G) > 64 * 1024) {
-            const hipError_t e = hipFuncSetAttribute(
-                reinterpret_cast<const void*>(&decode_mfma_kernel<TK, TV, D>),
-                hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-            if (e != hipSuccess) return e;
-        }
-        hipLaunchKernelGGL((decode_mfma_kernel<TK, TV, D>), grid, dim3(NT), dyn, s, a);
-        return hipGetLastError();
+        return a.nq > 1 ? launch4<TK, TV, D, true>(a, s) : launch4<TK, TV, D, false>(a, s);
     }
 }
 
@@ -865,9 +904,10 @@ hipError_t launch1(const DecodeArgs& a, hipStream_t s)
 template <int TK, int TV>
 bool supports2(const DecodeArgs& a)
 {
-    if (a.D == 128) return cfg_valid<TK, TV, 128>() && lds_bytes<TK, TV, 128>(a.G) <= 160 * 1024;
-    if (a.D == 256) return cfg_valid<TK, TV, 256>() && lds_bytes<TK, TV, 256>(a.G) <= 160 * 1024;
-    if (a.D == 512) return cfg_valid<TK, TV, 512>() && lds_bytes<TK, TV, 512>(a.G) <= 160 * 1024;
+    const int nc = a.nq * a.G;
+    if (a.D == 128) return cfg_valid<TK, TV, 128>() && lds_bytes<TK, TV, 128>(nc) <= 160 * 1024;
+    if (a.D == 256) return cfg_valid<TK, TV, 256>() && lds_bytes<TK, TV, 256>(nc) <= 160 * 1024;
+    if (a.D == 512) return cfg_valid<TK, TV, 512>() && lds_bytes<TK, TV, 512>(nc) <= 160 * 1024;
     return false;
 }
 
@@ -886,7 +926,7 @@ bool supports1(const DecodeArgs& a)
 bool decode_mfma_supports(const DecodeArgs& a)
 {
     if (a.D != 128 && a.D != 256 && a.D != 512) return false;
-    if (a.G < 1 || a.G > 16) return false;
+    if (a.G < 1 || a.nq < 1 || a.nq * a.G > 16) return false;
     // rows read are below max_seq_len; their offsets inside one (sequence,
     // KV head) plane are computed in 32 bits
     const int64_t rows = a.max_seq_len;

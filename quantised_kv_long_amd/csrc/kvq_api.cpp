@@ -80,6 +80,7 @@ kvq::DecodeArgs decode_args(const kvq_plane_desc* k_cache, const kvq_plane_desc*
     a.Hkv = Hkv;
     a.D = D;
     a.G = Hq / Hkv;
+    a.nq = 1;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.max_seq_len = max_seq_len;
     a.split_tokens = split_tokens;
@@ -105,6 +106,57 @@ size_t kvq_scale_row_bytes(int type, int head_dim)
 {
     if (!known_type(type) || head_dim <= 0 || head_dim % 32 != 0) return 0;
     return type == KVQ_F16 ? 0 : (size_t)(head_dim / 16);
+}
+
+int64_t kvq_tier_cache_bytes(int tier, int64_t n_ctx, int n_layers, int Hkv, int D)
+{
+    if (n_ctx <= 0 || n_layers <= 0 || Hkv <= 0 || D <= 0 || D % 32 != 0) return -1;
+    // bytes of 32 values: f16 64, q8_0 34, q4_0 18, q5_1 24
+    int kb, vb;
+    switch (tier) {
+    case KVQ_TIER_F16: kb = 64; vb = 64; break;
+    case KVQ_TIER_Q8_Q8: kb = 34; vb = 34; break;
+    case KVQ_TIER_Q8_Q4: kb = 34; vb = 18; break;
+    case KVQ_TIER_Q51_Q4: kb = 24; vb = 18; break;
+    default: return -1;
+    }
+    return n_ctx * (int64_t)n_layers * Hkv * (D / 32) * (int64_t)(kb + vb);
+}
+
+int kvq_select_kv_tier(int64_t n_ctx, int n_layers, int Hkv, int D, int64_t free_bytes,
+                       int64_t resident_bytes, int64_t vram_target_bytes, int64_t* budget_bytes,
+                       int64_t* cache_bytes)
+{
+    if (n_ctx <= 0 || n_layers <= 0 || Hkv <= 0 || D <= 0 || D % 32 != 0) return KVQ_ERR_SHAPE;
+    if (free_bytes < 0 || resident_bytes < 0 || vram_target_bytes < 0) return KVQ_ERR_SHAPE;
+    const int64_t reserve = 3LL << 29;  // 1.5 GiB for compute
+    const int64_t cap = vram_target_bytes > 0 && vram_target_bytes < free_bytes ? vram_target_bytes
+                                                                                : free_bytes;
+    const int64_t budget = cap - resident_bytes - reserve;
+    int tier = KVQ_TIER_Q51_Q4;
+    for (int t = KVQ_TIER_F16; t <= KVQ_TIER_Q51_Q4; ++t) {
+        if (kvq_tier_cache_bytes(t, n_ctx, n_layers, Hkv, D) <= budget) {
+            tier = t;
+            break;
+        }
+    }
+    if (budget_bytes) *budget_bytes = budget;
+    if (cache_bytes) *cache_bytes = kvq_tier_cache_bytes(tier, n_ctx, n_layers, Hkv, D);
+    return tier;
+}
+
+int kvq_tier_types(int tier, int* type_k, int* type_v)
+{
+    int tk, tv;
+    switch (tier) {
+    case KVQ_TIER_F16: tk = KVQ_F16; tv = KVQ_F16; break;
+    case KVQ_TIER_Q8_Q8: tk = KVQ_Q8_0; tv = KVQ_Q8_0; break;
+    case KVQ_TIER_Q8_Q4: tk = KVQ_Q8_0; tv = KVQ_Q4_0; break;
+    default: return KVQ_ERR_TYPE;
+    }
+    if (type_k) *type_k = tk;
+    if (type_v) *type_v = tv;
+    return KVQ_OK;
 }
 
 const char* kvq_status_string(int status)
@@ -145,10 +197,62 @@ int kvq_quantize_append(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_c
     a.tv = v_cache->type;
     a.k_new = static_cast<const uint16_t*>(k_new);
     a.v_new = static_cast<const uint16_t*>(v_new);
+    // [B][n_new][Hkv][D]
+    a.k_sb = a.v_sb = (int64_t)n_new * Hkv * D;
+    a.k_sr = a.v_sr = (int64_t)Hkv * D;
+    a.k_sg = a.v_sg = D;
+    a.counts = nullptr;
     a.positions = positions;
     a.seq_lens = nullptr;
     a.B = B;
     a.n_new = n_new;
+    a.Hkv = Hkv;
+    a.D = D;
+    (void)hipGetLastError();
+    return finish(kvq::launch_quantize_append(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvq_quantize_rows(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache,
+                      const kvq_plane_desc* k_src, const kvq_plane_desc* v_src, const int32_t* counts,
+                      const int32_t* positions, int B, int max_rows, int Hkv, int D, int max_end,
+                      void* stream)
+{
+    if (B < 0 || max_rows < 0 || Hkv < 1 || !valid_head_dim(D)) return KVQ_ERR_SHAPE;
+    if (B == 0 || max_rows == 0) return KVQ_OK;  // nothing to write (pointers may be NULL)
+    if (!counts || !positions) return KVQ_ERR_NULL;
+    if (max_end < 0) return KVQ_ERR_SHAPE;
+    int rc = check_plane(k_src, B, Hkv, max_rows);
+    if (rc != KVQ_OK) return rc;
+    rc = check_plane(v_src, B, Hkv, max_rows);
+    if (rc != KVQ_OK) return rc;
+    if (k_src->type != KVQ_F16 || v_src->type != KVQ_F16) return KVQ_ERR_TYPE;
+    rc = check_plane(k_cache, B, Hkv, max_end);
+    if (rc != KVQ_OK) return rc;
+    rc = check_plane(v_cache, B, Hkv, max_end);
+    if (rc != KVQ_OK) return rc;
+    if (!aligned(counts, 4) || !aligned(positions, 4)) return KVQ_ERR_ALIGN;
+    const int64_t n_blocks = (int64_t)B * max_rows * Hkv * (D / 32);
+    if ((n_blocks + 255) / 256 > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+
+    kvq::AppendArgs a;
+    a.k = to_plane(k_cache);
+    a.v = to_plane(v_cache);
+    a.tk = k_cache->type;
+    a.tv = v_cache->type;
+    a.k_new = static_cast<const uint16_t*>(k_src->data);
+    a.v_new = static_cast<const uint16_t*>(v_src->data);
+    // rows of fp16 planes: D values per row
+    a.k_sb = k_src->seq_stride_rows * D;
+    a.k_sr = D;
+    a.k_sg = k_src->head_stride_rows * D;
+    a.v_sb = v_src->seq_stride_rows * D;
+    a.v_sr = D;
+    a.v_sg = v_src->head_stride_rows * D;
+    a.counts = counts;
+    a.positions = positions;
+    a.seq_lens = nullptr;
+    a.B = B;
+    a.n_new = max_rows;
     a.Hkv = Hkv;
     a.D = D;
     (void)hipGetLastError();
@@ -185,6 +289,24 @@ int kvq_decode_attn(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache
                                    KVQ_VARIANT_AUTO, stream);
 }
 
+int kvq_decode_attn_multi(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache,
+                          const void* q, const int32_t* seq_lens, int B, int n_q, int Hq, int Hkv,
+                          int D, float softmax_scale, int max_seq_len, int split_tokens,
+                          int max_splits, float* part_o, float* part_lse, void* stream)
+{
+    int rc = validate_decode(k_cache, v_cache, q, seq_lens, B, Hq, Hkv, D, softmax_scale, max_seq_len,
+                             split_tokens, max_splits, part_o, part_lse);
+    if (rc != KVQ_OK) return rc;
+    if (n_q < 1 || (int64_t)n_q * (Hq / Hkv) > 16 || max_seq_len < n_q) return KVQ_ERR_SHAPE;
+    if ((int64_t)B * n_q * Hq > 65535LL * 65535LL) return KVQ_ERR_SHAPE;
+    kvq::DecodeArgs a = decode_args(k_cache, v_cache, q, seq_lens, B, Hq, Hkv, D, softmax_scale,
+                                    max_seq_len, split_tokens, max_splits, part_o, part_lse);
+    a.nq = n_q;
+    if (!kvq::decode_mfma_supports(a)) return KVQ_ERR_SHAPE;
+    (void)hipGetLastError();
+    return finish(kvq::launch_decode_mfma(a, static_cast<hipStream_t>(stream)));
+}
+
 int kvq_combine(const float* part_o, const float* part_lse, const int32_t* seq_lens, int B, int Hq,
                 int D, int split_tokens, int max_splits, int out_type, void* out, float* lse_out,
                 void* stream)
@@ -212,6 +334,41 @@ int kvq_combine(const float* part_o, const float* part_lse, const int32_t* seq_l
     a.lse_out = lse_out;
     (void)hipGetLastError();
     return finish(kvq::launch_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvq_combine_regions(int n_regions, const float* const* part_o, const float* const* part_lse,
+                        const int32_t* const* seq_lens, const int* split_tokens, const int* max_splits,
+                        int B, int Hq, int D, int out_type, void* out, float* lse_out, void* stream)
+{
+    if (n_regions < 1 || n_regions > kvq::MAX_REGIONS) return KVQ_ERR_SHAPE;
+    if (!part_o || !part_lse || !seq_lens || !split_tokens || !max_splits || !out) return KVQ_ERR_NULL;
+    if (out_type != KVQ_F16 && out_type != KVQ_OUT_F32) return KVQ_ERR_TYPE;
+    if (B < 1 || Hq < 1 || !valid_head_dim(D)) return KVQ_ERR_SHAPE;
+    if (B > 65535 || Hq > 65535) return KVQ_ERR_SHAPE;
+    if (!aligned(out, 16) || (lse_out && !aligned(lse_out, 4))) return KVQ_ERR_ALIGN;
+    kvq::CombineRegionsArgs a;
+    a.n = n_regions;
+    for (int i = 0; i < n_regions; ++i) {
+        if (!part_o[i] || !part_lse[i] || !seq_lens[i]) return KVQ_ERR_NULL;
+        if (split_tokens[i] < KVQ_SPLIT_GRANULE || split_tokens[i] % KVQ_SPLIT_GRANULE != 0)
+            return KVQ_ERR_SPLITS;
+        if (max_splits[i] < 1 || max_splits[i] > 65535) return KVQ_ERR_SPLITS;
+        if (!aligned(part_o[i], 16) || !aligned(part_lse[i], 4) || !aligned(seq_lens[i], 4))
+            return KVQ_ERR_ALIGN;
+        a.part_o[i] = part_o[i];
+        a.part_lse[i] = part_lse[i];
+        a.seq_lens[i] = seq_lens[i];
+        a.split_tokens[i] = split_tokens[i];
+        a.max_splits[i] = max_splits[i];
+    }
+    a.B = B;
+    a.Hq = Hq;
+    a.D = D;
+    a.out_f16 = out_type == KVQ_F16;
+    a.out = out;
+    a.lse_out = lse_out;
+    (void)hipGetLastError();
+    return finish(kvq::launch_combine_regions(a, static_cast<hipStream_t>(stream)));
 }
 
 int kvq_decode_step(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache, const void* k_new,
@@ -248,6 +405,11 @@ int kvq_decode_step(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache
         ap.tv = a.tv;
         ap.k_new = static_cast<const uint16_t*>(k_new);
         ap.v_new = static_cast<const uint16_t*>(v_new);
+        // [B][Hkv][D], one row
+        ap.k_sb = ap.v_sb = (int64_t)Hkv * D;
+        ap.k_sr = ap.v_sr = 0;
+        ap.k_sg = ap.v_sg = D;
+        ap.counts = nullptr;
         ap.positions = nullptr;  // row seq_lens[b] - 1
         ap.seq_lens = seq_lens;
         ap.B = B;

@@ -30,15 +30,25 @@ struct CombineLds {
     float4 a[CMB_NT];
 };
 
-// pl: the S partial lse values; po: the S partial rows of D floats (16-byte
-// aligned); writes D outputs at out (fp16 or fp32) and, if lse_dst is not
-// NULL, the merged lse.  Splits with lse = -inf carry no weight; S == 0 (or all
-// splits empty) gives out = 0, lse = -inf.  U splits are loaded per batch.
-// Weights are exp2((lse - m) * log2 e) on the hardware exp2: the relative
-// error of a weight is a few fp32 ulps times |lse - m|.
+// The running merge of one thread: max m, sum l, weighted row a.
+struct CombineState {
+    float m, l;
+    float4 a;
+};
+
+__device__ __forceinline__ CombineState combine_init()
+{
+    return CombineState{-INFINITY, 0.0f, make_float4(0.0f, 0.0f, 0.0f, 0.0f)};
+}
+
+// Folds the S partials at pl (lse values) / po (rows of D floats, 16-byte
+// aligned) into the thread's running state: its four columns of its residue
+// class of the splits.  Splits with lse = -inf carry no weight.  U splits are
+// loaded per batch.  Weights are exp2((lse - m) * log2 e) on the hardware
+// exp2: the relative error of a weight is a few fp32 ulps times |lse - m|.
 template <int U>
-__device__ __forceinline__ void combine_rows(const float* pl, const float* po, int S, int D,
-                                             bool out_f16, void* out, float* lse_dst, CombineLds& sm)
+__device__ __forceinline__ void combine_fold(const float* pl, const float* po, int S, int D,
+                                             CombineState& st)
 {
     const int tid = threadIdx.x;
     const int D4 = D >> 2;                 // float4 columns (D <= 512: at most 128)
@@ -46,8 +56,8 @@ __device__ __forceinline__ void combine_rows(const float* pl, const float* po, i
     const int c = tid % D4, r = tid / D4;
     const float4* po4 = reinterpret_cast<const float4*>(po);
 
-    float m = -INFINITY, l = 0.0f;
-    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float m = st.m, l = st.l;
+    float4 a = st.a;
     for (int s0 = r; s0 < S; s0 += R * U) {
         float ls[U];
         float4 v[U];
@@ -84,11 +94,24 @@ __device__ __forceinline__ void combine_rows(const float* pl, const float* po, i
             a.w += w * v[u].w;
         }
     }
+    st.m = m;
+    st.l = l;
+    st.a = a;
+}
 
+// Merges the residue classes' states through LDS and writes D outputs at out
+// (fp16 or fp32) and, if lse_dst is not NULL, the merged lse.  No weight at
+// all (no splits, or all empty) gives out = 0, lse = -inf.
+__device__ __forceinline__ void combine_finish(const CombineState& st, int D, bool out_f16, void* out,
+                                               float* lse_dst, CombineLds& sm)
+{
+    const int tid = threadIdx.x;
+    const int D4 = D >> 2;
+    const int R = CMB_NT / D4;
     __syncthreads();
-    sm.m[tid] = m;
-    sm.l[tid] = l;
-    sm.a[tid] = a;
+    sm.m[tid] = st.m;
+    sm.l[tid] = st.l;
+    sm.a[tid] = st.a;
     __syncthreads();
     if (tid < D4) {
         float M = -INFINITY;
@@ -123,6 +146,16 @@ __device__ __forceinline__ void combine_rows(const float* pl, const float* po, i
         }
         if (tid == 0 && lse_dst) *lse_dst = L > 0.0f ? M + logf(L) : -INFINITY;
     }
+}
+
+// The whole merge of the S partials of one (sequence, query head).
+template <int U>
+__device__ __forceinline__ void combine_rows(const float* pl, const float* po, int S, int D,
+                                             bool out_f16, void* out, float* lse_dst, CombineLds& sm)
+{
+    CombineState st = combine_init();
+    combine_fold<U>(pl, po, S, D, st);
+    combine_finish(st, D, out_f16, out, lse_dst, sm);
 }
 
 }  // namespace kvq

@@ -13,8 +13,12 @@ namespace kvq {
 struct AppendArgs {
     Plane k, v;
     int tk, tv;
+    // the source rows: value d of row r of KV head g of sequence b is at
+    // k_new + b*k_sb + r*k_sr + g*k_sg + d (fp16; likewise for V)
     const uint16_t* k_new;
     const uint16_t* v_new;
+    int64_t k_sb, k_sr, k_sg, v_sb, v_sr, v_sg;
+    const int32_t* counts;     // rows written per sequence; or null: n_new each
     const int32_t* positions;  // first row per sequence; or null: seq_lens[b] - n_new
     const int32_t* seq_lens;
     int B, n_new, Hkv, D;
@@ -26,6 +30,10 @@ struct DecodeArgs {
     const uint16_t* q;
     const int32_t* seq_lens;
     int B, Hq, Hkv, D, G;
+    // query tokens per sequence (1: single-token decode).  With nq > 1 (the
+    // matrix-core kernel only) q is [B][nq][Hq][D], the partials are
+    // [B][nq*Hq][max_splits][D], and token i of b sees rows [0, L_b - nq + 1 + i)
+    int nq;
     float scale_log2;  // softmax scale * log2(e)
     int max_seq_len, split_tokens, max_splits;
     float* part_o;
@@ -35,6 +43,22 @@ struct DecodeArgs {
     // workgroup whose split holds that row, before it reads it
     const uint16_t* k_new;
     const uint16_t* v_new;
+};
+
+// Partials of up to MAX_REGIONS regions (separate decode launches over
+// separate caches) merged into one output.
+constexpr int MAX_REGIONS = 4;
+struct CombineRegionsArgs {
+    int n;
+    const float* part_o[MAX_REGIONS];
+    const float* part_lse[MAX_REGIONS];
+    const int32_t* seq_lens[MAX_REGIONS];
+    int split_tokens[MAX_REGIONS];
+    int max_splits[MAX_REGIONS];
+    int B, Hq, D;
+    bool out_f16;
+    void* out;
+    float* lse_out;
 };
 
 struct CombineArgs {
@@ -52,5 +76,6 @@ hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
 bool decode_mfma_supports(const DecodeArgs& a);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_combine_regions(const CombineRegionsArgs& a, hipStream_t s);
 
 }  // namespace kvq

@@ -3,7 +3,9 @@
 // is quantised once, when it is written; section 1 gives the block formats).
 //
 // One thread per 32-value block; the block quantiser itself is in
-// kvq_quant.hpp.
+// kvq_quant.hpp.  The source rows are addressed through strides, so the same
+// kernel takes new tokens ([B][n_new][Hkv][D]) and rows of fp16 cache planes
+// (the rolling fp16 window of a mixed cache, quantised when it is evicted).
 #include "kvq_internal.hpp"
 #include "kvq_quant.hpp"
 
@@ -19,7 +21,6 @@ __global__ void __launch_bounds__(256) quantize_append_kernel(AppendArgs a)
     const bool is_v = blockIdx.y == 1;
     const Plane& P = is_v ? a.v : a.k;
     const int t = is_v ? a.tv : a.tk;
-    const uint16_t* src = (is_v ? a.v_new : a.k_new) + idx * 32;
 
     const int blk = (int)(idx % nb);
     int64_t rest = idx / nb;
@@ -27,6 +28,10 @@ __global__ void __launch_bounds__(256) quantize_append_kernel(AppendArgs a)
     rest /= a.Hkv;
     const int r = (int)(rest % a.n_new);
     const int b = (int)(rest / a.n_new);
+    if (a.counts && r >= a.counts[b]) return;
+    const uint16_t* src = is_v ? a.v_new + b * a.v_sb + r * a.v_sr + g * a.v_sg
+                               : a.k_new + b * a.k_sb + r * a.k_sr + g * a.k_sg;
+    src += 32 * blk;
     const int pos0 = a.positions ? a.positions[b] : a.seq_lens[b] - a.n_new;
     const int64_t row = (int64_t)b * P.seq_stride + (int64_t)g * P.head_stride + pos0 + r;
     uint8_t* dst = P.data + row * data_row_bytes(t, a.D) + (int64_t)blk * data_row_bytes(t, 32);

@@ -33,7 +33,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kvq_quantize_append", "kvq_decode_attn", "kvq_combine", "kvq_decode_attn_variant",
-              "kvq_decode_step", "kvq_data_row_bytes", "kvq_scale_row_bytes", "kvq_status_string"):
+              "kvq_decode_step", "kvq_quantize_rows", "kvq_combine_regions", "kvq_decode_attn_multi",
+              "kvq_select_kv_tier", "kvq_tier_cache_bytes", "kvq_tier_types", "kvq_data_row_bytes",
+              "kvq_scale_row_bytes", "kvq_status_string"):
         assert n in names
 
 
@@ -223,3 +225,72 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(_lib.KVQLibraryMissing):
         _lib.load(str(tmp_path / "libkvq.so"))
+
+
+def qrows(lib, k=None, v=None, ks=None, vs=None, counts=A, pos=A, B=2, max_rows=16, H=8, D=128,
+          max_end=100):
+    k = k if k is not None else plane()
+    v = v if v is not None else plane()
+    ks = ks if ks is not None else plane(t=0, cap=16)
+    vs = vs if vs is not None else plane(t=0, cap=16)
+    return lib.kvq_quantize_rows(ctypes.byref(k), ctypes.byref(v), ctypes.byref(ks), ctypes.byref(vs),
+                                 counts, pos, B, max_rows, H, D, max_end, None)
+
+
+@nogpu
+def test_quantize_rows_validation(lib):
+    assert qrows(lib, B=0) == 0 and qrows(lib, max_rows=0) == 0      # nothing to do
+    assert qrows(lib, B=-1) == -2
+    assert qrows(lib, D=48) == -2
+    assert qrows(lib, counts=None) == -1
+    assert qrows(lib, pos=None) == -1
+    assert qrows(lib, ks=plane(t=1, cap=16)) == -3                  # sources are fp16
+    assert qrows(lib, vs=plane(t=2, cap=16)) == -3
+    assert qrows(lib, ks=plane(t=0, cap=8)) == -5                   # max_rows beyond the source
+    assert qrows(lib, max_end=101) == -5
+    assert qrows(lib, counts=A + 2) == -4
+    assert qrows(lib, ks=plane(t=0, cap=16, data=A + 8)) == -4
+
+
+def cregions(lib, n=2, po=(A, A), pl=(A, A), lens=(A, A), split=(64, 64), ms=(4, 4), B=1, Hq=40,
+             D=128, ot=3, out=A, lse=None):
+    P = ctypes.c_void_p
+    k = max(n, 1)
+    arr = lambda xs: (P * k)(*(list(xs) + [None] * k)[:k])
+    ints = lambda xs: (ctypes.c_int * k)(*(list(xs) + [0] * k)[:k])
+    return lib.kvq_combine_regions(n, arr(po), arr(pl), arr(lens), ints(split), ints(ms), B, Hq, D, ot,
+                                   out, lse, None)
+
+
+@nogpu
+def test_combine_regions_validation(lib):
+    assert cregions(lib, n=0) == -2
+    assert cregions(lib, n=5, po=[A] * 5, pl=[A] * 5, lens=[A] * 5, split=[64] * 5, ms=[4] * 5) == -2
+    assert cregions(lib, po=(A, None)) == -1
+    assert cregions(lib, lens=(None, A)) == -1
+    assert cregions(lib, out=None) == -1
+    assert cregions(lib, ot=1) == -3
+    assert cregions(lib, D=40) == -2
+    assert cregions(lib, split=(64, 32)) == -6
+    assert cregions(lib, ms=(0, 4)) == -6
+    assert cregions(lib, po=(A, A + 8)) == -4
+    assert cregions(lib, out=A + 8, ot=3) == -4
+
+
+def multi(lib, k=None, v=None, q=A, lens=A, B=1, nq=3, Hq=40, Hkv=8, D=128, scale=0.088, max_len=100,
+          split=64, max_splits=2, po=A, pl=A):
+    k = k if k is not None else plane()
+    v = v if v is not None else plane()
+    return lib.kvq_decode_attn_multi(ctypes.byref(k), ctypes.byref(v), q, lens, B, nq, Hq, Hkv, D, scale,
+                                     max_len, split, max_splits, po, pl, None)
+
+
+@nogpu
+def test_decode_multi_validation(lib):
+    assert multi(lib, q=None) == -1                 # the decode checks come first
+    assert multi(lib, Hq=41) == -2
+    assert multi(lib, split=100) == -6
+    assert multi(lib, nq=0) == -2
+    assert multi(lib, nq=4) == -2                   # 4 tokens x 5 heads = 20 columns
+    assert multi(lib, nq=3, max_len=2, max_splits=1) == -2   # fewer rows than query tokens
+    assert multi(lib, D=64, nq=1) == -2             # the matrix-core kernel covers D 128/256/512

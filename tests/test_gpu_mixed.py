@@ -1,0 +1,254 @@
+"""The position-axis mixed cache (HAL #582 "per-layer KV compression study",
+section 5 P2): recent tokens in an fp16 window, older ones in a quantised tail.
+Each region gets its own kvq_decode_attn launch, kvq_combine_regions merges
+the two sets of partials, and kvq_quantize_rows quantises the window's rows
+into the tail when the window is evicted.
+
+Checked against the oracle: the merged output against its fp64 attention over
+the union of the regions' rows (attend_regions), the evicted rows byte for
+byte against its quantiser, and a run of decode steps with evictions in
+between against the oracle at every step."""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+
+from .gpu_util import (assert_close, download_planes, fill_pair, note, oracle_planes,
+                       oracle_threads, planes_to_oracle, require_gpu, to_host_u16,
+                       upload_oracle_planes)
+
+torch = pytest.importorskip("torch")
+from quantised_kv_long_amd import cache as C  # noqa: E402
+from quantised_kv_long_amd import synth  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+SENT_D, SENT_S = 0xA5, 0x5A5A
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def attend_mixed(tail, win, q, tail_lens, win_lens, st_tail, st_win, out_dtype=torch.float32):
+    """Two attention launches and the region merge; returns host fp64 (out, lse)."""
+    B, Hq, D = q.shape
+    scale = 1.0 / math.sqrt(D)
+    parts, lens_t = [], []
+    for (kc, vc), lens, st in ((tail, tail_lens, st_tail), (win, win_lens, st_win)):
+        lt = torch.tensor(lens, dtype=torch.int32, device=q.device)
+        cap = kc.capacity
+        part = C.Partials(B, Hq, D, cap, st)
+        C.decode(kc, vc, q, lt, cap, part, scale)
+        parts.append(part)
+        lens_t.append(lt)
+    out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    C.combine_regions(parts, lens_t, out, lse)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_mixed(tail, win, q, tail_lens, win_lens):
+    D = q.shape[-1]
+    return O.attend_regions(to_host_u16(q), [(planes_to_oracle(tail[0]), planes_to_oracle(tail[1]), tail_lens),
+                                             (planes_to_oracle(win[0]), planes_to_oracle(win[1]), win_lens)],
+                            tail[0].Hkv, 1.0 / math.sqrt(D), lib=None)
+
+
+CASES = [
+    # (B, Hkv, G, D, tail_lens, tail capacity, win_lens, window capacity, tail split, window split)
+    (2, 2, 5, 128, [1000, 300], 1000, [37, 64], 64, 256, 64),
+    (3, 2, 4, 128, [0, 129, 2000], 2000, [5, 0, 64], 64, 256, 64),
+    (1, 2, 8, 256, [777], 800, [100], 128, 128, 64),
+    (2, 1, 4, 512, [300, 65], 300, [1, 33], 64, 64, 64),
+    (2, 2, 5, 64, [200, 1], 200, [17, 64], 64, 64, 64),
+]
+
+
+@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0"), ("q8_0", "q8_0"), ("f16", "q4_0")])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_regions_match_oracle(tk, tv, case):
+    B, Hkv, G, D, tl, tcap, wl, wcap, st_t, st_w = CASES[case]
+    note(f"mixed {tk}/{tv} B={B} Hkv={Hkv} G={G} D={D} tail={tl} window={wl}")
+    dev = "cuda"
+    seed = 2100 + case
+    tail = fill_pair(tk, tv, synth.normal_f16((B, Hkv, tcap, D), seed, dev),
+                     synth.normal_f16((B, Hkv, tcap, D), seed + 1, dev))
+    win = fill_pair("f16", "f16", synth.normal_f16((B, Hkv, wcap, D), seed + 2, dev),
+                    synth.normal_f16((B, Hkv, wcap, D), seed + 3, dev))
+    q = synth.normal_f16((B, Hkv * G, D), seed + 4, dev)
+    out, lse = attend_mixed(tail, win, q, tl, wl, st_t, st_w)
+    ref, ref_lse = oracle_mixed(tail, win, q, tl, wl)
+    empty = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(lse), empty)
+    assert np.all(out[empty] == 0)
+    live = ~empty
+    if live.any():
+        assert_close(out[live], lse[live], ref[live], ref_lse[live], f"mixed {tk}/{tv} case {case}")
+
+
+def test_one_region_merge_equals_combine():
+    """kvq_combine_regions over one region gives kvq_combine's output (the same
+    merge; the loads are batched differently, so within fp32 rounding)."""
+    B, Hkv, G, D, L, st = 2, 2, 5, 128, [5000, 700], 64
+    note("combine_regions with one region")
+    dev = "cuda"
+    kc, vc = fill_pair("q8_0", "q4_0", synth.normal_f16((B, Hkv, max(L), D), 2201, dev),
+                       synth.normal_f16((B, Hkv, max(L), D), 2202, dev))
+    q = synth.normal_f16((B, Hkv * G, D), 2203, dev)
+    lt = torch.tensor(L, dtype=torch.int32, device=dev)
+    part = C.Partials(B, Hkv * G, D, max(L), st)
+    C.decode(kc, vc, q, lt, max(L), part, 1 / math.sqrt(D))
+    o1 = torch.empty((B, Hkv * G, D), dtype=torch.float32, device=dev)
+    l1 = torch.empty((B, Hkv * G), dtype=torch.float32, device=dev)
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    C.combine(part, lt, o1, l1)
+    C.combine_regions([part], [lt], o2, l2)
+    torch.cuda.synchronize()
+    assert torch.allclose(o1, o2, atol=1e-6, rtol=1e-5)
+    assert torch.allclose(l1, l2, atol=1e-6)
+
+
+@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q8_0"), ("f16", "q4_0")])
+def test_quantize_rows_bit_exact(tk, tv):
+    """Rows [0, counts[b]) of fp16 window planes land at rows positions[b] + r
+    of the tail, byte for byte the oracle's quantisation; no other row of the
+    tail changes."""
+    B, Hkv, D, W, cap = 3, 2, 128, 40, 200
+    counts, positions = [40, 0, 17], [0, 100, 183]
+    note(f"quantize_rows {tk}/{tv}")
+    dev = "cuda"
+    kw = synth.normal_f16((B, Hkv, W, D), 2301, dev)
+    vw = synth.normal_f16((B, Hkv, W, D), 2302, dev)
+    win = fill_pair("f16", "f16", kw, vw)
+    k_exp, v_exp = oracle_planes(tk, np.zeros((B, Hkv, cap, D), np.uint16)), \
+        oracle_planes(tv, np.zeros((B, Hkv, cap, D), np.uint16))
+    for p in (k_exp, v_exp):
+        p[1][:] = SENT_D
+        p[2][:] = SENT_S
+    k_dev = upload_oracle_planes(k_exp[0], k_exp[1].copy(), k_exp[2].copy())
+    v_dev = upload_oracle_planes(v_exp[0], v_exp[1].copy(), v_exp[2].copy())
+    kq = oracle_planes(tk, to_host_u16(kw))
+    vq = oracle_planes(tv, to_host_u16(vw))
+    for b in range(B):
+        n, p0 = counts[b], positions[b]
+        k_exp[1][b, :, p0:p0 + n] = kq[1][b, :, :n]
+        k_exp[2][b, :, p0:p0 + n] = kq[2][b, :, :n]
+        v_exp[1][b, :, p0:p0 + n] = vq[1][b, :, :n]
+        v_exp[2][b, :, p0:p0 + n] = vq[2][b, :, :n]
+    ct = torch.tensor(counts, dtype=torch.int32, device=dev)
+    pt = torch.tensor(positions, dtype=torch.int32, device=dev)
+    C.quantize_rows(k_dev, v_dev, win[0], win[1], ct, pt, W, max(c + p for c, p in zip(counts, positions)))
+    torch.cuda.synchronize()
+    for dev_p, want, what in ((k_dev, k_exp, "K"), (v_dev, v_exp, "V")):
+        d, s = download_planes(dev_p)
+        assert np.array_equal(d, want[1]), f"{what} data"
+        if want[0] != "f16":
+            assert np.array_equal(s, want[2]), f"{what} scales"
+
+
+@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0")])
+def test_rolling_window_decode_steps(tk, tv):
+    """Decode steps on a mixed cache: each new token goes into the fp16 window
+    (kvq_quantize_append on fp16 planes: a copy); when the window is full its
+    rows are quantised into the tail (kvq_quantize_rows) and it starts empty.
+    Every step's attention (two launches + the region merge) against the
+    oracle over tail + window, and the tail's bytes against the oracle's
+    quantiser of the same tokens."""
+    B, Hkv, G, D, W = 2, 2, 5, 128, 16
+    L0 = [300, 45]                      # tokens in the tail at the start
+    steps = 40
+    cap = max(L0) + steps + W
+    dev = "cuda"
+    note(f"rolling window {tk}/{tv}")
+    # every token's K and V (the tail holds tokens [0, Lq), the window the next Lw)
+    k_all = synth.normal_f16((B, Hkv, cap, D), 2401, dev)
+    v_all = synth.normal_f16((B, Hkv, cap, D), 2402, dev)
+    kh, vh = to_host_u16(k_all), to_host_u16(v_all)
+    k_q, v_q = oracle_planes(tk, kh), oracle_planes(tv, vh)        # expected tail bytes
+    tail_k = upload_oracle_planes(k_q[0], k_q[1].copy(), k_q[2].copy())
+    tail_v = upload_oracle_planes(v_q[0], v_q[1].copy(), v_q[2].copy())
+    # the tail on the device holds only tokens [0, L0) written by the oracle;
+    # later rows must come from evictions: blank them
+    for p in (tail_k, tail_v):
+        for b in range(B):
+            p.data[b, :, L0[b]:] = SENT_D
+            if p.scales is not None:
+                p.scales[b, :, L0[b]:] = SENT_S
+    win_k = C.CachePlanes.alloc("f16", B, Hkv, W, D)
+    win_v = C.CachePlanes.alloc("f16", B, Hkv, W, D)
+    Lq, Lw = list(L0), [0] * B
+    q_all = synth.normal_f16((steps, B, Hkv * G, D), 2403, dev)
+    for i in range(steps):
+        # the new token of sequence b is token Lq[b] + Lw[b]
+        tok = [Lq[b] + Lw[b] for b in range(B)]
+        k_new = torch.stack([k_all[b, :, tok[b]] for b in range(B)]).unsqueeze(1).contiguous()
+        v_new = torch.stack([v_all[b, :, tok[b]] for b in range(B)]).unsqueeze(1).contiguous()
+        pos = torch.tensor(Lw, dtype=torch.int32, device=dev)
+        C.append(win_k, win_v, k_new, v_new, pos, max(Lw) + 1)
+        Lw = [x + 1 for x in Lw]
+        q = q_all[i].contiguous()
+        out, lse = attend_mixed((tail_k, tail_v), (win_k, win_v), q, Lq, Lw, 64, 64)
+        # the oracle: tail rows from its own quantiser, window rows the tokens' fp16 values
+        ref, ref_lse = O.attend_regions(
+            to_host_u16(q), [(k_q, v_q, Lq), (k_win_ref(kh, Lq, Lw, W), k_win_ref(vh, Lq, Lw, W), Lw)],
+            Hkv, 1 / math.sqrt(D))
+        assert_close(out, lse, ref, ref_lse, f"step {i} tail {Lq} window {Lw}")
+        full = [b for b in range(B) if Lw[b] == W]
+        if full:
+            counts = torch.tensor([Lw[b] if b in full else 0 for b in range(B)], dtype=torch.int32, device=dev)
+            posq = torch.tensor(Lq, dtype=torch.int32, device=dev)
+            C.quantize_rows(tail_k, tail_v, win_k, win_v, counts, posq, W, max(Lq) + W)
+            for b in full:
+                Lq[b] += W
+                Lw[b] = 0
+            torch.cuda.synchronize()
+            d, s = download_planes(tail_k)
+            for b in range(B):
+                assert np.array_equal(d[b, :, :Lq[b]], k_q[1][b, :, :Lq[b]]), f"tail K bytes after step {i}"
+                assert np.array_equal(s[b, :, :Lq[b]], k_q[2][b, :, :Lq[b]])
+            d, s = download_planes(tail_v)
+            for b in range(B):
+                assert np.array_equal(d[b, :, :Lq[b]], v_q[1][b, :, :Lq[b]]), f"tail V bytes after step {i}"
+                assert np.array_equal(s[b, :, :Lq[b]], v_q[2][b, :, :Lq[b]])
+    assert sum(Lq) > sum(L0), "no eviction happened"
+
+
+def k_win_ref(xh, Lq, Lw, W):
+    """The window as the oracle sees it: fp16 planes of tokens [Lq_b, Lq_b + Lw_b)."""
+    B, Hkv, _, D = xh.shape
+    w = np.zeros((B, Hkv, W, D), np.uint16)
+    for b in range(B):
+        w[b, :, :Lw[b]] = xh[b, :, Lq[b]:Lq[b] + Lw[b]]
+    return oracle_planes("f16", w)
+
+
+@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0")])
+def test_mixed_full_size_64k_tail_and_window(tk, tv):
+    """A layer of the 64k workload split as 63488 quantised tail rows and a
+    2048-row fp16 window, in the launch configuration of the benchmark (split
+    1024 for the tail, 256 for the window); sampled query heads against the
+    oracle restricted to the KV heads they read."""
+    wl = synth.WORKLOADS["stack48_d128_ctx64k"]
+    B, Hkv, D, G = wl.B, wl.Hkv, wl.D, wl.G
+    Lw, Lt = 2048, wl.ctx - 2048
+    dev = "cuda"
+    note(f"mixed full size {tk}/{tv}")
+    tail = fill_pair(tk, tv, synth.normal_f16((B, Hkv, Lt, D), 2501, dev),
+                     synth.normal_f16((B, Hkv, Lt, D), 2502, dev))
+    win = fill_pair("f16", "f16", synth.normal_f16((B, Hkv, Lw, D), 2503, dev),
+                    synth.normal_f16((B, Hkv, Lw, D), 2504, dev))
+    q = synth.normal_f16((B, wl.Hq, D), 2505, dev)
+    out, lse = attend_mixed(tail, win, q, [Lt], [Lw], 1024, 256)
+    for h in (0, 17, 39):
+        g = h // G
+        sub = lambda p: (p[0], np.ascontiguousarray(p[1][:, g:g + 1]), np.ascontiguousarray(p[2][:, g:g + 1]))
+        ref, ref_lse = O.attend_regions(
+            to_host_u16(q[:, h:h + 1]),
+            [(sub(planes_to_oracle(tail[0])), sub(planes_to_oracle(tail[1])), [Lt]),
+             (sub(planes_to_oracle(win[0])), sub(planes_to_oracle(win[1])), [Lw])], 1, 1 / math.sqrt(D))
+        assert_close(out[:, h:h + 1], lse[:, h:h + 1], ref, ref_lse, f"head {h}")

@@ -212,3 +212,65 @@ def test_thread_count_does_not_change_results():
     a = O.attend(q, kc, vc, [L], Hkv, 0.1, nthreads=1)
     b = O.attend(q, kc, vc, [L], Hkv, 0.1, nthreads=7)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------------ regions of a mixed cache
+
+def test_regions_one_region_equals_attend():
+    rng = np.random.default_rng(21)
+    B, Hkv, G, D, C = 2, 2, 3, 64, 50
+    lens = [50, 17]
+    q = rand_f16(rng, (B, Hkv * G, D))
+    kc = make_cache("q8_0", rand_f16(rng, (B, Hkv, C, D)))
+    vc = make_cache("q4_0", rand_f16(rng, (B, Hkv, C, D)))
+    ref, ref_lse = O.attend(q, kc, vc, lens, Hkv, 0.125)
+    got, got_lse = O.attend_regions(q, [(kc, vc, lens)], Hkv, 0.125)
+    assert np.allclose(got, ref, atol=1e-12, rtol=0) and np.allclose(got_lse, ref_lse, atol=1e-12)
+
+
+def test_regions_cutting_one_cache_in_two_changes_nothing():
+    """Rows [0, a) as one region and [a, L) as another give the attention over
+    [0, L) (the regions are a partition of the rows)."""
+    rng = np.random.default_rng(22)
+    B, Hkv, G, D, C = 1, 2, 4, 64, 90
+    L, a = 90, 37
+    q = rand_f16(rng, (B, Hkv * G, D))
+    for tK, tV in [("q8_0", "q4_0"), ("f16", "q8_0")]:
+        kt, vt = rand_f16(rng, (B, Hkv, C, D)), rand_f16(rng, (B, Hkv, C, D))
+        kc, vc = make_cache(tK, kt), make_cache(tV, vt)
+        ref, ref_lse = O.attend(q, kc, vc, [L], Hkv, 0.125)
+        head = lambda c: (c[0], c[1][:, :, :a], c[2][:, :, :a])
+        tail = lambda c: (c[0], np.ascontiguousarray(c[1][:, :, a:]), np.ascontiguousarray(c[2][:, :, a:]))
+        got, got_lse = O.attend_regions(q, [(head(kc), head(vc), [a]), (tail(kc), tail(vc), [L - a])],
+                                        Hkv, 0.125)
+        assert np.allclose(got, ref, atol=1e-12, rtol=0)
+        assert np.allclose(got_lse, ref_lse, atol=1e-12)
+
+
+def test_regions_fp16_window_and_exact_quantised_tail_equal_one_f16_cache():
+    """A q8_0/q4_0 tail holding values the format stores exactly, plus an fp16
+    window: the same attention as one fp16 cache of all the rows."""
+    rng = np.random.default_rng(23)
+    B, Hkv, G, D = 2, 2, 5, 64
+    Lt, Lw = [40, 0], [9, 13]
+    q = rand_f16(rng, (B, Hkv * G, D))
+    kt = identity_values(rng, "q8_0", (B, Hkv, 40, D), -7)
+    vt = identity_values(rng, "q4_0", (B, Hkv, 40, D), -2)
+    kw, vw = rand_f16(rng, (B, Hkv, 13, D)), rand_f16(rng, (B, Hkv, 13, D))
+    got, got_lse = O.attend_regions(q, [(make_cache("q8_0", kt), make_cache("q4_0", vt), Lt),
+                                        (make_cache("f16", kw), make_cache("f16", vw), Lw)], Hkv, 0.125)
+    for b in range(B):
+        k_all = np.concatenate([kt[b:b + 1, :, :Lt[b]], kw[b:b + 1, :, :Lw[b]]], axis=2)
+        v_all = np.concatenate([vt[b:b + 1, :, :Lt[b]], vw[b:b + 1, :, :Lw[b]]], axis=2)
+        ref, ref_lse = O.attend(q[b:b + 1], make_cache("f16", k_all), make_cache("f16", v_all),
+                                [Lt[b] + Lw[b]], Hkv, 0.125)
+        assert np.allclose(got[b:b + 1], ref, atol=1e-12, rtol=0)
+        assert np.allclose(got_lse[b:b + 1], ref_lse, atol=1e-12)
+
+
+def test_regions_all_empty_gives_zero_and_minus_infinity():
+    rng = np.random.default_rng(24)
+    q = rand_f16(rng, (1, 2, 32))
+    kc = make_cache("q4_0", rand_f16(rng, (1, 1, 4, 32)))
+    got, got_lse = O.attend_regions(q, [(kc, kc, [0]), (kc, kc, [0])], 1, 0.2)
+    assert np.all(got == 0) and np.all(np.isneginf(got_lse))
