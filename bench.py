@@ -17,6 +17,16 @@ layers (f16 2*D, q8_0 34*D/32, q4_0 18*D/32 bytes per row).
 
 Prints ONE JSON line.  Steps are captured once in a HIP graph and replayed
 (--no-graph replays eager launches instead).
+
+Two further modes time the wider calls on the same workloads:
+  --queries N  N query tokens per sequence and step (the verify step of
+               speculative decoding): append the N rows, kvq_decode_attn_multi,
+               kvq_combine over N * Hq heads;
+  --window W   a mixed cache: the last W rows of each sequence in an fp16 window,
+               the rest in the arm's types; append the new token to the window,
+               one attention launch per region, kvq_combine_regions.  The
+               eviction of a full window into the tail (kvq_quantize_rows) is
+               timed on its own and reported per layer.
 """
 from __future__ import annotations
 
@@ -76,6 +86,13 @@ def parse():
     p.add_argument("--arms", default=None, help="comma list like q8_0/q4_0,f16/f16 (default: all)")
     p.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
     p.add_argument("--split-tokens", type=int, default=None)
+    p.add_argument("--queries", type=int, default=1,
+                   help="query tokens per sequence and step (> 1: multi-query decode, "
+                        "kvq_decode_attn_multi)")
+    p.add_argument("--window", type=int, default=0,
+                   help="> 0: mixed cache, the last WINDOW rows of each sequence in an fp16 window "
+                        "and the rest in the arm's types (two attention launches and "
+                        "kvq_combine_regions)")
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline (0 disables it)")
@@ -95,7 +112,7 @@ def log(msg):
 class Arm:
     """All device state of one (K type, V type) arm of a workload."""
 
-    def __init__(self, wl, tk, tv, split_tokens, replicas, dev):
+    def __init__(self, wl, tk, tv, split_tokens, replicas, dev, queries=1, window=0):
         import torch
 
         from quantised_kv_long_amd import cache as C
@@ -106,6 +123,10 @@ class Arm:
         cap = max(self.lens)
         B, Hkv, Hq, D = wl.B, wl.Hkv, wl.Hq, wl.D
         self.wl = wl
+        N, W = queries, window
+        self.N, self.W = N, W
+        if W and (N != 1 or min(self.lens) <= W):
+            raise ValueError("a window needs one query token and sequences longer than the window")
         self.layers = []  # per layer: dict of planes and per-step tensors
         zero = torch.zeros(B, dtype=torch.int32, device=dev)
         n_copies = wl.layers * replicas
@@ -113,28 +134,53 @@ class Arm:
             layer = i % wl.layers
             k = synth.normal_f16((B, cap, Hkv, D), synth.seed_for(wl.seed, layer, "k"), dev)
             v = synth.normal_f16((B, cap, Hkv, D), synth.seed_for(wl.seed, layer, "v"), dev)
-            q = synth.normal_f16((B, Hq, D), synth.seed_for(wl.seed, layer, "q"), dev)
+            q = synth.normal_f16((B, N, Hq, D) if N > 1 else (B, Hq, D),
+                                 synth.seed_for(wl.seed, layer, "q"), dev)
             if wl.k_outlier_frac:
                 ch = synth.outlier_channels(D, synth.seed_for(wl.seed, layer, "aux"), wl.k_outlier_frac)
                 k[..., ch] = (k[..., ch].float() * 8).half()
             if wl.needle:
                 p = self.lens[0] // 3
+                q0 = q[:, 0] if N > 1 else q
                 for g in range(Hkv):
-                    k[0, p, g] = synth.needle_row(q[0, g * wl.G], synth.seed_for(wl.seed, g, "aux"))
+                    k[0, p, g] = synth.needle_row(q0[0, g * wl.G], synth.seed_for(wl.seed, g, "aux"))
             kc = C.CachePlanes.alloc(tk, B, Hkv, cap, D, dev)
             vc = C.CachePlanes.alloc(tv, B, Hkv, cap, D, dev)
-            C.append(kc, vc, k[:, :cap - 1].contiguous(), v[:, :cap - 1].contiguous(), zero, cap - 1)
+            entry = dict(kc=kc, vc=vc, q=q)
+            if W:
+                # tail: rows [0, L - W) in the arm's types (capacity L, room for
+                # an eviction); window: rows [0, W - 1) as fp16, the step
+                # writes row W - 1
+                C.append(kc, vc, k[:, :cap - W].contiguous(), v[:, :cap - W].contiguous(), zero, cap - W)
+                kw = C.CachePlanes.alloc("f16", B, Hkv, W, D, dev)
+                vw = C.CachePlanes.alloc("f16", B, Hkv, W, D, dev)
+                C.append(kw, vw, k[:, cap - W:cap - 1].contiguous(), v[:, cap - W:cap - 1].contiguous(),
+                         zero, W - 1)
+                entry.update(kw=kw, vw=vw)
+            else:
+                C.append(kc, vc, k[:, :cap - N].contiguous(), v[:, :cap - N].contiguous(), zero, cap - N)
             del k, v
-            knew = synth.normal_f16((B, 1, Hkv, D), synth.seed_for(wl.seed, layer, "k_new"), dev)
-            vnew = synth.normal_f16((B, 1, Hkv, D), synth.seed_for(wl.seed, layer, "v_new"), dev)
-            self.layers.append(dict(kc=kc, vc=vc, q=q, knew=knew, vnew=vnew))
+            entry["knew"] = synth.normal_f16((B, N, Hkv, D), synth.seed_for(wl.seed, layer, "k_new"), dev)
+            entry["vnew"] = synth.normal_f16((B, N, Hkv, D), synth.seed_for(wl.seed, layer, "v_new"), dev)
+            self.layers.append(entry)
         torch.cuda.synchronize()
-        self.pos = torch.tensor([L - 1 for L in self.lens], dtype=torch.int32, device=dev)
+        if W and len(set(self.lens)) != 1:
+            raise ValueError("the window mode takes sequences of one length")
+        self.pos = torch.tensor([(W if W else L) - N for L in self.lens], dtype=torch.int32, device=dev)
         self.lens_t = torch.tensor(self.lens, dtype=torch.int32, device=dev)
         self.max_len = cap
-        self.part = C.Partials(B, Hq, D, cap, split_tokens, dev)
-        self.out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+        self.part = C.Partials(B, N * Hq, D, cap, split_tokens, dev)
+        self.out = torch.empty((B, N * Hq, D), dtype=torch.float16, device=dev)
         self.stored_bytes_layer = kc.stored_bytes(self.lens) + vc.stored_bytes(self.lens)
+        if W:
+            self.tail_lens = [L - W for L in self.lens]
+            self.tail_lens_t = torch.tensor(self.tail_lens, dtype=torch.int32, device=dev)
+            self.win_lens_t = torch.full((B,), W, dtype=torch.int32, device=dev)
+            self.evict_pos = self.tail_lens_t
+            self.part_w = C.Partials(B, Hq, D, W, min(split_tokens, 256), dev)
+            kw = self.layers[0]["kw"]
+            self.stored_bytes_layer = (kc.stored_bytes(self.tail_lens) + vc.stored_bytes(self.tail_lens) +
+                                       kw.stored_bytes([W] * B) * 2)
         self.stored_bytes_step = self.stored_bytes_layer * wl.layers
         self.replicas = replicas
 
@@ -150,9 +196,46 @@ class Arm:
         scale = 1.0 / math.sqrt(wl.D)
         part = self.part
         self.calls = []
+        N, W, Hq = self.N, self.W, wl.Hq
         for L in self.layers:
             kd, vd = L["kc"].desc(), L["vc"].desc()
             L["descs"] = (kd, vd)  # keep alive
+            if W:
+                kwd, vwd = L["kw"].desc(), L["vw"].desc()
+                L["wdescs"] = (kwd, vwd)
+                pw = self.part_w
+                P = ctypes.c_void_p
+                regions = ((P * 2)(part.o.data_ptr(), pw.o.data_ptr()), (P * 2)(part.lse.data_ptr(), pw.lse.data_ptr()),
+                           (P * 2)(self.tail_lens_t.data_ptr(), self.win_lens_t.data_ptr()),
+                           (ctypes.c_int * 2)(part.split_tokens, pw.split_tokens),
+                           (ctypes.c_int * 2)(part.max_splits, pw.max_splits))
+                L["regions"] = regions
+                self.calls.append(dict(
+                    append=(ctypes.byref(kwd), ctypes.byref(vwd), L["knew"].data_ptr(), L["vnew"].data_ptr(),
+                            self.pos.data_ptr(), wl.B, 1, wl.Hkv, wl.D, W),
+                    decode=(ctypes.byref(kd), ctypes.byref(vd), L["q"].data_ptr(), self.tail_lens_t.data_ptr(),
+                            wl.B, Hq, wl.Hkv, wl.D, scale, self.max_len, part.split_tokens,
+                            part.max_splits, part.o.data_ptr(), part.lse.data_ptr(), vcode),
+                    decode_w=(ctypes.byref(kwd), ctypes.byref(vwd), L["q"].data_ptr(), self.win_lens_t.data_ptr(),
+                              wl.B, Hq, wl.Hkv, wl.D, scale, W, pw.split_tokens, pw.max_splits,
+                              pw.o.data_ptr(), pw.lse.data_ptr(), vcode),
+                    combine=(2, *regions, wl.B, Hq, wl.D, 0, self.out.data_ptr(), None),
+                    evict=(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(kwd), ctypes.byref(vwd),
+                           self.win_lens_t.data_ptr(), self.evict_pos.data_ptr(), wl.B, W, wl.Hkv, wl.D,
+                           self.max_len),
+                ))
+                continue
+            if N > 1:
+                self.calls.append(dict(
+                    append=(ctypes.byref(kd), ctypes.byref(vd), L["knew"].data_ptr(), L["vnew"].data_ptr(),
+                            self.pos.data_ptr(), wl.B, N, wl.Hkv, wl.D, self.max_len),
+                    multi=(ctypes.byref(kd), ctypes.byref(vd), L["q"].data_ptr(), self.lens_t.data_ptr(),
+                           wl.B, N, Hq, wl.Hkv, wl.D, scale, self.max_len, part.split_tokens,
+                           part.max_splits, part.o.data_ptr(), part.lse.data_ptr()),
+                    combine=(part.o.data_ptr(), part.lse.data_ptr(), self.lens_t.data_ptr(), wl.B, N * Hq,
+                             wl.D, part.split_tokens, part.max_splits, 0, self.out.data_ptr(), None),
+                ))
+                continue
             self.calls.append(dict(
                 step=(ctypes.byref(kd), ctypes.byref(vd), L["knew"].data_ptr(), L["vnew"].data_ptr(),
                       L["q"].data_ptr(), self.lens_t.data_ptr(), wl.B, wl.Hq, wl.Hkv, wl.D, scale,
@@ -170,10 +253,28 @@ class Arm:
 
     def step(self, stream, rep=0, mode="step"):
         """One step over all layers of replica `rep`: mode "step" (kvq_decode_step),
-        "three" (append + decode + combine) or "decode" (the attention launch alone)."""
+        "three" (append + decode + combine) or "decode" (the attention launch alone).
+        Multi-query: append the N tokens, kvq_decode_attn_multi, kvq_combine (step and
+        three alike).  Window: append the token to the fp16 window, one attention
+        launch per region, kvq_combine_regions."""
         lib = self.lib
         n = self.wl.layers
         for c in self.calls[rep * n:(rep + 1) * n]:
+            if self.W:
+                if mode != "decode":
+                    assert lib.kvq_quantize_append(*c["append"], stream) == 0
+                assert lib.kvq_decode_attn_variant(*c["decode"], stream) == 0
+                assert lib.kvq_decode_attn_variant(*c["decode_w"], stream) == 0
+                if mode != "decode":
+                    assert lib.kvq_combine_regions(*c["combine"], stream) == 0
+                continue
+            if self.N > 1:
+                if mode != "decode":
+                    assert lib.kvq_quantize_append(*c["append"], stream) == 0
+                assert lib.kvq_decode_attn_multi(*c["multi"], stream) == 0
+                if mode != "decode":
+                    assert lib.kvq_combine(*c["combine"], stream) == 0
+                continue
             if mode == "step":
                 rc = lib.kvq_decode_step(*c["step"], stream)
                 assert rc == 0, rc
@@ -254,6 +355,36 @@ def time_arm(arm, steps, warmup, use_graph, variant):
         torch.cuda.synchronize()
         samples = [a.elapsed_time(b) * 1e3 for a, b in ev]
     return ms, samples
+
+
+def workload_key(name, args):
+    """The workload's name, with the multi-query / window mode appended."""
+    return name + (f"+queries{args.queries}" if args.queries > 1 else "") + \
+        (f"+window{args.window}" if args.window else "")
+
+
+def time_evictions(arm, reps=10):
+    """µs per layer of one eviction of the fp16 window into the tail
+    (kvq_quantize_rows of WINDOW rows), from a graph of every layer's call."""
+    import torch
+
+    lib = arm.lib
+    n = arm.wl.layers
+    stream = torch.cuda.current_stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream().cuda_stream
+        for c in arm.calls[:n]:
+            assert lib.kvq_quantize_rows(*c["evict"], cs) == 0
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * n)
 
 
 def percentile(xs, q):
@@ -386,10 +517,11 @@ def main():
             kvq.kvq_data_row_bytes(tv, wl.D) + kvq.kvq_scale_row_bytes(tv, wl.D))
         reps = args.replicas or max(1, math.ceil(1.0e9 / (per_layer * wl.layers)))
         log(f"arm {tk}/{tv}: building {wl.layers} layer(s) x {reps} replica(s)")
-        arm = Arm(wl, tk, tv, split_tokens, reps, dev)
+        arm = Arm(wl, tk, tv, split_tokens, reps, dev, args.queries, args.window)
         log(f"arm {tk}/{tv}: timing {args.steps} steps")
         ms, samples = time_arm(arm, args.steps, args.warmup, not args.no_graph, args.variant)
         per_launch = {m: ms[m] / wl.layers for m in MODES}
+        evict_us = time_evictions(arm) if args.window else None
         results[f"{tk}/{tv}"] = {
             "us_per_step": round(ms["step"] * 1e3, 2),
             "stored_bytes_per_step": arm.stored_bytes_step,
@@ -401,6 +533,13 @@ def main():
             "decode_only_GBps": round(arm.stored_bytes_layer / (per_launch["decode"] * 1e-3) / 1e9, 1),
             "replicas": reps,
         }
+        if args.queries > 1:
+            results[f"{tk}/{tv}"]["tokens_per_step"] = args.queries
+            results[f"{tk}/{tv}"]["us_per_token_per_layer"] = round(per_launch["step"] * 1e3 / args.queries, 3)
+        if evict_us is not None:
+            # once every WINDOW steps per layer: quantise the window into the tail
+            results[f"{tk}/{tv}"]["eviction_us_per_layer"] = round(evict_us, 3)
+            results[f"{tk}/{tv}"]["eviction_us_per_step_layer_amortised"] = round(evict_us / args.window, 4)
         if samples:
             results[f"{tk}/{tv}"]["single_step_us_p10_p50_p90"] = [
                 round(percentile(samples, q), 2) for q in (0.1, 0.5, 0.9)]
@@ -413,7 +552,7 @@ def main():
 
     h = results[f"{headline[0]}/{headline[1]}"]
     cpu = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and args.queries == 1 and not args.window:
         log("oracle CPU baseline")
         cpu = cpu_baseline(head_arm, args.cpu_seconds)
     ratios = {}
@@ -430,7 +569,7 @@ def main():
                                                 results["q8_0/q4_0"]["us_per_step"], 3)
     dec_us = h["decode_only_us_per_launch"]
     achieved = head_arm.stored_bytes_layer / (dec_us * 1e-6) / 1e9
-    rec = traffic_record(wl.name, headline[0], headline[1])
+    rec = traffic_record(workload_key(wl.name, args), headline[0], headline[1])
     traffic = None
     if rec is not None:
         traffic = round((rec[0] + rec[1]) / (dec_us * 1e-6) / 1e9, 1)
@@ -457,7 +596,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "arm": f"{headline[0]}K/{headline[1]}V",
+        "config": {"workload": workload_key(wl.name, args), "arm": f"{headline[0]}K/{headline[1]}V",
+                   "queries": args.queries, "window": args.window,
                    "layers": wl.layers, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
                    "head_dim": wl.D, "ctx": wl.ctx, "split_tokens": split_tokens,
                    "path": "kvq_decode_step", "graph": not args.no_graph},
