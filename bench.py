@@ -24,9 +24,10 @@ Two further modes time the wider calls on the same workloads:
                kvq_combine over N * Hq heads;
   --window W   a mixed cache: the last W rows of each sequence in an fp16 window,
                the rest in the arm's types; append the new token to the window,
-               one attention launch per region, kvq_combine_regions.  The
-               eviction of a full window into the tail (kvq_quantize_rows) is
-               timed on its own and reported per layer.
+               attention over both regions in one launch (kvq_decode_attn_mixed),
+               kvq_combine_regions.  The eviction of a full window into the
+               tail (kvq_quantize_rows) is timed on its own and reported per
+               layer.
 """
 from __future__ import annotations
 
@@ -91,7 +92,7 @@ def parse():
                         "kvq_decode_attn_multi)")
     p.add_argument("--window", type=int, default=0,
                    help="> 0: mixed cache, the last WINDOW rows of each sequence in an fp16 window "
-                        "and the rest in the arm's types (two attention launches and "
+                        "and the rest in the arm's types (kvq_decode_attn_mixed and "
                         "kvq_combine_regions)")
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -112,9 +113,10 @@ def log(msg):
 class Arm:
     """All device state of one (K type, V type) arm of a workload."""
 
-    def __init__(self, wl, tk, tv, split_tokens, replicas, dev, queries=1, window=0):
+    def __init__(self, wl, tk, tv, split_tokens, replicas, dev, queries=1, window=0, win_split_tokens=None):
         import torch
 
+        from quantised_kv_long_amd import _lib
         from quantised_kv_long_amd import cache as C
         from quantised_kv_long_amd import synth
 
@@ -169,6 +171,13 @@ class Arm:
         self.pos = torch.tensor([(W if W else L) - N for L in self.lens], dtype=torch.int32, device=dev)
         self.lens_t = torch.tensor(self.lens, dtype=torch.int32, device=dev)
         self.max_len = cap
+        if W and split_tokens is None:
+            # one round of resident workgroups covers both regions
+            row_t = sum(_lib.kvq_data_row_bytes(t, D) + _lib.kvq_scale_row_bytes(t, D) for t in (tk, tv))
+            split_tokens, win_split_tokens = C.mixed_splits(cap - W, W, row_t, 4 * D, B, Hkv, D)
+        elif W and win_split_tokens is None:
+            win_split_tokens = split_tokens
+        self.split_tokens, self.win_split_tokens = split_tokens, win_split_tokens
         self.part = C.Partials(B, N * Hq, D, cap, split_tokens, dev)
         self.out = torch.empty((B, N * Hq, D), dtype=torch.float16, device=dev)
         self.stored_bytes_layer = kc.stored_bytes(self.lens) + vc.stored_bytes(self.lens)
@@ -177,7 +186,7 @@ class Arm:
             self.tail_lens_t = torch.tensor(self.tail_lens, dtype=torch.int32, device=dev)
             self.win_lens_t = torch.full((B,), W, dtype=torch.int32, device=dev)
             self.evict_pos = self.tail_lens_t
-            self.part_w = C.Partials(B, Hq, D, W, min(split_tokens, 256), dev)
+            self.part_w = C.Partials(B, Hq, D, W, win_split_tokens, dev)
             kw = self.layers[0]["kw"]
             self.stored_bytes_layer = (kc.stored_bytes(self.tail_lens) + vc.stored_bytes(self.tail_lens) +
                                        kw.stored_bytes([W] * B) * 2)
@@ -214,11 +223,22 @@ class Arm:
                     append=(ctypes.byref(kwd), ctypes.byref(vwd), L["knew"].data_ptr(), L["vnew"].data_ptr(),
                             self.pos.data_ptr(), wl.B, 1, wl.Hkv, wl.D, W),
                     decode=(ctypes.byref(kd), ctypes.byref(vd), L["q"].data_ptr(), self.tail_lens_t.data_ptr(),
-                            wl.B, Hq, wl.Hkv, wl.D, scale, self.max_len, part.split_tokens,
+                            wl.B, Hq, wl.Hkv, wl.D, scale, max(self.tail_lens), part.split_tokens,
                             part.max_splits, part.o.data_ptr(), part.lse.data_ptr(), vcode),
                     decode_w=(ctypes.byref(kwd), ctypes.byref(vwd), L["q"].data_ptr(), self.win_lens_t.data_ptr(),
                               wl.B, Hq, wl.Hkv, wl.D, scale, W, pw.split_tokens, pw.max_splits,
                               pw.o.data_ptr(), pw.lse.data_ptr(), vcode),
+                    step_mixed=(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(kwd), ctypes.byref(vwd),
+                                L["knew"].data_ptr(), L["vnew"].data_ptr(), L["q"].data_ptr(),
+                                self.tail_lens_t.data_ptr(), self.win_lens_t.data_ptr(), wl.B, Hq, wl.Hkv,
+                                wl.D, scale, max(self.tail_lens), part.split_tokens, part.max_splits,
+                                part.o.data_ptr(), part.lse.data_ptr(), W, pw.split_tokens, pw.max_splits,
+                                pw.o.data_ptr(), pw.lse.data_ptr(), 0, self.out.data_ptr(), None),
+                    mixed=(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(kwd), ctypes.byref(vwd),
+                           L["q"].data_ptr(), self.tail_lens_t.data_ptr(), self.win_lens_t.data_ptr(),
+                           wl.B, Hq, wl.Hkv, wl.D, scale, max(self.tail_lens), part.split_tokens, part.max_splits,
+                           part.o.data_ptr(), part.lse.data_ptr(), W, pw.split_tokens, pw.max_splits,
+                           pw.o.data_ptr(), pw.lse.data_ptr()),
                     combine=(2, *regions, wl.B, Hq, wl.D, 0, self.out.data_ptr(), None),
                     evict=(ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(kwd), ctypes.byref(vwd),
                            self.win_lens_t.data_ptr(), self.evict_pos.data_ptr(), wl.B, W, wl.Hkv, wl.D,
@@ -250,21 +270,30 @@ class Arm:
                          wl.D, part.split_tokens, part.max_splits, 0, self.out.data_ptr(), None),
             ))
         self.lib = lib
+        self.one_call = variant == "auto"
 
     def step(self, stream, rep=0, mode="step"):
         """One step over all layers of replica `rep`: mode "step" (kvq_decode_step),
         "three" (append + decode + combine) or "decode" (the attention launch alone).
         Multi-query: append the N tokens, kvq_decode_attn_multi, kvq_combine (step and
-        three alike).  Window: append the token to the fp16 window, one attention
-        launch per region, kvq_combine_regions."""
+        three alike).  Window: "step" is kvq_decode_step_mixed (the attention
+        kernel writes the token into the fp16 window); "three" appends the token,
+        runs kvq_decode_attn_mixed and kvq_combine_regions.  With a forced
+        variant both run one kvq_decode_attn_variant per region instead."""
         lib = self.lib
         n = self.wl.layers
         for c in self.calls[rep * n:(rep + 1) * n]:
             if self.W:
+                if mode == "step" and self.one_call:
+                    assert lib.kvq_decode_step_mixed(*c["step_mixed"], stream) == 0
+                    continue
                 if mode != "decode":
                     assert lib.kvq_quantize_append(*c["append"], stream) == 0
-                assert lib.kvq_decode_attn_variant(*c["decode"], stream) == 0
-                assert lib.kvq_decode_attn_variant(*c["decode_w"], stream) == 0
+                if self.one_call:
+                    assert lib.kvq_decode_attn_mixed(*c["mixed"], stream) == 0
+                else:
+                    assert lib.kvq_decode_attn_variant(*c["decode"], stream) == 0
+                    assert lib.kvq_decode_attn_variant(*c["decode_w"], stream) == 0
                 if mode != "decode":
                     assert lib.kvq_combine_regions(*c["combine"], stream) == 0
                 continue
@@ -355,6 +384,16 @@ def time_arm(arm, steps, warmup, use_graph, variant):
         torch.cuda.synchronize()
         samples = [a.elapsed_time(b) * 1e3 for a, b in ev]
     return ms, samples
+
+
+def step_path(args):
+    """The entry points one step of one layer calls."""
+    if args.window:
+        return ("kvq_decode_step_mixed" if args.variant == "auto" else
+                "kvq_quantize_append + kvq_decode_attn_variant x2 + kvq_combine_regions")
+    if args.queries > 1:
+        return "kvq_quantize_append + kvq_decode_attn_multi + kvq_combine"
+    return "kvq_decode_step"
 
 
 def workload_key(name, args):
@@ -517,7 +556,8 @@ def main():
             kvq.kvq_data_row_bytes(tv, wl.D) + kvq.kvq_scale_row_bytes(tv, wl.D))
         reps = args.replicas or max(1, math.ceil(1.0e9 / (per_layer * wl.layers)))
         log(f"arm {tk}/{tv}: building {wl.layers} layer(s) x {reps} replica(s)")
-        arm = Arm(wl, tk, tv, split_tokens, reps, dev, args.queries, args.window)
+        arm = Arm(wl, tk, tv, args.split_tokens if args.window else split_tokens, reps, dev, args.queries,
+                  args.window)
         log(f"arm {tk}/{tv}: timing {args.steps} steps")
         ms, samples = time_arm(arm, args.steps, args.warmup, not args.no_graph, args.variant)
         per_launch = {m: ms[m] / wl.layers for m in MODES}
@@ -530,6 +570,8 @@ def main():
             "step_us_per_layer": round(per_launch["step"] * 1e3, 3),
             "three_call_us_per_step": round(ms["three"] * 1e3, 2),
             "decode_only_us_per_launch": round(per_launch["decode"] * 1e3, 3),
+            "split_tokens": arm.split_tokens,
+            **({"window_split_tokens": arm.win_split_tokens} if args.window else {}),
             "decode_only_GBps": round(arm.stored_bytes_layer / (per_launch["decode"] * 1e-3) / 1e9, 1),
             "replicas": reps,
         }
@@ -579,7 +621,8 @@ def main():
     log(f"probe read bandwidth {probe} GB/s")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "decode_mfma_kernel", "avg_launch_us": dec_us,
+                "kernel": ("decode_mfma_dual_kernel" if args.window and args.variant == "auto"
+                           else "decode_mfma_kernel"), "avg_launch_us": dec_us,
                 "algorithmic_bytes_per_launch": head_arm.stored_bytes_layer,
                 "probe_read_GBps": probe,
                 "frac_of_probe": round(achieved / probe, 4) if probe else None}
@@ -599,8 +642,8 @@ def main():
         "config": {"workload": workload_key(wl.name, args), "arm": f"{headline[0]}K/{headline[1]}V",
                    "queries": args.queries, "window": args.window,
                    "layers": wl.layers, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
-                   "head_dim": wl.D, "ctx": wl.ctx, "split_tokens": split_tokens,
-                   "path": "kvq_decode_step", "graph": not args.no_graph},
+                   "head_dim": wl.D, "ctx": wl.ctx, "split_tokens": head_arm.split_tokens,
+                   "path": step_path(args), "graph": not args.no_graph},
         # the dominant kernel is the split-KV attention kernel: its average
         # launch duration is measured with HIP events around graph replays of
         # that launch alone (one per layer, back to back)

@@ -204,11 +204,15 @@ int kvq_quantize_rows(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cac
  * Sequence b attends over its rows [0, seq_lens[b]) with no mask.  The rows
  * are cut into splits of split_tokens rows; split s of sequence b covers rows
  * [s*split_tokens, min((s+1)*split_tokens, L_b)).  For every (b, h, s) with
- * s < max_splits the call writes, in fp32,
+ * s < ceil(max_seq_len / split_tokens) the call writes, in fp32,
  *   part_lse[b][h][s]   = ln sum_t exp(score_t)   (-inf for an empty split)
  *   part_o[b][h][s][:]  = sum_t exp(score_t - part_lse) * v_t   (0 if empty)
  * with score_t = softmax_scale * sum_d q[b][h][d] * k_t[d] and k_t, v_t the
- * dequantised rows (code * scale, exactly).
+ * dequantised rows (code * scale, exactly).  Splits from there up to
+ * max_splits are left as they are: every length is at most max_seq_len, so
+ * no merge reads them, and the launch does not spend workgroups on them
+ * (partials sized for the cache's capacity cost nothing while the sequences
+ * are shorter).
  *
  *   q              : device, [B][Hq][D] binary16.
  *   seq_lens       : device, [B] int32, 0 <= L_b <= max_seq_len <= capacity
@@ -287,6 +291,60 @@ int kvq_decode_attn_variant(const kvq_plane_desc* k_cache, const kvq_plane_desc*
 int kvq_combine(const float* part_o, const float* part_lse, const int32_t* seq_lens, int B,
                 int Hq, int D, int split_tokens, int max_splits, int out_type, void* out,
                 float* lse_out, void* stream);
+
+/*
+ * Split-KV attention over both regions of a mixed cache (HAL #582 section 5
+ * P2: a quantised tail and an fp16 window of recent tokens) in one call.
+ * Equivalent to kvq_decode_attn over the tail (k_tail / v_tail, tail_lens,
+ * tail_* splits and partials) followed by kvq_decode_attn over the window
+ * (k_win / v_win, fp16, win_lens, win_* splits and partials) with the same q,
+ * and bit-identical to it.  Where the matrix-core kernel covers the shape
+ * (tail K and V of q8_0 / q4_0, D = 128, 256 or 512) both regions run in one
+ * launch: a small window then costs its bytes, not a second launch's start
+ * and end.  Otherwise the two launches are made.  The partials merge with
+ * kvq_combine_regions.
+ *
+ *   k_win, v_win : fp16 planes (KVQ_ERR_TYPE otherwise).
+ *   Each region's lengths, max_len, splits and partials follow the rules of
+ *   kvq_decode_attn; a region's lengths may be 0.
+ */
+int kvq_decode_attn_mixed(const kvq_plane_desc* k_tail, const kvq_plane_desc* v_tail,
+                          const kvq_plane_desc* k_win, const kvq_plane_desc* v_win, const void* q,
+                          const int32_t* tail_lens, const int32_t* win_lens, int B, int Hq, int Hkv,
+                          int D, float softmax_scale, int tail_max_len, int tail_split_tokens,
+                          int tail_max_splits, float* tail_part_o, float* tail_part_lse,
+                          int win_max_len, int win_split_tokens, int win_max_splits,
+                          float* win_part_o, float* win_part_lse, void* stream);
+
+/*
+ * One decode step over a mixed cache (HAL #582 section 5 P2: a quantised tail
+ * and an fp16 window that receives the new token): the new row is written into
+ * the window at row win_lens[b] - 1, attention runs over both regions as in
+ * kvq_decode_attn_mixed, and the partials are merged as by
+ * kvq_combine_regions with n_regions = 2 (tail, then window).  Results equal
+ * kvq_quantize_append of the row into the window followed by those two calls,
+ * bit for bit.  Where the matrix-core kernel covers the shape this is two
+ * launches: the window's attention workgroup that holds row win_lens[b] - 1
+ * writes it before reading it, then the merge runs.
+ *
+ *   k_new, v_new   : device, [B][Hkv][D] binary16: the new token's K and V.
+ *   win_lens       : lengths of the window *including* the new token,
+ *                    1 <= win_lens[b] <= win_max_len (a sequence with
+ *                    win_lens[b] = 0 gets no new row).
+ *   tail_lens      : 0 <= tail_lens[b] <= tail_max_len.
+ *   out_type, out, lse_out : as for kvq_combine.
+ *   The remaining arguments are those of kvq_decode_attn_mixed.
+ * Moving full windows into the tail (eviction) is kvq_quantize_rows, called
+ * by the owner of the cache between steps.
+ */
+int kvq_decode_step_mixed(const kvq_plane_desc* k_tail, const kvq_plane_desc* v_tail,
+                          const kvq_plane_desc* k_win, const kvq_plane_desc* v_win, const void* k_new,
+                          const void* v_new, const void* q, const int32_t* tail_lens,
+                          const int32_t* win_lens, int B, int Hq, int Hkv, int D, float softmax_scale,
+                          int tail_max_len, int tail_split_tokens, int tail_max_splits,
+                          float* tail_part_o, float* tail_part_lse, int win_max_len,
+                          int win_split_tokens, int win_max_splits, float* win_part_o,
+                          float* win_part_lse, int out_type, void* out, float* lse_out, void* stream);
 
 /*
  * Exact log-sum-exp merge of the partials of several regions (HAL #582

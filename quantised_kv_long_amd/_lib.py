@@ -85,6 +85,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         ctypes.POINTER(i32), ctypes.POINTER(i32), i32, i32, i32, i32,
                                         P, P, P]
     lib.kvq_combine_regions.restype = i32
+    lib.kvq_decode_attn_mixed.argtypes = [DP, DP, DP, DP, P, P, P, i32, i32, i32, i32, f32, i32, i32,
+                                          i32, P, P, i32, i32, i32, P, P, P]
+    lib.kvq_decode_attn_mixed.restype = i32
+    lib.kvq_decode_step_mixed.argtypes = [DP, DP, DP, DP, P, P, P, P, P, i32, i32, i32, i32, f32, i32,
+                                          i32, i32, P, P, i32, i32, i32, P, P, i32, P, P, P]
+    lib.kvq_decode_step_mixed.restype = i32
     lib.kvq_decode_attn_multi.argtypes = [DP, DP, P, P, i32, i32, i32, i32, i32, f32, i32, i32, i32,
                                           P, P, P]
     lib.kvq_decode_attn_multi.restype = i32
@@ -195,6 +201,39 @@ def kvq_decode_attn(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, q, seq_len
                                 split_tokens, max_splits, _ptr(part_o), _ptr(part_lse),
                                 _stream(stream))
     return _check("kvq_decode_attn", rc)
+
+
+def kvq_decode_attn_mixed(k_tail: kvq_plane_desc, v_tail: kvq_plane_desc, k_win: kvq_plane_desc,
+                          v_win: kvq_plane_desc, q, tail_lens, win_lens, B: int, Hq: int, Hkv: int,
+                          D: int, softmax_scale: float, tail_max_len: int, tail_split_tokens: int,
+                          tail_max_splits: int, tail_part_o, tail_part_lse, win_max_len: int,
+                          win_split_tokens: int, win_max_splits: int, win_part_o, win_part_lse,
+                          stream=None) -> int:
+    rc = load().kvq_decode_attn_mixed(ctypes.byref(k_tail), ctypes.byref(v_tail), ctypes.byref(k_win),
+                                      ctypes.byref(v_win), _ptr(q), _ptr(tail_lens), _ptr(win_lens), B,
+                                      Hq, Hkv, D, float(softmax_scale), tail_max_len, tail_split_tokens,
+                                      tail_max_splits, _ptr(tail_part_o), _ptr(tail_part_lse),
+                                      win_max_len, win_split_tokens, win_max_splits, _ptr(win_part_o),
+                                      _ptr(win_part_lse), _stream(stream))
+    return _check("kvq_decode_attn_mixed", rc)
+
+
+def kvq_decode_step_mixed(k_tail: kvq_plane_desc, v_tail: kvq_plane_desc, k_win: kvq_plane_desc,
+                          v_win: kvq_plane_desc, k_new, v_new, q, tail_lens, win_lens, B: int, Hq: int,
+                          Hkv: int, D: int, softmax_scale: float, tail_max_len: int,
+                          tail_split_tokens: int, tail_max_splits: int, tail_part_o, tail_part_lse,
+                          win_max_len: int, win_split_tokens: int, win_max_splits: int, win_part_o,
+                          win_part_lse, out_type, out, lse_out=None, stream=None) -> int:
+    ot = OUT_F32 if out_type in ("f32", OUT_F32) else _tcode(out_type)
+    rc = load().kvq_decode_step_mixed(ctypes.byref(k_tail), ctypes.byref(v_tail), ctypes.byref(k_win),
+                                      ctypes.byref(v_win), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                      _ptr(tail_lens), _ptr(win_lens), B, Hq, Hkv, D,
+                                      float(softmax_scale), tail_max_len, tail_split_tokens,
+                                      tail_max_splits, _ptr(tail_part_o), _ptr(tail_part_lse),
+                                      win_max_len, win_split_tokens, win_max_splits, _ptr(win_part_o),
+                                      _ptr(win_part_lse), ot, _ptr(out), _ptr(lse_out),
+                                      _stream(stream))
+    return _check("kvq_decode_step_mixed", rc)
 
 
 def kvq_decode_attn_multi(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, q, seq_lens, B: int,

@@ -79,6 +79,71 @@ def quantize_rows(kc: CachePlanes, vc: CachePlanes, k_src: CachePlanes, v_src: C
                                   kc.B, max_rows, kc.Hkv, kc.D, max_end, stream)
 
 
+def decode_mixed(tail, win, q: torch.Tensor, tail_lens: torch.Tensor, win_lens: torch.Tensor,
+                 tail_part: "Partials", win_part: "Partials", softmax_scale: float, stream=None,
+                 tail_max_len=None, win_max_len=None):
+    """kvq_decode_attn_mixed: ``tail`` and ``win`` are (K, V) CachePlanes pairs
+    (the window fp16); max lengths default to the caches' capacities."""
+    B, Hq, D = q.shape
+    kt, vt = tail
+    kw, vw = win
+    return _lib.kvq_decode_attn_mixed(kt.desc(), vt.desc(), kw.desc(), vw.desc(), q, tail_lens, win_lens,
+                                      B, Hq, kt.Hkv, D, softmax_scale, tail_max_len or kt.capacity,
+                                      tail_part.split_tokens, tail_part.max_splits, tail_part.o,
+                                      tail_part.lse, win_max_len or kw.capacity,
+                                      win_part.split_tokens, win_part.max_splits, win_part.o, win_part.lse,
+                                      stream)
+
+
+def decode_step_mixed(tail, win, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                      tail_lens: torch.Tensor, win_lens: torch.Tensor, tail_part: "Partials",
+                      win_part: "Partials", softmax_scale: float, out: torch.Tensor, lse_out=None,
+                      stream=None, tail_max_len=None, win_max_len=None):
+    """kvq_decode_step_mixed: the new row (B, Hkv, D) fp16 into the fp16 window
+    at row win_lens[b] - 1, attention over both regions, the region merge into
+    ``out`` (B, Hq, D)."""
+    B, Hq, D = q.shape
+    kt, vt = tail
+    kw, vw = win
+    ot = "f16" if out.dtype == torch.float16 else "f32"
+    return _lib.kvq_decode_step_mixed(kt.desc(), vt.desc(), kw.desc(), vw.desc(), k_new, v_new, q,
+                                      tail_lens, win_lens, B, Hq, kt.Hkv, D, softmax_scale,
+                                      tail_max_len or kt.capacity, tail_part.split_tokens,
+                                      tail_part.max_splits, tail_part.o, tail_part.lse,
+                                      win_max_len or kw.capacity, win_part.split_tokens,
+                                      win_part.max_splits, win_part.o, win_part.lse, ot, out, lse_out,
+                                      stream)
+
+
+# Workgroups of the matrix-core decode kernel resident at once on the 256
+# compute units: two per CU where a wave fits in 256 registers (two waves per
+# SIMD), one at head_dim 256 (one wave per SIMD).
+def resident_workgroups(D: int, cus: int = 256) -> int:
+    return cus * (1 if D == 256 else 2)
+
+
+def mixed_splits(tail_len: int, win_len: int, tail_row_bytes: int, win_row_bytes: int, B: int,
+                 Hkv: int, D: int, granule: int = _lib.SPLIT_GRANULE) -> tuple[int, int]:
+    """Split sizes (tail, window) for kvq_decode_attn_mixed: the resident
+    workgroups are shared between the two regions so that one round of
+    workgroups covers both, and the split whose workgroup reads the most bytes
+    is as small as it can be.  Row bytes are the K plus V bytes of one row of
+    one KV head (codes and scales)."""
+    def cdiv(a, b):
+        return -(-a // b)
+
+    units = max(2, resident_workgroups(D) // max(1, B * Hkv))
+    best = None
+    for n_w in range(1, units):
+        n_t = units - n_w
+        st = cdiv(cdiv(max(1, tail_len), n_t), granule) * granule
+        sw = cdiv(cdiv(max(1, win_len), n_w), granule) * granule
+        cost = (max(st * tail_row_bytes, sw * win_row_bytes), cdiv(tail_len, st) + cdiv(win_len, sw))
+        if best is None or cost < best[0]:
+            best = (cost, st, sw)
+    return best[1], best[2]
+
+
 def combine_regions(parts, seq_lens, out: torch.Tensor, lse_out=None, stream=None):
     """kvq_combine_regions over the Partials of several regions (one seq_lens
     tensor per region) into ``out`` (B, Hq, D) fp16 or fp32."""

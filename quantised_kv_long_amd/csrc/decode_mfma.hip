@@ -195,20 +195,21 @@ __host__ __device__ constexpr size_t merge_lds_bytes(int nc)
 
 // 128-column slices are built for two waves per SIMD (at most 256
 // registers); head_dim 256 needs more and runs one
+// The work of one workgroup: split s of (sequence blockIdx.z, KV head
+// blockIdx.y).  LDS: lds_a, lds_cap bytes (at least WAVES * BUF: one buffer
+// per wave, the V rows of the current tile, then the K and V scale tiles
+// transposed to [block][row]; also the merge area when that fits), lds_sx
+// (the partial-score exchange of a 512-wide head) and lds_merge_dyn (the
+// merge area otherwise).
 // MQ: several query tokens per sequence (a.nq > 1); a separate instance, so
 // that the single-token kernels carry none of its per-column index arithmetic
 template <int TK, int TV, int D, bool MQ>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
-decode_mfma_kernel(DecodeArgs a)
+__device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint8_t* const lds_a,
+                                          const size_t lds_cap, float* const lds_sx,
+                                          uint8_t* const lds_merge_dyn)
 {
     using C = Cfg<TK, TV, D>;
-    // One LDS buffer per wave: the V rows of the current tile, then the K and
-    // V scale tiles, transposed to [block][row].
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[WAVES * C::BUF];
-    __shared__ __attribute__((aligned(16))) float lds_sx[C::SX_FLOATS];
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
-
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, lq = lane >> 4;       // column / lane row of the 16x16 layouts
     const int G = a.G;
@@ -754,7 +755,7 @@ decode_mfma_kernel(DecodeArgs a)
     //      every output column is a four-term weighted sum.
     const float l_head = xsum4(l_part);
     __syncthreads();
-    uint8_t* marea = merge_lds_bytes<TK, TV, D>(NC) <= sizeof(lds_a) ? lds_a : lds_merge_dyn;
+    uint8_t* marea = merge_lds_bytes<TK, TV, D>(NC) <= lds_cap ? lds_a : lds_merge_dyn;
     float* mw = reinterpret_cast<float*>(marea);          // [WAVES][16]   running max
     float* lw = mw + WAVES * 16;                          // [WAVES][16]   running sum
     float* fw = lw + WAVES * 16;                          // [WAVES][16]   merge weights
@@ -834,6 +835,47 @@ decode_mfma_kernel(DecodeArgs a)
     }
 }
 
+template <int TK, int TV, int D, bool MQ>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
+decode_mfma_kernel(DecodeArgs a)
+{
+    using C = Cfg<TK, TV, D>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[WAVES * C::BUF];
+    __shared__ __attribute__((aligned(16))) float lds_sx[C::SX_FLOATS];
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
+    decode_wg<TK, TV, D, MQ>(a, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn);
+}
+
+// The two regions of a mixed cache in one launch (HAL #582 section 5 P2): the
+// workgroups of the tail's splits [0, grid_splits(t)) run over the tail (types
+// TK / TV), the others over the fp16 window w; each region writes its own
+// partials.
+// One launch instead of two saves the second launch's start and end, which
+// for a window of a few thousand rows cost more than its bytes.
+template <int TK, int TV, int D>
+struct DualCfg {
+    using T = Cfg<TK, TV, D>;
+    using F = Cfg<T_F16, T_F16, D>;
+    static constexpr int BUF = WAVES * (T::BUF > F::BUF ? T::BUF : F::BUF);
+    static constexpr int SX = T::SX_FLOATS > F::SX_FLOATS ? T::SX_FLOATS : F::SX_FLOATS;
+    static constexpr bool VALID = T::VALID && F::VALID;
+};
+
+template <int TK, int TV, int D>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
+decode_mfma_dual_kernel(DecodeArgs t, DecodeArgs w)
+{
+    using DC = DualCfg<TK, TV, D>;
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[DC::BUF];
+    __shared__ __attribute__((aligned(16))) float lds_sx[DC::SX];
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
+    const int ts = grid_splits(t);  // the first ts workgroups of each row take the tail
+    if ((int)blockIdx.x < ts)
+        decode_wg<TK, TV, D, false>(t, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn);
+    else
+        decode_wg<T_F16, T_F16, D, false>(w, blockIdx.x - ts, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn);
+}
+
 template <int TK, int TV, int D>
 constexpr bool cfg_valid() { return Cfg<TK, TV, D>::VALID; }
 
@@ -857,7 +899,7 @@ size_t lds_bytes(int nc)
 template <int TK, int TV, int D, bool MQ>
 hipError_t launch4(const DecodeArgs& a, hipStream_t s)
 {
-    dim3 grid(a.max_splits, a.Hkv, a.B);
+    dim3 grid(grid_splits(a), a.Hkv, a.B);
     const int nc = a.nq * a.G;
     const size_t dyn = dyn_lds_bytes<TK, TV, D>(nc);
     if (lds_bytes<TK, TV, D>(nc) > 64 * 1024) {
@@ -878,6 +920,67 @@ hipError_t launch3(const DecodeArgs& a, hipStream_t s)
     } else {
         return a.nq > 1 ? launch4<TK, TV, D, true>(a, s) : launch4<TK, TV, D, false>(a, s);
     }
+}
+
+template <int TK, int TV, int D>
+size_t dual_dyn_bytes(int G)
+{
+    using DC = DualCfg<TK, TV, D>;
+    const size_t mt = merge_lds_bytes<TK, TV, D>(G), mf = merge_lds_bytes<T_F16, T_F16, D>(G);
+    const size_t m = mt > mf ? mt : mf;
+    return m <= (size_t)DC::BUF ? 0 : m;
+}
+
+template <int TK, int TV, int D>
+bool dual_supports3(const DecodeArgs& t)
+{
+    using DC = DualCfg<TK, TV, D>;
+    if constexpr (!DC::VALID) {
+        return false;
+    } else {
+        return (size_t)DC::BUF + sizeof(float) * DC::SX + dual_dyn_bytes<TK, TV, D>(t.G) <= 160 * 1024;
+    }
+}
+
+template <int TK, int TV, int D>
+hipError_t launch_dual3(const DecodeArgs& t, const DecodeArgs& w, hipStream_t s)
+{
+    using DC = DualCfg<TK, TV, D>;
+    if constexpr (!DC::VALID) {
+        return hipErrorInvalidConfiguration;
+    } else {
+        const size_t dyn = dual_dyn_bytes<TK, TV, D>(t.G);
+        if ((size_t)DC::BUF + sizeof(float) * DC::SX + dyn > 64 * 1024) {
+            const hipError_t e = hipFuncSetAttribute(
+                reinterpret_cast<const void*>(&decode_mfma_dual_kernel<TK, TV, D>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+            if (e != hipSuccess) return e;
+        }
+        dim3 grid(grid_splits(t) + grid_splits(w), t.Hkv, t.B);
+        hipLaunchKernelGGL((decode_mfma_dual_kernel<TK, TV, D>), grid, dim3(NT), dyn, s, t, w);
+        return hipGetLastError();
+    }
+}
+
+// tail types: the quantised pairs
+template <int D>
+bool dual_supports2(const DecodeArgs& t)
+{
+    if (t.tk == T_Q8 && t.tv == T_Q8) return dual_supports3<T_Q8, T_Q8, D>(t);
+    if (t.tk == T_Q8 && t.tv == T_Q4) return dual_supports3<T_Q8, T_Q4, D>(t);
+    if (t.tk == T_Q4 && t.tv == T_Q8) return dual_supports3<T_Q4, T_Q8, D>(t);
+    if (t.tk == T_Q4 && t.tv == T_Q4) return dual_supports3<T_Q4, T_Q4, D>(t);
+    return false;
+}
+
+template <int D>
+hipError_t launch_dual2(const DecodeArgs& t, const DecodeArgs& w, hipStream_t s)
+{
+    if (t.tk == T_Q8 && t.tv == T_Q8) return launch_dual3<T_Q8, T_Q8, D>(t, w, s);
+    if (t.tk == T_Q8 && t.tv == T_Q4) return launch_dual3<T_Q8, T_Q4, D>(t, w, s);
+    if (t.tk == T_Q4 && t.tv == T_Q8) return launch_dual3<T_Q4, T_Q8, D>(t, w, s);
+    if (t.tk == T_Q4 && t.tv == T_Q4) return launch_dual3<T_Q4, T_Q4, D>(t, w, s);
+    return hipErrorInvalidConfiguration;
 }
 
 template <int TK, int TV>
@@ -936,6 +1039,30 @@ bool decode_mfma_supports(const DecodeArgs& a)
     case T_F16: return supports1<T_F16>(a);
     case T_Q8: return supports1<T_Q8>(a);
     default: return supports1<T_Q4>(a);
+    }
+}
+
+bool decode_mfma_dual_supports(const DecodeArgs& t, const DecodeArgs& w)
+{
+    if (w.tk != T_F16 || w.tv != T_F16 || t.nq != 1 || w.nq != 1) return false;
+    if (w.D != t.D || w.B != t.B || w.Hkv != t.Hkv || w.Hq != t.Hq) return false;
+    if (!decode_mfma_supports(t) || !decode_mfma_supports(w)) return false;
+    if ((int64_t)t.max_splits + w.max_splits > 0x7fffffffLL) return false;
+    switch (t.D) {
+    case 128: return dual_supports2<128>(t);
+    case 256: return dual_supports2<256>(t);
+    case 512: return dual_supports2<512>(t);
+    default: return false;
+    }
+}
+
+hipError_t launch_decode_mfma_dual(const DecodeArgs& t, const DecodeArgs& w, hipStream_t s)
+{
+    switch (t.D) {
+    case 128: return launch_dual2<128>(t, w, s);
+    case 256: return launch_dual2<256>(t, w, s);
+    case 512: return launch_dual2<512>(t, w, s);
+    default: return hipErrorInvalidConfiguration;
     }
 }
 

@@ -193,7 +193,7 @@ template <int TK, int TV>
 hipError_t launch_tv(const DecodeArgs& a, hipStream_t s)
 {
     const int NC = a.D >> 3, NG = NT / NC;
-    dim3 grid(a.max_splits, a.Hkv, a.B);
+    dim3 grid(grid_splits(a), a.Hkv, a.B);
     if (a.G <= 8) {
         const size_t lds = sizeof(float) * (8 * a.D + 8 * TILE + 3 * 8 + NG * a.D);
         hipLaunchKernelGGL((decode_valu_kernel<TK, TV, 8>), grid, dim3(NT), lds, s, a);

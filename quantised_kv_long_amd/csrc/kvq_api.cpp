@@ -336,6 +336,122 @@ int kvq_combine(const float* part_o, const float* part_lse, const int32_t* seq_l
     return finish(kvq::launch_combine(a, static_cast<hipStream_t>(stream)));
 }
 
+int kvq_decode_attn_mixed(const kvq_plane_desc* k_tail, const kvq_plane_desc* v_tail,
+                          const kvq_plane_desc* k_win, const kvq_plane_desc* v_win, const void* q,
+                          const int32_t* tail_lens, const int32_t* win_lens, int B, int Hq, int Hkv,
+                          int D, float softmax_scale, int tail_max_len, int tail_split_tokens,
+                          int tail_max_splits, float* tail_part_o, float* tail_part_lse,
+                          int win_max_len, int win_split_tokens, int win_max_splits,
+                          float* win_part_o, float* win_part_lse, void* stream)
+{
+    int rc = validate_decode(k_tail, v_tail, q, tail_lens, B, Hq, Hkv, D, softmax_scale, tail_max_len,
+                             tail_split_tokens, tail_max_splits, tail_part_o, tail_part_lse);
+    if (rc != KVQ_OK) return rc;
+    rc = validate_decode(k_win, v_win, q, win_lens, B, Hq, Hkv, D, softmax_scale, win_max_len,
+                         win_split_tokens, win_max_splits, win_part_o, win_part_lse);
+    if (rc != KVQ_OK) return rc;
+    if (k_win->type != KVQ_F16 || v_win->type != KVQ_F16) return KVQ_ERR_TYPE;
+    const kvq::DecodeArgs t = decode_args(k_tail, v_tail, q, tail_lens, B, Hq, Hkv, D, softmax_scale,
+                                          tail_max_len, tail_split_tokens, tail_max_splits, tail_part_o,
+                                          tail_part_lse);
+    const kvq::DecodeArgs w = decode_args(k_win, v_win, q, win_lens, B, Hq, Hkv, D, softmax_scale,
+                                          win_max_len, win_split_tokens, win_max_splits, win_part_o,
+                                          win_part_lse);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (kvq::decode_mfma_dual_supports(t, w)) return finish(kvq::launch_decode_mfma_dual(t, w, s));
+    // otherwise one launch per region, each with the kernel its shape takes
+    hipError_t e = kvq::decode_mfma_supports(t) ? kvq::launch_decode_mfma(t, s) : kvq::launch_decode_valu(t, s);
+    if (e == hipSuccess)
+        e = kvq::decode_mfma_supports(w) ? kvq::launch_decode_mfma(w, s) : kvq::launch_decode_valu(w, s);
+    return finish(e);
+}
+
+int kvq_decode_step_mixed(const kvq_plane_desc* k_tail, const kvq_plane_desc* v_tail,
+                          const kvq_plane_desc* k_win, const kvq_plane_desc* v_win, const void* k_new,
+                          const void* v_new, const void* q, const int32_t* tail_lens,
+                          const int32_t* win_lens, int B, int Hq, int Hkv, int D, float softmax_scale,
+                          int tail_max_len, int tail_split_tokens, int tail_max_splits,
+                          float* tail_part_o, float* tail_part_lse, int win_max_len,
+                          int win_split_tokens, int win_max_splits, float* win_part_o,
+                          float* win_part_lse, int out_type, void* out, float* lse_out, void* stream)
+{
+    int rc = validate_decode(k_tail, v_tail, q, tail_lens, B, Hq, Hkv, D, softmax_scale, tail_max_len,
+                             tail_split_tokens, tail_max_splits, tail_part_o, tail_part_lse);
+    if (rc != KVQ_OK) return rc;
+    rc = validate_decode(k_win, v_win, q, win_lens, B, Hq, Hkv, D, softmax_scale, win_max_len,
+                         win_split_tokens, win_max_splits, win_part_o, win_part_lse);
+    if (rc != KVQ_OK) return rc;
+    if (k_win->type != KVQ_F16 || v_win->type != KVQ_F16) return KVQ_ERR_TYPE;
+    if (!k_new || !v_new || !out) return KVQ_ERR_NULL;
+    if (out_type != KVQ_F16 && out_type != KVQ_OUT_F32) return KVQ_ERR_TYPE;
+    if (B > 65535 || Hq > 65535) return KVQ_ERR_SHAPE;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16) ||
+        (lse_out && !aligned(lse_out, 4)))
+        return KVQ_ERR_ALIGN;
+    const kvq::DecodeArgs t = decode_args(k_tail, v_tail, q, tail_lens, B, Hq, Hkv, D, softmax_scale,
+                                          tail_max_len, tail_split_tokens, tail_max_splits, tail_part_o,
+                                          tail_part_lse);
+    kvq::DecodeArgs w = decode_args(k_win, v_win, q, win_lens, B, Hq, Hkv, D, softmax_scale,
+                                    win_max_len, win_split_tokens, win_max_splits, win_part_o,
+                                    win_part_lse);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    hipError_t e;
+    const bool window_mfma = kvq::decode_mfma_supports(w);
+    if (window_mfma) {
+        // the window's attention workgroup that holds row win_lens[b] - 1
+        // writes the new row before reading it
+        w.k_new = static_cast<const uint16_t*>(k_new);
+        w.v_new = static_cast<const uint16_t*>(v_new);
+    }
+    if (kvq::decode_mfma_dual_supports(t, w)) {
+        e = kvq::launch_decode_mfma_dual(t, w, s);
+    } else {
+        e = kvq::decode_mfma_supports(t) ? kvq::launch_decode_mfma(t, s) : kvq::launch_decode_valu(t, s);
+        if (e == hipSuccess && !window_mfma) {
+            kvq::AppendArgs ap;
+            ap.k = w.k;
+            ap.v = w.v;
+            ap.tk = w.tk;
+            ap.tv = w.tv;
+            ap.k_new = static_cast<const uint16_t*>(k_new);
+            ap.v_new = static_cast<const uint16_t*>(v_new);
+            ap.k_sb = ap.v_sb = (int64_t)Hkv * D;  // [B][Hkv][D], one row
+            ap.k_sr = ap.v_sr = 0;
+            ap.k_sg = ap.v_sg = D;
+            ap.counts = nullptr;
+            ap.positions = nullptr;  // row win_lens[b] - 1
+            ap.seq_lens = win_lens;
+            ap.B = B;
+            ap.n_new = 1;
+            ap.Hkv = Hkv;
+            ap.D = D;
+            e = kvq::launch_quantize_append(ap, s);
+        }
+        if (e == hipSuccess) e = window_mfma ? kvq::launch_decode_mfma(w, s) : kvq::launch_decode_valu(w, s);
+    }
+    if (e != hipSuccess) return KVQ_ERR_LAUNCH;
+
+    kvq::CombineRegionsArgs c;
+    c.n = 2;
+    const kvq::DecodeArgs* r[2] = {&t, &w};
+    for (int i = 0; i < 2; ++i) {
+        c.part_o[i] = r[i]->part_o;
+        c.part_lse[i] = r[i]->part_lse;
+        c.seq_lens[i] = r[i]->seq_lens;
+        c.split_tokens[i] = r[i]->split_tokens;
+        c.max_splits[i] = r[i]->max_splits;
+    }
+    c.B = B;
+    c.Hq = Hq;
+    c.D = D;
+    c.out_f16 = out_type == KVQ_F16;
+    c.out = out;
+    c.lse_out = lse_out;
+    return finish(kvq::launch_combine_regions(c, s));
+}
+
 int kvq_combine_regions(int n_regions, const float* const* part_o, const float* const* part_lse,
                         const int32_t* const* seq_lens, const int* split_tokens, const int* max_splits,
                         int B, int Hq, int D, int out_type, void* out, float* lse_out, void* stream)

@@ -45,6 +45,15 @@ struct DecodeArgs {
     const uint16_t* v_new;
 };
 
+// Splits a decode launch covers: those that can hold a row below
+// max_seq_len (every length is at most max_seq_len), at most max_splits.
+// Partials past them are never read by the merge.
+__host__ __device__ inline int grid_splits(const DecodeArgs& a)
+{
+    const int n = (a.max_seq_len + a.split_tokens - 1) / a.split_tokens;
+    return n < a.max_splits ? n : a.max_splits;
+}
+
 // Partials of up to MAX_REGIONS regions (separate decode launches over
 // separate caches) merged into one output.
 constexpr int MAX_REGIONS = 4;
@@ -75,6 +84,9 @@ hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
 bool decode_mfma_supports(const DecodeArgs& a);
+// the tail (quantised K and V) and the fp16 window of a mixed cache in one launch
+hipError_t launch_decode_mfma_dual(const DecodeArgs& tail, const DecodeArgs& window, hipStream_t s);
+bool decode_mfma_dual_supports(const DecodeArgs& tail, const DecodeArgs& window);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_combine_regions(const CombineRegionsArgs& a, hipStream_t s);
 

@@ -33,6 +33,7 @@ __global__ void __launch_bounds__(256) quantize_append_kernel(AppendArgs a)
                                : a.k_new + b * a.k_sb + r * a.k_sr + g * a.k_sg;
     src += 32 * blk;
     const int pos0 = a.positions ? a.positions[b] : a.seq_lens[b] - a.n_new;
+    if (pos0 + r < 0) return;  // a sequence shorter than its new rows: nothing before row 0
     const int64_t row = (int64_t)b * P.seq_stride + (int64_t)g * P.head_stride + pos0 + r;
     uint8_t* dst = P.data + row * data_row_bytes(t, a.D) + (int64_t)blk * data_row_bytes(t, 32);
     uint16_t* sdst = P.scales + row * nb + blk;

@@ -34,6 +34,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kvq_quantize_append", "kvq_decode_attn", "kvq_combine", "kvq_decode_attn_variant",
               "kvq_decode_step", "kvq_quantize_rows", "kvq_combine_regions", "kvq_decode_attn_multi",
+              "kvq_decode_attn_mixed", "kvq_decode_step_mixed",
               "kvq_select_kv_tier", "kvq_tier_cache_bytes", "kvq_tier_types", "kvq_data_row_bytes",
               "kvq_scale_row_bytes", "kvq_status_string"):
         assert n in names
@@ -294,3 +295,59 @@ def test_decode_multi_validation(lib):
     assert multi(lib, nq=4) == -2                   # 4 tokens x 5 heads = 20 columns
     assert multi(lib, nq=3, max_len=2, max_splits=1) == -2   # fewer rows than query tokens
     assert multi(lib, D=64, nq=1) == -2             # the matrix-core kernel covers D 128/256/512
+
+
+def mixed(lib, kt=None, vt=None, kw=None, vw=None, q=A, tl=A, wl=A, B=1, Hq=40, Hkv=8, D=128,
+          scale=0.088, tmax=100, tsplit=64, tms=2, tpo=A, tpl=A, wmax=100, wsplit=64, wms=2, wpo=A,
+          wpl=A):
+    kt = kt if kt is not None else plane()
+    vt = vt if vt is not None else plane()
+    kw = kw if kw is not None else plane(t=0)
+    vw = vw if vw is not None else plane(t=0)
+    return lib.kvq_decode_attn_mixed(ctypes.byref(kt), ctypes.byref(vt), ctypes.byref(kw), ctypes.byref(vw),
+                                     q, tl, wl, B, Hq, Hkv, D, scale, tmax, tsplit, tms, tpo, tpl, wmax,
+                                     wsplit, wms, wpo, wpl, None)
+
+
+@nogpu
+def test_decode_mixed_validation(lib):
+    # each region takes the decode checks; the window must be fp16 in K and V
+    assert mixed(lib, q=None) == -1
+    assert mixed(lib, tl=None) == -1
+    assert mixed(lib, wl=None) == -1
+    assert mixed(lib, wpo=None) == -1
+    assert mixed(lib, Hq=41) == -2
+    assert mixed(lib, kw=plane(t=1)) == -3
+    assert mixed(lib, vw=plane(t=2)) == -3
+    assert mixed(lib, kw=plane(t=7)) == -3
+    assert mixed(lib, tpl=A + 2) == -4
+    assert mixed(lib, wmax=101) == -5
+    assert mixed(lib, tsplit=100) == -6
+    assert mixed(lib, wms=1) == -6
+
+
+def step_mixed(lib, kt=None, vt=None, kw=None, vw=None, kn=A, vn=A, q=A, tl=A, wl=A, B=1, Hq=40, Hkv=8,
+               D=128, scale=0.088, tmax=100, tsplit=64, tms=2, tpo=A, tpl=A, wmax=100, wsplit=64, wms=2,
+               wpo=A, wpl=A, ot=0, out=A, lse=None):
+    kt = kt if kt is not None else plane()
+    vt = vt if vt is not None else plane()
+    kw = kw if kw is not None else plane(t=0)
+    vw = vw if vw is not None else plane(t=0)
+    return lib.kvq_decode_step_mixed(ctypes.byref(kt), ctypes.byref(vt), ctypes.byref(kw), ctypes.byref(vw),
+                                     kn, vn, q, tl, wl, B, Hq, Hkv, D, scale, tmax, tsplit, tms, tpo, tpl,
+                                     wmax, wsplit, wms, wpo, wpl, ot, out, lse, None)
+
+
+@nogpu
+def test_decode_step_mixed_validation(lib):
+    assert step_mixed(lib, q=None) == -1
+    assert step_mixed(lib, kn=None) == -1
+    assert step_mixed(lib, out=None) == -1
+    assert step_mixed(lib, Hq=41) == -2
+    assert step_mixed(lib, kw=plane(t=2)) == -3
+    assert step_mixed(lib, ot=1) == -3
+    assert step_mixed(lib, vn=A + 2) == -4
+    assert step_mixed(lib, out=A + 4) == -4
+    assert step_mixed(lib, lse=A + 2) == -4
+    assert step_mixed(lib, wmax=101) == -5
+    assert step_mixed(lib, tms=1) == -6

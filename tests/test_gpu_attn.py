@@ -98,6 +98,40 @@ def test_small_cases_all_type_pairs(variant, tk, tv, case):
     assert np.all(np.abs(po - ro) <= 2e-3 + 1e-2 * np.abs(ro))
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_partials_past_max_seq_len_untouched(variant):
+    """Partials sized for a capacity beyond max_seq_len: splits from
+    ceil(max_seq_len / split_tokens) on are not written (the launch covers only
+    the splits a row below max_seq_len can fall in), and the merge, which reads
+    only splits holding rows, matches the oracle."""
+    dev = "cuda"
+    B, Hkv, G, D, st = 2, 2, 5, 128, 64
+    lens, max_len, cap = [700, 123], 700, 2000
+    if not variant_ok(variant, D, G, "q8_0", "q4_0"):
+        pytest.skip(f"{variant} does not cover D={D} G={G}")
+    note(f"partials past max_seq_len {variant}")
+    k = synth.normal_f16((B, Hkv, cap, D), 1301, dev)
+    v = synth.normal_f16((B, Hkv, cap, D), 1302, dev)
+    q = synth.normal_f16((B, Hkv * G, D), 1303, dev)
+    kc, vc = fill_pair("q8_0", "q4_0", k, v)
+    part = C.Partials(B, Hkv * G, D, cap, st)
+    part.o.fill_(5.0)
+    part.lse.fill_(5.0)
+    lt = torch.tensor(lens, dtype=torch.int32, device=dev)
+    C.decode(kc, vc, q, lt, max_len, part, 1 / math.sqrt(D), variant)
+    out = torch.empty((B, Hkv * G, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hkv * G), dtype=torch.float32, device=dev)
+    C.combine(part, lt, out, lse)
+    torch.cuda.synchronize()
+    ns = -(-max_len // st)
+    assert part.max_splits > ns
+    assert torch.all(part.o[:, :, ns:] == 5.0) and torch.all(part.lse[:, :, ns:] == 5.0)
+    assert torch.all(part.lse[:, :, :ns] != 5.0)
+    ref, ref_lse = oracle_ref(kc, vc, q, lens, Hkv)
+    assert_close(out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ref, ref_lse,
+                 variant)
+
+
 def test_combine_alone_on_oracle_partials():
     """K3 fed the oracle's split partials (rounded to fp32) reproduces the
     oracle's exact merge."""

@@ -21,6 +21,7 @@ from .gpu_util import (assert_close, download_planes, fill_pair, note, oracle_pl
                        upload_oracle_planes)
 
 torch = pytest.importorskip("torch")
+from quantised_kv_long_amd import _lib  # noqa: E402
 from quantised_kv_long_amd import cache as C  # noqa: E402
 from quantised_kv_long_amd import synth  # noqa: E402
 
@@ -33,18 +34,22 @@ def _gpu():
     require_gpu()
 
 
-def attend_mixed(tail, win, q, tail_lens, win_lens, st_tail, st_win, out_dtype=torch.float32):
-    """Two attention launches and the region merge; returns host fp64 (out, lse)."""
+def attend_mixed(tail, win, q, tail_lens, win_lens, st_tail, st_win, out_dtype=torch.float32,
+                 one_call=True):
+    """Attention over both regions (kvq_decode_attn_mixed, or one
+    kvq_decode_attn per region) and the region merge; returns host fp64
+    (out, lse)."""
     B, Hq, D = q.shape
     scale = 1.0 / math.sqrt(D)
     parts, lens_t = [], []
     for (kc, vc), lens, st in ((tail, tail_lens, st_tail), (win, win_lens, st_win)):
-        lt = torch.tensor(lens, dtype=torch.int32, device=q.device)
-        cap = kc.capacity
-        part = C.Partials(B, Hq, D, cap, st)
-        C.decode(kc, vc, q, lt, cap, part, scale)
-        parts.append(part)
-        lens_t.append(lt)
+        lens_t.append(torch.tensor(lens, dtype=torch.int32, device=q.device))
+        parts.append(C.Partials(B, Hq, D, kc.capacity, st))
+    if one_call:
+        C.decode_mixed(tail, win, q, lens_t[0], lens_t[1], parts[0], parts[1], scale)
+    else:
+        for (kc, vc), lt, part in zip((tail, win), lens_t, parts):
+            C.decode(kc, vc, q, lt, kc.capacity, part, scale)
     out = torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     C.combine_regions(parts, lens_t, out, lse)
@@ -89,6 +94,95 @@ def test_regions_match_oracle(tk, tv, case):
     live = ~empty
     if live.any():
         assert_close(out[live], lse[live], ref[live], ref_lse[live], f"mixed {tk}/{tv} case {case}")
+
+
+@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0"), ("f16", "q4_0")])
+@pytest.mark.parametrize("case", [0, 2, 3, 4])
+def test_mixed_call_is_the_two_calls_bit_for_bit(tk, tv, case):
+    """kvq_decode_attn_mixed (one launch where the matrix-core kernel covers the
+    shape, two launches otherwise) writes the same partials as kvq_decode_attn
+    over each region."""
+    B, Hkv, G, D, tl, tcap, wl, wcap, st_t, st_w = CASES[case]
+    note(f"mixed call vs two calls {tk}/{tv} case {case}")
+    dev = "cuda"
+    seed = 2900 + case
+    tail = fill_pair(tk, tv, synth.normal_f16((B, Hkv, tcap, D), seed, dev),
+                     synth.normal_f16((B, Hkv, tcap, D), seed + 1, dev))
+    win = fill_pair("f16", "f16", synth.normal_f16((B, Hkv, wcap, D), seed + 2, dev),
+                    synth.normal_f16((B, Hkv, wcap, D), seed + 3, dev))
+    q = synth.normal_f16((B, Hkv * G, D), seed + 4, dev)
+    scale = 1.0 / math.sqrt(D)
+    ltt = torch.tensor(tl, dtype=torch.int32, device=dev)
+    ltw = torch.tensor(wl, dtype=torch.int32, device=dev)
+    p1 = (C.Partials(B, Hkv * G, D, tcap, st_t), C.Partials(B, Hkv * G, D, wcap, st_w))
+    p2 = (C.Partials(B, Hkv * G, D, tcap, st_t), C.Partials(B, Hkv * G, D, wcap, st_w))
+    for p in p1 + p2:
+        p.o.fill_(7.0)
+        p.lse.fill_(7.0)
+    C.decode_mixed(tail, win, q, ltt, ltw, p1[0], p1[1], scale)
+    C.decode(tail[0], tail[1], q, ltt, tcap, p2[0], scale)
+    C.decode(win[0], win[1], q, ltw, wcap, p2[1], scale)
+    torch.cuda.synchronize()
+    for a, b in zip(p1, p2):
+        assert torch.equal(a.o, b.o) and torch.equal(a.lse, b.lse)
+
+
+@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0"), ("f16", "q4_0")])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_step_mixed_is_append_attention_merge_bit_for_bit(tk, tv, case):
+    """kvq_decode_step_mixed equals kvq_quantize_append of the new row into the
+    window at row win_lens[b] - 1, kvq_decode_attn_mixed and
+    kvq_combine_regions, bit for bit: window rows, partials, output and LSE (a
+    sequence whose window length is 0 gets no row)."""
+    B, Hkv, G, D, tl, tcap, wl, wcap, st_t, st_w = CASES[case]
+    note(f"step_mixed vs three calls {tk}/{tv} case {case}")
+    dev = "cuda"
+    seed = 3100 + case
+    kt = synth.normal_f16((B, Hkv, tcap, D), seed, dev)
+    vt = synth.normal_f16((B, Hkv, tcap, D), seed + 1, dev)
+    kw = synth.normal_f16((B, Hkv, wcap, D), seed + 2, dev)
+    vw = synth.normal_f16((B, Hkv, wcap, D), seed + 3, dev)
+    q = synth.normal_f16((B, Hkv * G, D), seed + 4, dev)
+    k_new = synth.normal_f16((B, Hkv, D), seed + 5, dev)
+    v_new = synth.normal_f16((B, Hkv, D), seed + 6, dev)
+    scale = 1.0 / math.sqrt(D)
+    ltt = torch.tensor(tl, dtype=torch.int32, device=dev)
+    ltw = torch.tensor(wl, dtype=torch.int32, device=dev)
+    res = []
+    for fused in (True, False):
+        tail = fill_pair(tk, tv, kt, vt)
+        win = fill_pair("f16", "f16", kw, vw)   # rows [0, wcap) written; the step overwrites one
+        parts = (C.Partials(B, Hkv * G, D, tcap, st_t), C.Partials(B, Hkv * G, D, wcap, st_w))
+        out = torch.full((B, Hkv * G, D), 7.0, dtype=torch.float32, device=dev)
+        lse = torch.full((B, Hkv * G), 7.0, dtype=torch.float32, device=dev)
+        if fused:
+            C.decode_step_mixed(tail, win, k_new, v_new, q, ltt, ltw, parts[0], parts[1], scale, out, lse)
+        else:
+            C.append(win[0], win[1], k_new.unsqueeze(1), v_new.unsqueeze(1), ltw - 1, wcap)
+            C.decode_mixed(tail, win, q, ltt, ltw, parts[0], parts[1], scale)
+            C.combine_regions(parts, [ltt, ltw], out, lse)
+        torch.cuda.synchronize()
+        res.append((win[0].data.clone(), win[1].data.clone(), parts[0].o.clone(), parts[0].lse.clone(),
+                    parts[1].o.clone(), parts[1].lse.clone(), out, lse))
+    names = ("window K", "window V", "tail part_o", "tail part_lse", "window part_o", "window part_lse",
+             "out", "lse")
+    for n, a, b in zip(names, *res):
+        if n.endswith("part_o") or n.endswith("part_lse"):
+            # splits past a sequence's last one are not written by either path
+            continue
+        assert torch.equal(a, b), n
+    for b in range(B):
+        for (n, a, c), L, st in zip(((2, res[0][2], res[1][2]), (4, res[0][4], res[1][4])), (tl, wl),
+                                    (st_t, st_w)):
+            S = -(-L[b] // st)
+            assert torch.equal(a[b, :, :S], c[b, :, :S]), f"{names[n]} b {b}"
+            assert torch.equal(res[0][n + 1][b, :, :S], res[1][n + 1][b, :, :S]), f"{names[n + 1]} b {b}"
+    # the new row is in the window where the lengths say
+    kh = to_host_u16(k_new)
+    wk = res[0][0].cpu().numpy().view(np.uint16)
+    for b in range(B):
+        if wl[b] > 0:
+            assert np.array_equal(wk[b, :, wl[b] - 1], kh[b])
 
 
 def test_one_region_merge_equals_combine():
@@ -151,14 +245,16 @@ def test_quantize_rows_bit_exact(tk, tv):
             assert np.array_equal(s, want[2]), f"{what} scales"
 
 
+@pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0")])
-def test_rolling_window_decode_steps(tk, tv):
-    """Decode steps on a mixed cache: each new token goes into the fp16 window
-    (kvq_quantize_append on fp16 planes: a copy); when the window is full its
-    rows are quantised into the tail (kvq_quantize_rows) and it starts empty.
-    Every step's attention (two launches + the region merge) against the
-    oracle over tail + window, and the tail's bytes against the oracle's
-    quantiser of the same tokens."""
+def test_rolling_window_decode_steps(tk, tv, fused):
+    """Decode steps on a mixed cache: each new token goes into the fp16 window;
+    when the window is full its rows are quantised into the tail
+    (kvq_quantize_rows) and it starts empty.  Fused: kvq_decode_step_mixed
+    writes the token and attends; otherwise kvq_quantize_append on the fp16
+    planes (a copy), kvq_decode_attn_mixed and the region merge.  Every step's
+    output against the oracle over tail + window, and the tail's bytes
+    against the oracle's quantiser of the same tokens."""
     B, Hkv, G, D, W = 2, 2, 5, 128, 16
     L0 = [300, 45]                      # tokens in the tail at the start
     steps = 40
@@ -188,11 +284,25 @@ def test_rolling_window_decode_steps(tk, tv):
         tok = [Lq[b] + Lw[b] for b in range(B)]
         k_new = torch.stack([k_all[b, :, tok[b]] for b in range(B)]).unsqueeze(1).contiguous()
         v_new = torch.stack([v_all[b, :, tok[b]] for b in range(B)]).unsqueeze(1).contiguous()
-        pos = torch.tensor(Lw, dtype=torch.int32, device=dev)
-        C.append(win_k, win_v, k_new, v_new, pos, max(Lw) + 1)
-        Lw = [x + 1 for x in Lw]
         q = q_all[i].contiguous()
-        out, lse = attend_mixed((tail_k, tail_v), (win_k, win_v), q, Lq, Lw, 64, 64)
+        if fused:
+            Lw = [x + 1 for x in Lw]
+            ltt = torch.tensor(Lq, dtype=torch.int32, device=dev)
+            ltw = torch.tensor(Lw, dtype=torch.int32, device=dev)
+            parts = (C.Partials(B, Hkv * G, D, cap, 64), C.Partials(B, Hkv * G, D, W, 64))
+            o = torch.empty((B, Hkv * G, D), dtype=torch.float32, device=dev)
+            ls = torch.empty((B, Hkv * G), dtype=torch.float32, device=dev)
+            C.decode_step_mixed((tail_k, tail_v), (win_k, win_v), k_new[:, 0].contiguous(),
+                                v_new[:, 0].contiguous(), q, ltt, ltw, parts[0], parts[1],
+                                1 / math.sqrt(D), o, ls)
+            torch.cuda.synchronize()
+            out = o.cpu().numpy().astype(np.float64)
+            lse = ls.cpu().numpy().astype(np.float64)
+        else:
+            pos = torch.tensor(Lw, dtype=torch.int32, device=dev)
+            C.append(win_k, win_v, k_new, v_new, pos, max(Lw) + 1)
+            Lw = [x + 1 for x in Lw]
+            out, lse = attend_mixed((tail_k, tail_v), (win_k, win_v), q, Lq, Lw, 64, 64)
         # the oracle: tail rows from its own quantiser, window rows the tokens' fp16 values
         ref, ref_lse = O.attend_regions(
             to_host_u16(q), [(k_q, v_q, Lq), (k_win_ref(kh, Lq, Lw, W), k_win_ref(vh, Lq, Lw, W), Lw)],
@@ -230,9 +340,9 @@ def k_win_ref(xh, Lq, Lw, W):
 @pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0")])
 def test_mixed_full_size_64k_tail_and_window(tk, tv):
     """A layer of the 64k workload split as 63488 quantised tail rows and a
-    2048-row fp16 window, in the launch configuration of the benchmark (split
-    1024 for the tail, 256 for the window); sampled query heads against the
-    oracle restricted to the KV heads they read."""
+    2048-row fp16 window, in the launch configuration of the benchmark (the
+    splits of mixed_splits, one round of resident workgroups); sampled query
+    heads against the oracle restricted to the KV heads they read."""
     wl = synth.WORKLOADS["stack48_d128_ctx64k"]
     B, Hkv, D, G = wl.B, wl.Hkv, wl.D, wl.G
     Lw, Lt = 2048, wl.ctx - 2048
@@ -243,7 +353,9 @@ def test_mixed_full_size_64k_tail_and_window(tk, tv):
     win = fill_pair("f16", "f16", synth.normal_f16((B, Hkv, Lw, D), 2503, dev),
                     synth.normal_f16((B, Hkv, Lw, D), 2504, dev))
     q = synth.normal_f16((B, wl.Hq, D), 2505, dev)
-    out, lse = attend_mixed(tail, win, q, [Lt], [Lw], 1024, 256)
+    row_t = sum(_lib.kvq_data_row_bytes(t, D) + _lib.kvq_scale_row_bytes(t, D) for t in (tk, tv))
+    st, sw = C.mixed_splits(Lt, Lw, row_t, 4 * D, B, Hkv, D)
+    out, lse = attend_mixed(tail, win, q, [Lt], [Lw], st, sw)
     for h in (0, 17, 39):
         g = h // G
         sub = lambda p: (p[0], np.ascontiguousarray(p[1][:, g:g + 1]), np.ascontiguousarray(p[2][:, g:g + 1]))
