@@ -29,9 +29,37 @@ __global__ void __launch_bounds__(CMB_NT) combine_kernel(CombineArgs a)
         combine_rows<16>(pl, po, S, a.D, a.out_f16, out, lse, sm);
 }
 
+// The splits of all regions of one (sequence, query head) as one list:
+// region 0's splits, then region 1's, ... so that one batch of loads spans
+// the regions.
+struct CombineSrcN {
+    const float* pl[MAX_REGIONS];
+    const float4* po4[MAX_REGIONS];
+    int first[MAX_REGIONS];   // index of each region's split 0 in the list
+    int n, D4;
+    __device__ __forceinline__ void load(int sp, int c, float& ls, float4& v) const
+    {
+        // the last region whose first split is at or before sp (static
+        // indices only: the arrays stay in registers)
+        const float* p = pl[0];
+        const float4* o = po4[0];
+        int f = 0;
+#pragma unroll
+        for (int k = 1; k < MAX_REGIONS; ++k) {
+            if (k < n && sp >= first[k]) {
+                p = pl[k];
+                o = po4[k];
+                f = first[k];
+            }
+        }
+        ls = p[sp - f];
+        v = o[(int64_t)(sp - f) * D4 + c];
+    }
+};
+
 // The same merge over the partials of several regions (HAL #582 section 5
 // P2: each region of a mixed cache, the fp16 window and the quantised tail,
-// has its own typed attention launch; their partials are merged exactly).
+// has its own typed attention; their partials are merged exactly).
 __global__ void __launch_bounds__(CMB_NT) combine_regions_kernel(CombineRegionsArgs a)
 {
     __shared__ CombineLds sm;
@@ -39,14 +67,24 @@ __global__ void __launch_bounds__(CMB_NT) combine_regions_kernel(CombineRegionsA
     const int64_t bh = (int64_t)b * a.Hq + h;
     void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh * a.D)
                           : (void*)(reinterpret_cast<float*>(a.out) + bh * a.D);
-    CombineState st = combine_init();
-    for (int i = 0; i < a.n; ++i) {
+    CombineSrcN src;
+    src.n = a.n;
+    src.D4 = a.D >> 2;
+    int S = 0;
+#pragma unroll
+    for (int i = 0; i < MAX_REGIONS; ++i) {
+        src.first[i] = S;
+        if (i >= a.n) continue;
         const int L = a.seq_lens[i][b];
-        const int S = L > 0 ? min((L + a.split_tokens[i] - 1) / a.split_tokens[i], a.max_splits[i]) : 0;
-        const float* pl = a.part_lse[i] + bh * a.max_splits[i];
-        const float* po = a.part_o[i] + bh * a.max_splits[i] * a.D;
-        combine_fold<8>(pl, po, S, a.D, st);
+        S += L > 0 ? min((L + a.split_tokens[i] - 1) / a.split_tokens[i], a.max_splits[i]) : 0;
+        src.pl[i] = a.part_lse[i] + bh * a.max_splits[i];
+        src.po4[i] = reinterpret_cast<const float4*>(a.part_o[i] + bh * a.max_splits[i] * a.D);
     }
+    CombineState st = combine_init();
+    if (S <= 8 * (CMB_NT / (a.D / 4)))
+        combine_fold_src<8>(src, S, a.D, st);
+    else
+        combine_fold_src<16>(src, S, a.D, st);
     combine_finish(st, a.D, a.out_f16, out, a.lse_out ? a.lse_out + bh : nullptr, sm);
 }
 

@@ -41,20 +41,31 @@ __device__ __forceinline__ CombineState combine_init()
     return CombineState{-INFINITY, 0.0f, make_float4(0.0f, 0.0f, 0.0f, 0.0f)};
 }
 
-// Folds the S partials at pl (lse values) / po (rows of D floats, 16-byte
-// aligned) into the thread's running state: its four columns of its residue
-// class of the splits.  Splits with lse = -inf carry no weight.  U splits are
-// loaded per batch.  Weights are exp2((lse - m) * log2 e) on the hardware
-// exp2: the relative error of a weight is a few fp32 ulps times |lse - m|.
-template <int U>
-__device__ __forceinline__ void combine_fold(const float* pl, const float* po, int S, int D,
-                                             CombineState& st)
+// Partials of one region: lse values at pl, rows of D floats at po (16-byte
+// aligned).  load(sp, c) gives split sp's lse and its float4 column c.
+struct CombineSrc1 {
+    const float* pl;
+    const float4* po4;
+    int D4;
+    __device__ __forceinline__ void load(int sp, int c, float& ls, float4& v) const
+    {
+        ls = pl[sp];
+        v = po4[(int64_t)sp * D4 + c];
+    }
+};
+
+// Folds S partials (split sp read by src.load) into the thread's running
+// state: its four columns of its residue class of the splits.  Splits with
+// lse = -inf carry no weight.  U splits are loaded per batch.  Weights are
+// exp2((lse - m) * log2 e) on the hardware exp2: the relative error of a
+// weight is a few fp32 ulps times |lse - m|.
+template <int U, class Src>
+__device__ __forceinline__ void combine_fold_src(const Src& src, int S, int D, CombineState& st)
 {
     const int tid = threadIdx.x;
     const int D4 = D >> 2;                 // float4 columns (D <= 512: at most 128)
     const int R = CMB_NT / D4;             // split residue classes
     const int c = tid % D4, r = tid / D4;
-    const float4* po4 = reinterpret_cast<const float4*>(po);
 
     float m = st.m, l = st.l;
     float4 a = st.a;
@@ -65,8 +76,7 @@ __device__ __forceinline__ void combine_fold(const float* pl, const float* po, i
         for (int u = 0; u < U; ++u) {
             const int sp = s0 + u * R;
             if (sp < S) {
-                ls[u] = pl[sp];
-                v[u] = po4[(int64_t)sp * D4 + c];
+                src.load(sp, c, ls[u], v[u]);
             } else {
                 ls[u] = -INFINITY;
                 v[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -97,6 +107,14 @@ __device__ __forceinline__ void combine_fold(const float* pl, const float* po, i
     st.m = m;
     st.l = l;
     st.a = a;
+}
+
+// The S partials at pl / po.
+template <int U>
+__device__ __forceinline__ void combine_fold(const float* pl, const float* po, int S, int D,
+                                             CombineState& st)
+{
+    combine_fold_src<U>(CombineSrc1{pl, reinterpret_cast<const float4*>(po), D >> 2}, S, D, st);
 }
 
 // Merges the residue classes' states through LDS and writes D outputs at out
