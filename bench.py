@@ -20,8 +20,8 @@ Prints ONE JSON line.  Steps are captured once in a HIP graph and replayed
 
 Two further modes time the wider calls on the same workloads:
   --queries N  N query tokens per sequence and step (the verify step of
-               speculative decoding): append the N rows, kvq_decode_attn_multi,
-               kvq_combine over N * Hq heads;
+               speculative decoding): kvq_decode_step_multi (the attention
+               kernel writes the N rows, then kvq_combine over N * Hq heads);
   --window W   a mixed cache: the last W rows of each sequence in an fp16 window,
                the rest in the arm's types; append the new token to the window,
                attention over both regions in one launch (kvq_decode_attn_mixed),
@@ -89,7 +89,7 @@ def parse():
     p.add_argument("--split-tokens", type=int, default=None)
     p.add_argument("--queries", type=int, default=1,
                    help="query tokens per sequence and step (> 1: multi-query decode, "
-                        "kvq_decode_attn_multi)")
+                        "kvq_decode_step_multi)")
     p.add_argument("--window", type=int, default=0,
                    help="> 0: mixed cache, the last WINDOW rows of each sequence in an fp16 window "
                         "and the rest in the arm's types (kvq_decode_attn_mixed and "
@@ -249,6 +249,10 @@ class Arm:
                 self.calls.append(dict(
                     append=(ctypes.byref(kd), ctypes.byref(vd), L["knew"].data_ptr(), L["vnew"].data_ptr(),
                             self.pos.data_ptr(), wl.B, N, wl.Hkv, wl.D, self.max_len),
+                    step_multi=(ctypes.byref(kd), ctypes.byref(vd), L["knew"].data_ptr(), L["vnew"].data_ptr(),
+                                L["q"].data_ptr(), self.lens_t.data_ptr(), wl.B, N, Hq, wl.Hkv, wl.D, scale,
+                                self.max_len, part.split_tokens, part.max_splits, part.o.data_ptr(),
+                                part.lse.data_ptr(), 0, self.out.data_ptr(), None),
                     multi=(ctypes.byref(kd), ctypes.byref(vd), L["q"].data_ptr(), self.lens_t.data_ptr(),
                            wl.B, N, Hq, wl.Hkv, wl.D, scale, self.max_len, part.split_tokens,
                            part.max_splits, part.o.data_ptr(), part.lse.data_ptr()),
@@ -275,8 +279,9 @@ class Arm:
     def step(self, stream, rep=0, mode="step"):
         """One step over all layers of replica `rep`: mode "step" (kvq_decode_step),
         "three" (append + decode + combine) or "decode" (the attention launch alone).
-        Multi-query: append the N tokens, kvq_decode_attn_multi, kvq_combine (step and
-        three alike).  Window: "step" is kvq_decode_step_mixed (the attention
+        Multi-query: "step" is kvq_decode_step_multi (the attention kernel writes
+        the N tokens); "three" appends them, runs kvq_decode_attn_multi and
+        kvq_combine.  Window: "step" is kvq_decode_step_mixed (the attention
         kernel writes the token into the fp16 window); "three" appends the token,
         runs kvq_decode_attn_mixed and kvq_combine_regions.  With a forced
         variant both run one kvq_decode_attn_variant per region instead."""
@@ -298,6 +303,9 @@ class Arm:
                     assert lib.kvq_combine_regions(*c["combine"], stream) == 0
                 continue
             if self.N > 1:
+                if mode == "step":
+                    assert lib.kvq_decode_step_multi(*c["step_multi"], stream) == 0
+                    continue
                 if mode != "decode":
                     assert lib.kvq_quantize_append(*c["append"], stream) == 0
                 assert lib.kvq_decode_attn_multi(*c["multi"], stream) == 0
@@ -392,7 +400,7 @@ def step_path(args):
         return ("kvq_decode_step_mixed" if args.variant == "auto" else
                 "kvq_quantize_append + kvq_decode_attn_variant x2 + kvq_combine_regions")
     if args.queries > 1:
-        return "kvq_quantize_append + kvq_decode_attn_multi + kvq_combine"
+        return "kvq_decode_step_multi"
     return "kvq_decode_step"
 
 

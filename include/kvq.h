@@ -255,6 +255,27 @@ int kvq_decode_attn_multi(const kvq_plane_desc* k_cache, const kvq_plane_desc* v
                           int D, float softmax_scale, int max_seq_len, int split_tokens,
                           int max_splits, float* part_o, float* part_lse, void* stream);
 
+/*
+ * One multi-query decode step: the n_q new tokens' K and V rows are written
+ * at rows L_b - n_q .. L_b - 1 (row i of k_new / v_new at row L_b - n_q + i),
+ * then kvq_decode_attn_multi and kvq_combine over n_q * Hq heads run.
+ * Results equal kvq_quantize_append of the n_q rows (positions L_b - n_q)
+ * followed by those two calls, bit for bit.  Two kernel launches: each
+ * attention workgroup whose split holds some of the new rows writes them
+ * before it reads them, then the merge runs.
+ *
+ *   k_new, v_new : device, [B][n_q][Hkv][D] binary16.
+ *   out          : device, [B][n_q][Hq][D] of out_type; lse_out [B][n_q][Hq]
+ *                  fp32 or NULL.
+ *   Other arguments as for kvq_decode_attn_multi and kvq_combine.
+ */
+int kvq_decode_step_multi(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache,
+                          const void* k_new, const void* v_new, const void* q,
+                          const int32_t* seq_lens, int B, int n_q, int Hq, int Hkv, int D,
+                          float softmax_scale, int max_seq_len, int split_tokens, int max_splits,
+                          float* part_o, float* part_lse, int out_type, void* out, float* lse_out,
+                          void* stream);
+
 /* Kernel family for kvq_decode_attn_variant. */
 enum {
     KVQ_VARIANT_AUTO = 0, /* what kvq_decode_attn uses                         */

@@ -91,6 +91,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_decode_step_mixed.argtypes = [DP, DP, DP, DP, P, P, P, P, P, i32, i32, i32, i32, f32, i32,
                                           i32, i32, P, P, i32, i32, i32, P, P, i32, P, P, P]
     lib.kvq_decode_step_mixed.restype = i32
+    lib.kvq_decode_step_multi.argtypes = [DP, DP, P, P, P, P, i32, i32, i32, i32, i32, f32, i32, i32, i32,
+                                          P, P, i32, P, P, P]
+    lib.kvq_decode_step_multi.restype = i32
     lib.kvq_decode_attn_multi.argtypes = [DP, DP, P, P, i32, i32, i32, i32, i32, f32, i32, i32, i32,
                                           P, P, P]
     lib.kvq_decode_attn_multi.restype = i32
@@ -234,6 +237,18 @@ def kvq_decode_step_mixed(k_tail: kvq_plane_desc, v_tail: kvq_plane_desc, k_win:
                                       _ptr(win_part_lse), ot, _ptr(out), _ptr(lse_out),
                                       _stream(stream))
     return _check("kvq_decode_step_mixed", rc)
+
+
+def kvq_decode_step_multi(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, k_new, v_new, q, seq_lens,
+                          B: int, n_q: int, Hq: int, Hkv: int, D: int, softmax_scale: float,
+                          max_seq_len: int, split_tokens: int, max_splits: int, part_o, part_lse, out_type,
+                          out, lse_out=None, stream=None) -> int:
+    ot = OUT_F32 if out_type in ("f32", OUT_F32) else _tcode(out_type)
+    rc = load().kvq_decode_step_multi(ctypes.byref(k_cache), ctypes.byref(v_cache), _ptr(k_new), _ptr(v_new),
+                                      _ptr(q), _ptr(seq_lens), B, n_q, Hq, Hkv, D, float(softmax_scale),
+                                      max_seq_len, split_tokens, max_splits, _ptr(part_o), _ptr(part_lse),
+                                      ot, _ptr(out), _ptr(lse_out), _stream(stream))
+    return _check("kvq_decode_step_multi", rc)
 
 
 def kvq_decode_attn_multi(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, q, seq_lens, B: int,

@@ -164,6 +164,19 @@ def decode_multi(kc: CachePlanes, vc: CachePlanes, q: torch.Tensor, seq_lens: to
                                       part.max_splits, part.o, part.lse, stream)
 
 
+def decode_step_multi(kc: CachePlanes, vc: CachePlanes, k_new: torch.Tensor, v_new: torch.Tensor,
+                      q: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, part: "Partials",
+                      softmax_scale: float, out: torch.Tensor, lse_out=None, stream=None):
+    """kvq_decode_step_multi: k_new, v_new (B, n_q, Hkv, D) fp16 written at rows
+    seq_lens[b] - n_q .., then kvq_decode_attn_multi and the merge into ``out``
+    (B, n_q * Hq, D); ``part`` built for n_q * Hq heads."""
+    B, n_q, Hq, D = q.shape
+    ot = "f16" if out.dtype == torch.float16 else "f32"
+    return _lib.kvq_decode_step_multi(kc.desc(), vc.desc(), k_new, v_new, q, seq_lens, B, n_q, Hq, kc.Hkv, D,
+                                      softmax_scale, max_seq_len, part.split_tokens, part.max_splits,
+                                      part.o, part.lse, ot, out, lse_out, stream)
+
+
 def decode(kc: CachePlanes, vc: CachePlanes, q: torch.Tensor, seq_lens: torch.Tensor,
            max_seq_len: int, part: Partials, softmax_scale: float, variant="auto", stream=None):
     """kvq_decode_attn_variant on torch tensors: q (B, Hq, D) fp16."""

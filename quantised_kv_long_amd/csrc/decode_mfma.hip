@@ -242,11 +242,38 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     const uint8_t* vdata = a.v.data + vrow0 * C::RBV_ROW + wsl * C::RBV;
     const uint8_t* vscl = reinterpret_cast<const uint8_t*>(a.v.scales + vrow0 * C::NB_ROW + wsl * C::NB);
 
-    // ---- decode step with the new token: the workgroup whose split holds
-    //      row L-1 first quantises the new K and V rows of its KV head into
-    //      that row (the same block quantiser as kvq_quantize_append), then
-    //      makes them visible to its own loads
-    if (a.k_new != nullptr && t_end == L) {   // (single query token)
+    // ---- decode step with the new tokens: the workgroup whose split holds
+    //      row L-1 (multi-query: each workgroup whose split holds some of the
+    //      rows [L-NQ, L)) first quantises the new K and V rows of its KV head
+    //      into those rows (the same block quantiser as kvq_quantize_append),
+    //      then makes them visible to its own loads
+    if constexpr (MQ) {
+        const int r_lo = max(L - NQ, t_begin);
+        const int nrows = t_end - r_lo;
+        if (a.k_new != nullptr && nrows > 0) {
+            // nrows * 2*NB_ROW blocks (per row: K then V), one aligned
+            // half-wave of 32 lanes per block
+            for (int it = tid >> 5; it < nrows * 2 * C::NB_ROW; it += NT / 32) {
+                const int r = r_lo + it / (2 * C::NB_ROW);
+                const int blk2 = it % (2 * C::NB_ROW);
+                const bool isv = blk2 >= C::NB_ROW;
+                const int blk = isv ? blk2 - C::NB_ROW : blk2;
+                const int i = r - (L - NQ);                  // new row i of this sequence
+                const uint16_t* src =
+                    (isv ? a.v_new : a.k_new) + (((int64_t)b * NQ + i) * a.Hkv + g) * D + 32 * blk;
+                const int64_t row = (isv ? vrow0 : krow0) + r;
+                if (isv) {
+                    quantize_block_lanes<TV>(src, a.v.data + row * C::RBV_ROW + blk * rb(TV, 32),
+                                             a.v.scales + row * C::NB_ROW + blk, tid & 31);
+                } else {
+                    quantize_block_lanes<TK>(src, a.k.data + row * C::RBK_ROW + blk * rb(TK, 32),
+                                             a.k.scales + row * C::NB_ROW + blk, tid & 31);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(VMCNT0);
+            __syncthreads();
+        }
+    } else if (a.k_new != nullptr && t_end == L) {
         // 2*NB_ROW blocks (K then V), one aligned half-wave of 32 lanes per block
         for (int blk2 = tid >> 5; blk2 < 2 * C::NB_ROW; blk2 += NT / 32) {
             const bool isv = blk2 >= C::NB_ROW;

@@ -307,6 +307,47 @@ int kvq_decode_attn_multi(const kvq_plane_desc* k_cache, const kvq_plane_desc* v
     return finish(kvq::launch_decode_mfma(a, static_cast<hipStream_t>(stream)));
 }
 
+int kvq_decode_step_multi(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache, const void* k_new,
+                          const void* v_new, const void* q, const int32_t* seq_lens, int B, int n_q, int Hq,
+                          int Hkv, int D, float softmax_scale, int max_seq_len, int split_tokens,
+                          int max_splits, float* part_o, float* part_lse, int out_type, void* out,
+                          float* lse_out, void* stream)
+{
+    int rc = validate_decode(k_cache, v_cache, q, seq_lens, B, Hq, Hkv, D, softmax_scale, max_seq_len,
+                             split_tokens, max_splits, part_o, part_lse);
+    if (rc != KVQ_OK) return rc;
+    if (n_q < 1 || (int64_t)n_q * (Hq / Hkv) > 16 || max_seq_len < n_q) return KVQ_ERR_SHAPE;
+    if ((int64_t)n_q * Hq > 65535 || B > 65535) return KVQ_ERR_SHAPE;
+    if (!k_new || !v_new || !out) return KVQ_ERR_NULL;
+    if (out_type != KVQ_F16 && out_type != KVQ_OUT_F32) return KVQ_ERR_TYPE;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16) ||
+        (lse_out && !aligned(lse_out, 4)))
+        return KVQ_ERR_ALIGN;
+    kvq::DecodeArgs a = decode_args(k_cache, v_cache, q, seq_lens, B, Hq, Hkv, D, softmax_scale,
+                                    max_seq_len, split_tokens, max_splits, part_o, part_lse);
+    a.nq = n_q;
+    if (!kvq::decode_mfma_supports(a)) return KVQ_ERR_SHAPE;
+    // the attention kernel writes the n_q new rows itself
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (kvq::launch_decode_mfma(a, s) != hipSuccess) return KVQ_ERR_LAUNCH;
+    kvq::CombineArgs c;
+    c.part_o = part_o;
+    c.part_lse = part_lse;
+    c.seq_lens = seq_lens;
+    c.B = B;
+    c.Hq = n_q * Hq;
+    c.D = D;
+    c.split_tokens = split_tokens;
+    c.max_splits = max_splits;
+    c.out_f16 = out_type == KVQ_F16;
+    c.out = out;
+    c.lse_out = lse_out;
+    return finish(kvq::launch_combine(c, s));
+}
+
 int kvq_combine(const float* part_o, const float* part_lse, const int32_t* seq_lens, int B, int Hq,
                 int D, int split_tokens, int max_splits, int out_type, void* out, float* lse_out,
                 void* stream)

@@ -38,8 +38,8 @@ struct DecodeArgs {
     int max_seq_len, split_tokens, max_splits;
     float* part_o;
     float* part_lse;
-    // decode step only (null otherwise): the new K/V row of every (sequence,
-    // KV head), [B][Hkv][D] fp16, written at row seq_lens[b] - 1 by the
+    // decode step only (null otherwise): the new K/V rows, [B][nq][Hkv][D]
+    // fp16, row i of sequence b written at row seq_lens[b] - nq + i by the
     // workgroup whose split holds that row, before it reads it
     const uint16_t* k_new;
     const uint16_t* v_new;

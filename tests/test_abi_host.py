@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kvq_quantize_append", "kvq_decode_attn", "kvq_combine", "kvq_decode_attn_variant",
               "kvq_decode_step", "kvq_quantize_rows", "kvq_combine_regions", "kvq_decode_attn_multi",
-              "kvq_decode_attn_mixed", "kvq_decode_step_mixed",
+              "kvq_decode_attn_mixed", "kvq_decode_step_mixed", "kvq_decode_step_multi",
               "kvq_select_kv_tier", "kvq_tier_cache_bytes", "kvq_tier_types", "kvq_data_row_bytes",
               "kvq_scale_row_bytes", "kvq_status_string"):
         assert n in names
@@ -351,3 +351,27 @@ def test_decode_step_mixed_validation(lib):
     assert step_mixed(lib, lse=A + 2) == -4
     assert step_mixed(lib, wmax=101) == -5
     assert step_mixed(lib, tms=1) == -6
+
+
+def step_multi(lib, k=None, v=None, kn=A, vn=A, q=A, lens=A, B=1, nq=3, Hq=40, Hkv=8, D=128, scale=0.088,
+               max_len=100, split=64, max_splits=2, po=A, pl=A, ot=0, out=A, lse=None):
+    k = k if k is not None else plane()
+    v = v if v is not None else plane()
+    return lib.kvq_decode_step_multi(ctypes.byref(k), ctypes.byref(v), kn, vn, q, lens, B, nq, Hq, Hkv, D,
+                                     scale, max_len, split, max_splits, po, pl, ot, out, lse, None)
+
+
+@nogpu
+def test_decode_step_multi_validation(lib):
+    assert step_multi(lib, q=None) == -1            # the decode checks come first
+    assert step_multi(lib, Hq=41) == -2
+    assert step_multi(lib, split=100) == -6
+    assert step_multi(lib, nq=0) == -2
+    assert step_multi(lib, nq=4) == -2              # 4 tokens x 5 heads = 20 columns
+    assert step_multi(lib, nq=3, max_len=2, max_splits=1) == -2
+    assert step_multi(lib, kn=None) == -1
+    assert step_multi(lib, out=None) == -1
+    assert step_multi(lib, ot=2) == -3
+    assert step_multi(lib, vn=A + 2) == -4
+    assert step_multi(lib, lse=A + 1) == -4
+    assert step_multi(lib, D=64, nq=1) == -2        # the matrix-core kernel covers D 128/256/512
