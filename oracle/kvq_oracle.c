@@ -47,7 +47,11 @@
 #define KVO_MUTANT 0
 #endif
 
-enum { KVO_F16 = 0, KVO_Q8_0 = 1, KVO_Q4_0 = 2 };
+enum { KVO_F16 = 0, KVO_Q8_0 = 1, KVO_Q4_0 = 2,
+       /* more scalar types (the pages' served pairs name them and give their
+        * block sizes; the layouts and quantisers are this project's readings,
+        * documented at their quantisers below) */
+       KVO_Q4_1 = 4, KVO_Q5_0 = 5, KVO_Q5_1 = 6, KVO_Q6_0 = 7 };
 
 /* ---------------------------------------------------------------- fp16 -- */
 
@@ -174,19 +178,165 @@ static void quant_block_q4_0(const uint16_t* x, uint8_t* packed, uint16_t* scale
     }
 }
 
-/* Bytes of the data plane per row of D values, and of the scale plane. */
+/* ----------------------------------------- more scalar types (readings) --
+ *
+ * Block sizes on the pages: q5_0 22 bytes per 32 values (HAL #582 section 1
+ * size table: 66 KiB per token for q5_0/q5_0 at 48 layers x 8 KV heads x 128),
+ * q5_1 24 bytes (section 5 P1 ladder figures), q4_1 20 and q6_0 26 bytes (the
+ * same family: 16 bytes of low nibbles, 4 or 8 bytes of high bits, one fp16
+ * scale, and for the "_1" types one fp16 minimum).  The pages print no
+ * layout; this oracle's readings:
+ *   - a row's data plane holds the low 4 bits of every code first (D/2
+ *     bytes, block b at 16*b, byte j of a block = element j in the low nibble
+ *     and element j+16 in the high nibble, as q4_0), then the high bits:
+ *     q5_0 / q5_1 one little-endian 32-bit word per block whose bit j is bit 4
+ *     of element j's code; q6_0 one little-endian 64-bit word per block whose
+ *     bits 2j, 2j+1 are bits 4, 5 of element j's code;
+ *   - the scale plane holds one fp16 per block (q5_0, q6_0: the scale d) or
+ *     two (q4_1, q5_1: d, then the minimum m);
+ *   - q5_0 / q6_0 extend q4_0: d = fp16(s / -16) or fp16(s / -32) with s the
+ *     first value of largest magnitude; code = clamp(round_half_away(x / d),
+ *     -16, 15) + 16 or clamp(..., -32, 31) + 32; value = d * (code - 16 or
+ *     32); d = 0 gives every code the offset;
+ *   - q4_1 / q5_1 map [min, max] onto the codes: m = fp16(min x), d =
+ *     fp16((max x - min x) / 15 or 31) (binary32 subtraction and division),
+ *     code = clamp(round_half_away((x - m) / d), 0, 15 or 31) with the stored
+ *     m and d (binary32 subtraction and division); d = 0 gives code 0;
+ *     value = d * code + m. */
+
+/* The value of largest magnitude, first index on ties (+0 for a block of
+ * zeros). */
+static float first_absmax(const uint16_t* x)
+{
+    float amax = 0.0f, smax = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+        float v = kvo_f16_to_f32(x[i]);
+        if (fabsf(v) > amax) { amax = fabsf(v); smax = v; }
+    }
+    return smax;
+}
+
+/* Codes of a symmetric block with 2^(bits-1) negative levels: q5_0 (bits 5)
+ * and q6_0 (bits 6).  Writes n[32] in [0, 2^bits) and the fp16 scale. */
+static void quant_codes_sym(const uint16_t* x, int bits, int* n, uint16_t* scale)
+{
+    const int half = 1 << (bits - 1);
+    float smax = first_absmax(x);
+    uint16_t d16 = kvo_f32_to_f16(smax / -(float)half);
+    float d = kvo_f16_to_f32(d16);
+    *scale = d16;
+    for (int i = 0; i < 32; ++i) {
+        if (d == 0.0f) { n[i] = half; continue; }
+        float v = kvo_f16_to_f32(x[i]) / d;
+        double r = kvo_round_half_away((double)v);
+#if KVO_MUTANT == 8
+        if (r > half) r = half;                  /* planted: clamp one level too high */
+#else
+        if (r > half - 1) r = half - 1;
+#endif
+        if (r < -half) r = -half;
+        n[i] = (int)r + half;
+    }
+}
+
+/* Codes of a min/max block: q4_1 (levels 15) and q5_1 (levels 31).  Writes
+ * n[32] in [0, levels] and the fp16 scale and minimum. */
+static void quant_codes_minmax(const uint16_t* x, int levels, int* n, uint16_t* scale, uint16_t* minv)
+{
+    float mn = kvo_f16_to_f32(x[0]), mx = mn;
+    for (int i = 1; i < 32; ++i) {
+        float v = kvo_f16_to_f32(x[i]);
+        if (v < mn) mn = v;
+        if (v > mx) mx = v;
+    }
+    uint16_t d16 = kvo_f32_to_f16((mx - mn) / (float)levels);
+    uint16_t m16 = kvo_f32_to_f16(mn);
+    float d = kvo_f16_to_f32(d16), m = kvo_f16_to_f32(m16);
+#if KVO_MUTANT == 6
+    d = (mx - mn) / (float)levels;               /* planted: unrounded min/max scale */
+#endif
+    *scale = d16;
+    *minv = m16;
+    for (int i = 0; i < 32; ++i) {
+        if (d == 0.0f) { n[i] = 0; continue; }
+        float v = (kvo_f16_to_f32(x[i]) - m) / d;
+        double r = kvo_round_half_away((double)v);
+        if (r > levels) r = levels;
+        if (r < 0.0) r = 0.0;
+        n[i] = (int)r;
+    }
+}
+
+/* Writes the low nibbles of block b (16 bytes at lo + 16*b) and its high
+ * bits (hb_bits 1 or 2 per element, at hi + 4*b or 8*b, little endian). */
+static void pack_codes(const int* n, int hb_bits, uint8_t* lo, uint8_t* hi, int b)
+{
+    for (int j = 0; j < 16; ++j)
+        lo[16 * b + j] = (uint8_t)((n[j] & 15) | ((n[j + 16] & 15) << 4));
+    if (hb_bits == 0) return;
+    uint64_t w = 0;
+    for (int j = 0; j < 32; ++j)
+#if KVO_MUTANT == 7
+        w |= (uint64_t)(n[j] >> 4) << (hb_bits * (j ^ 1));   /* planted: high bits of pairs swapped */
+#else
+        w |= (uint64_t)(n[j] >> 4) << (hb_bits * j);
+#endif
+    int nbytes = 4 * hb_bits;
+    for (int k = 0; k < nbytes; ++k) hi[nbytes * b + k] = (uint8_t)(w >> (8 * k));
+}
+
+/* Code of element i of a row (low nibble plus high bits). */
+static int unpack_code(int type, const uint8_t* row, int D, int i)
+{
+    int b = i / 32, e = i % 32;
+    uint8_t byte = row[16 * b + (e % 16)];
+    int n = e < 16 ? (byte & 0x0f) : (byte >> 4);
+    if (type == KVO_Q5_0 || type == KVO_Q5_1) {
+        const uint8_t* hi = row + D / 2 + 4 * b;
+        n |= ((hi[e / 8] >> (e % 8)) & 1) << 4;
+    } else if (type == KVO_Q6_0) {
+        const uint8_t* hi = row + D / 2 + 8 * b;
+        n |= ((hi[e / 4] >> (2 * (e % 4))) & 3) << 4;
+    }
+    return n;
+}
+
+static int is_quant_type(int type)
+{
+    return type == KVO_Q8_0 || type == KVO_Q4_0 || type == KVO_Q4_1 || type == KVO_Q5_0 ||
+           type == KVO_Q5_1 || type == KVO_Q6_0;
+}
+
+/* fp16 entries of the scale plane per block: 2 for the min/max types. */
+static int scales_per_block(int type)
+{
+    return type == KVO_Q4_1 || type == KVO_Q5_1 ? 2 : type == KVO_F16 ? 0 : 1;
+}
+
+/* Bytes of the data plane per row of D values, and of the scale plane
+ * (0 for an unknown type). */
 int64_t kvo_data_row_bytes(int type, int D)
 {
-    return type == KVO_F16 ? 2 * (int64_t)D : type == KVO_Q8_0 ? D : D / 2;
+    switch (type) {
+    case KVO_F16: return 2 * (int64_t)D;
+    case KVO_Q8_0: return D;
+    case KVO_Q4_0:
+    case KVO_Q4_1: return D / 2;
+    case KVO_Q5_0:
+    case KVO_Q5_1: return D / 2 + D / 8;
+    case KVO_Q6_0: return D / 2 + D / 4;
+    default: return 0;
+    }
 }
 int64_t kvo_scale_row_bytes(int type, int D)
 {
-    return type == KVO_F16 ? 0 : 2 * (int64_t)(D / 32);
+    return is_quant_type(type) ? 2 * (int64_t)scales_per_block(type) * (D / 32) : 0;
 }
 
 /* Quantise nrows rows of D f16 values (D a multiple of 32) into a data plane
- * (nrows x data_row_bytes) and a scale plane (nrows x D/32 fp16), or copy the
- * f16 bits unchanged for the f16 type.  Returns 0, or -1 on bad arguments. */
+ * (nrows x data_row_bytes) and a scale plane (nrows x scale_row_bytes / 2
+ * fp16), or copy the f16 bits unchanged for the f16 type.  Returns 0, or -1
+ * on bad arguments. */
 int kvo_quantize_rows(int type, const uint16_t* src, int64_t nrows, int D,
                       uint8_t* data, uint16_t* scales)
 {
@@ -204,6 +354,23 @@ int kvo_quantize_rows(int type, const uint16_t* src, int64_t nrows, int D,
             for (int b = 0; b < nb; ++b)
                 quant_block_q4_0(x + 32 * b, data + r * (D / 2) + 16 * b,
                                  scales + r * nb + b);
+        } else if (type == KVO_Q5_0 || type == KVO_Q6_0) {
+            int bits = type == KVO_Q5_0 ? 5 : 6;
+            uint8_t* row = data + r * kvo_data_row_bytes(type, D);
+            for (int b = 0; b < nb; ++b) {
+                int n[32];
+                quant_codes_sym(x + 32 * b, bits, n, scales + r * nb + b);
+                pack_codes(n, bits - 4, row, row + D / 2, b);
+            }
+        } else if (type == KVO_Q4_1 || type == KVO_Q5_1) {
+            int levels = type == KVO_Q4_1 ? 15 : 31;
+            uint8_t* row = data + r * kvo_data_row_bytes(type, D);
+            for (int b = 0; b < nb; ++b) {
+                int n[32];
+                uint16_t* sc = scales + r * 2 * nb + 2 * b;
+                quant_codes_minmax(x + 32 * b, levels, n, sc, sc + 1);
+                pack_codes(n, type == KVO_Q4_1 ? 0 : 1, row, row + D / 2, b);
+            }
         } else {
             return -1;
         }
@@ -222,6 +389,18 @@ static double deq(int type, const uint8_t* data, const uint16_t* scales,
         uint16_t h;
         memcpy(&h, data + (r * D + i) * 2, 2);
         return kvo_f16_value(h);
+    }
+    if (type != KVO_Q8_0 && type != KVO_Q4_0) {
+        const uint8_t* row = data + r * kvo_data_row_bytes(type, D);
+        int n = unpack_code(type, row, D, i);
+        int spb = scales_per_block(type);
+        const uint16_t* sc = scales + r * spb * (D / 32) + spb * (i / 32);
+        double ds = kvo_f16_value(sc[0]);
+        switch (type) {
+        case KVO_Q5_0: return ds * (double)(n - 16);
+        case KVO_Q6_0: return ds * (double)(n - 32);
+        default: return ds * (double)n + kvo_f16_value(sc[1]);   /* q4_1, q5_1 */
+        }
     }
     double d = kvo_f16_value(scales[r * (D / 32) + i / 32]);
     if (type == KVO_Q8_0) {
@@ -245,7 +424,7 @@ int kvo_dequant_rows(int type, const uint8_t* data, const uint16_t* scales,
                      int64_t nrows, int D, double* out)
 {
     if (D <= 0 || D % 32 != 0 || nrows < 0) return -1;
-    if (type != KVO_F16 && type != KVO_Q8_0 && type != KVO_Q4_0) return -1;
+    if (type != KVO_F16 && !is_quant_type(type)) return -1;
     for (int64_t r = 0; r < nrows; ++r)
         for (int i = 0; i < D; ++i)
             out[r * D + i] = deq(type, data, scales, r, D, i);

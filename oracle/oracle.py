@@ -20,7 +20,9 @@ SRC = os.path.join(HERE, "kvq_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 F16, Q8_0, Q4_0 = 0, 1, 2
-TYPE_NAMES = {"f16": F16, "q8_0": Q8_0, "q4_0": Q4_0}
+Q4_1, Q5_0, Q5_1, Q6_0 = 4, 5, 6, 7
+TYPE_NAMES = {"f16": F16, "q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1, "q5_0": Q5_0, "q5_1": Q5_1,
+              "q6_0": Q6_0}
 
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-pthread",
           "-std=c11", "-Wall", "-Wextra", "-Wno-missing-field-initializers"]
@@ -102,7 +104,8 @@ def scale_row_bytes(t, D: int, lib=None) -> int:
 
 def quantize(t, x_f16: np.ndarray, lib=None):
     """Quantise rows of fp16 values.  ``x_f16``: (..., D) float16 or uint16 bits.
-    Returns (data uint8 (..., data_row_bytes), scales uint16 (..., D/32)); the
+    Returns (data uint8 (..., data_row_bytes), scales uint16 (..., scale_row_bytes
+    / 2): D/32 scales, or D/32 (scale, minimum) pairs for q4_1 / q5_1); the
     scale plane is an empty last axis for the f16 type."""
     lib = lib or load()
     t = _tcode(t)
@@ -111,7 +114,7 @@ def quantize(t, x_f16: np.ndarray, lib=None):
     lead = x.shape[:-1]
     n = int(np.prod(lead, dtype=np.int64)) if lead else 1
     data = np.zeros(lead + (data_row_bytes(t, D, lib),), np.uint8)
-    scales = np.zeros(lead + (max(D // 32, 1) if t != F16 else 0,), np.uint16)
+    scales = np.zeros(lead + (scale_row_bytes(t, D, lib) // 2,), np.uint16)
     sc = scales if t != F16 else np.zeros(1, np.uint16)
     rc = lib.kvo_quantize_rows(t, _ptr(x), n, D, _ptr(data), _ptr(sc))
     if rc != 0:

@@ -10,6 +10,7 @@ from oracle import brute
 from oracle import oracle as O
 
 from .test_oracle_quant import WORKED
+from .test_oracle_quant_n3 import BITS, LEVELS, WORKED as WORKED_N3
 
 MUTANTS = {
     1: "round half to even",
@@ -17,6 +18,9 @@ MUTANTS = {
     3: "q4_0 signed maximum taken at the last index on ties",
     4: "q4_0 nibbles packed as adjacent pairs",
     5: "combine drops the last split",
+    6: "q4_1 / q5_1 divide by the unrounded binary32 scale",
+    7: "q5 / q6 high bits of adjacent elements swapped",
+    8: "q5_0 / q6_0 clamp one level too high",
 }
 
 
@@ -60,7 +64,34 @@ def split_combine_matches(lib) -> bool:
     return bool(np.allclose(out, ref, atol=1e-12) and np.allclose(lse, ref_lse, atol=1e-12))
 
 
-BATTERY = [worked_blocks_pass, brute_agrees, split_combine_matches]
+def n3_worked_blocks_pass(lib) -> bool:
+    for _, t, x, scales, data in WORKED_N3:
+        d, s = O.quantize(t, x[None, :], lib=lib)
+        if [int(v) for v in s[0]] != scales or d[0].tobytes() != data:
+            return False
+    return True
+
+
+def n3_brute_agrees(lib) -> bool:
+    rng = np.random.default_rng(23)
+    x = np.concatenate([rng.standard_normal((100, 32)), 2 + rng.random((100, 32)),
+                        rng.integers(-20, 20, (100, 32)) / 8.0]).astype(np.float16).view(np.uint16)
+    for t in ("q4_1", "q5_0", "q5_1", "q6_0"):
+        data, scales = O.quantize(t, x, lib=lib)
+        for i in range(x.shape[0]):
+            bits = [int(v) for v in x[i]]
+            if t in BITS:
+                d16, n = brute.quant_sym(bits, BITS[t])
+                sc = [d16]
+            else:
+                d16, m16, n = brute.quant_minmax(bits, LEVELS[t])
+                sc = [d16, m16]
+            if [int(v) for v in scales[i]] != sc or brute.pack_row(t, [n]) != data[i].tobytes():
+                return False
+    return True
+
+
+BATTERY = [worked_blocks_pass, brute_agrees, split_combine_matches, n3_worked_blocks_pass, n3_brute_agrees]
 
 
 def test_unmutated_oracle_passes_battery():
