@@ -42,8 +42,20 @@ extern "C" {
 typedef enum {
     KVQ_F16 = 0,  /* IEEE binary16 values, 2*D bytes per row, no scale plane   */
     KVQ_Q8_0 = 1, /* per 32-value block: 32 int8 codes + one fp16 scale        */
-    KVQ_Q4_0 = 2  /* per 32-value block: 32 codes in [0,15] (value = code - 8),
+    KVQ_Q4_0 = 2, /* per 32-value block: 32 codes in [0,15] (value = code - 8),
                      packed two per byte, + one fp16 scale                     */
+    /* Further scalar types of the pages' served pairs (HAL #582 section 1 size
+     * table and section 5; block sizes 20, 22, 24 and 26 bytes per 32 values).
+     * A row's data plane holds the low 4 bits of every code (D/2 bytes, block
+     * b at 16*b, byte j = code j | code j+16 << 4), then for q5 / q6 every
+     * block's high bits (a little-endian 32-bit word per block, bit j = bit 4
+     * of code j; or a 64-bit word, bits 2j and 2j+1 = bits 4 and 5).  Rows of
+     * these types are 4-byte aligned.  The value 3 is not a storage type (it
+     * names fp32 output, KVQ_OUT_F32). */
+    KVQ_Q4_1 = 4, /* codes in [0,15], value = d * code + m; scales d, m        */
+    KVQ_Q5_0 = 5, /* codes in [0,31], value = d * (code - 16); scale d         */
+    KVQ_Q5_1 = 6, /* codes in [0,31], value = d * code + m; scales d, m        */
+    KVQ_Q6_0 = 7  /* codes in [0,63], value = d * (code - 32); scale d         */
 } kvq_type;
 
 /* Status codes (negative = error, nothing was enqueued). */
@@ -74,8 +86,13 @@ enum {
  *                bytes [32b, 32b+32).  q4_0: D/2 bytes, block b at bytes
  *                [16b, 16b+16); byte j of a block holds the code of element j
  *                in its low nibble and of element j+16 in its high nibble.
- *   scale plane: rows of D/32 binary16 scales (scale of block b at index b);
- *                unused (may be NULL) for f16.
+ *                q4_1: as q4_0.  q5_0, q5_1: the q4_0 bytes of the low
+ *                nibbles, then D/8 bytes of high bits (block b's 32-bit word
+ *                at D/2 + 4b).  q6_0: the low nibbles, then D/4 bytes (block
+ *                b's 64-bit word at D/2 + 8b).
+ *   scale plane: rows of D/32 binary16 scales (scale of block b at index b),
+ *                or for q4_1 / q5_1 D/16 entries (block b: scale at 2b,
+ *                minimum at 2b+1); unused (may be NULL) for f16.
  * Row t of KV head g of sequence b is row index
  *     b * seq_stride_rows + g * head_stride_rows + t
  * in both planes; rows t in [0, capacity) are addressable.  The usual layout
@@ -91,11 +108,13 @@ typedef struct {
     int64_t head_stride_rows; /* rows between KV heads of one sequence      */
 } kvq_plane_desc;
 
-/* Bytes of one data-plane row: 2*D (f16), D (q8_0), D/2 (q4_0); 0 for an
- * unknown type or a D that is not a positive multiple of 32. */
+/* Bytes of one data-plane row: 2*D (f16), D (q8_0), D/2 (q4_0, q4_1),
+ * 5*D/8 (q5_0, q5_1), 3*D/4 (q6_0); 0 for an unknown type or a D that is not
+ * a positive multiple of 32. */
 size_t kvq_data_row_bytes(int type, int head_dim);
 
-/* Bytes of one scale-plane row: 0 (f16), D/16 (q8_0, q4_0); 0 when invalid. */
+/* Bytes of one scale-plane row: 0 (f16), D/16 (q8_0, q4_0, q5_0, q6_0), D/8
+ * (q4_1, q5_1); 0 when invalid. */
 size_t kvq_scale_row_bytes(int type, int head_dim);
 
 /*
@@ -107,8 +126,7 @@ size_t kvq_scale_row_bytes(int type, int head_dim);
  *   KVQ_TIER_Q8_Q8   q8_0 / q8_0
  *   KVQ_TIER_Q8_Q4   q8_0 / q4_0
  *   KVQ_TIER_Q51_Q4  q5_1 / q4_0   (the last resort; q5_1 blocks are 24 bytes
- *                    per 32 values -- a size this library counts but does not
- *                    store: kvq_tier_types reports KVQ_ERR_TYPE for it)
+ *                    per 32 values)
  */
 enum { KVQ_TIER_F16 = 0, KVQ_TIER_Q8_Q8 = 1, KVQ_TIER_Q8_Q4 = 2, KVQ_TIER_Q51_Q4 = 3 };
 
@@ -132,8 +150,8 @@ int kvq_select_kv_tier(int64_t n_ctx, int n_layers, int Hkv, int D, int64_t free
                        int64_t resident_bytes, int64_t vram_target_bytes, int64_t* budget_bytes,
                        int64_t* cache_bytes);
 
-/* K and V storage types of a tier; KVQ_ERR_TYPE for KVQ_TIER_Q51_Q4 and
- * unknown tiers (types not written). */
+/* K and V storage types of a tier; KVQ_ERR_TYPE for an unknown tier (types
+ * not written). */
 int kvq_tier_types(int tier, int* type_k, int* type_v);
 
 /* Static, human-readable name of a status code. */
@@ -154,6 +172,12 @@ const char* kvq_status_string(int status);
  *   q4_0: s = the x_i of largest magnitude (lowest i on ties, +0 if none);
  *         d = fp16_rne(s / -8); code_i = clamp(round_half_away(x_i / d),
  *         -8, 7) + 8; all codes 8 when d == 0.
+ *   q5_0, q6_0: as q4_0 with -16 / -32 in place of -8: code_i =
+ *         clamp(round_half_away(x_i / d), -16, 15) + 16 or (-32, 31) + 32.
+ *   q4_1, q5_1: m = fp16(min_i x_i) (exact), d = fp16_rne((max_i x_i -
+ *         min_i x_i) / 15 or 31) (binary32 subtraction and division);
+ *         code_i = clamp(round_half_away((x_i - m) / d), 0, 15 or 31) with
+ *         the stored m and d; all codes 0 when d == 0.
  *   f16 : the bits are copied unchanged.
  * Inputs of the quantised types must be finite: a block holding an infinity
  * or a NaN gets unspecified codes (the method defines none).

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(PKG, "libkvq.so")
 
 F16, Q8_0, Q4_0 = 0, 1, 2
 OUT_F32 = 3
-TYPES = {"f16": F16, "q8_0": Q8_0, "q4_0": Q4_0}
+Q4_1, Q5_0, Q5_1, Q6_0 = 4, 5, 6, 7
+TYPES = {"f16": F16, "q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1, "q5_0": Q5_0, "q5_1": Q5_1, "q6_0": Q6_0}
 VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
 VARIANTS = {"auto": VARIANT_AUTO, "valu": VARIANT_VALU, "mfma": VARIANT_MFMA}
 SPLIT_GRANULE = 64

@@ -4,7 +4,7 @@ here: every step of the decode path runs in the library's HIP kernels.
 
 Layout (matches kvq_plane_desc): for cache tensor X of one layer,
     data   : uint8  [B, Hkv, capacity, data_row_bytes(type, D)]
-    scales : int16  [B, Hkv, capacity, D / 32]      (absent for f16)
+    scales : int16  [B, Hkv, capacity, scale_row_bytes(type, D) / 2]   (absent for f16)
 so row t of KV head g of sequence b is row (b * Hkv + g) * capacity + t.
 """
 from __future__ import annotations
@@ -36,7 +36,8 @@ class CachePlanes:
         data = torch.empty((B, Hkv, capacity, rb), dtype=torch.uint8, device=device)
         scales = None
         if t != _lib.F16:
-            scales = torch.empty((B, Hkv, capacity, D // 32), dtype=torch.int16, device=device)
+            ns = _lib.kvq_scale_row_bytes(t, D) // 2
+            scales = torch.empty((B, Hkv, capacity, ns), dtype=torch.int16, device=device)
         return cls(t, B, Hkv, capacity, D, data, scales)
 
     def desc(self) -> _lib.kvq_plane_desc:

@@ -1055,6 +1055,9 @@ bool supports1(const DecodeArgs& a)
 
 bool decode_mfma_supports(const DecodeArgs& a)
 {
+    // the matrix-core kernel is built for f16, q8_0 and q4_0 rows
+    auto built = [](int t) { return t == T_F16 || t == T_Q8 || t == T_Q4; };
+    if (!built(a.tk) || !built(a.tv)) return false;
     if (a.D != 128 && a.D != 256 && a.D != 512) return false;
     if (a.G < 1 || a.nq < 1 || a.nq * a.G > 16) return false;
     // rows read are below max_seq_len; their offsets inside one (sequence,

@@ -62,13 +62,13 @@ __global__ void __launch_bounds__(NT) decode_valu_kernel(DecodeArgs a)
     if (tid < GP) { mrun[tid] = -INFINITY; lrun[tid] = 0.0f; }
 
     const int rbK = data_row_bytes(TK, D), rbV = data_row_bytes(TV, D);
-    const int nb = D >> 5;
+    const int nsK = (D >> 5) * scales_per_block(TK), nsV = (D >> 5) * scales_per_block(TV);
     const int64_t krow0 = (int64_t)b * a.k.seq_stride + (int64_t)g * a.k.head_stride;
     const int64_t vrow0 = (int64_t)b * a.v.seq_stride + (int64_t)g * a.v.head_stride;
     const uint8_t* kdata = a.k.data + krow0 * rbK;
-    const uint16_t* kscl = a.k.scales + krow0 * nb;
+    const uint16_t* kscl = a.k.scales + krow0 * nsK;
     const uint8_t* vdata = a.v.data + vrow0 * rbV;
-    const uint16_t* vscl = a.v.scales + vrow0 * nb;
+    const uint16_t* vscl = a.v.scales + vrow0 * nsV;
 
     // QK mapping: row = tid / 4, quarter = tid % 4
     const int qk_row = tid >> 2, qk_part = tid & 3;
@@ -96,10 +96,10 @@ __global__ void __launch_bounds__(NT) decode_valu_kernel(DecodeArgs a)
             const int t = t0 + qk_row;
             if (qk_row < nt) {
                 const uint8_t* row = kdata + (int64_t)t * rbK;
-                const uint16_t* srow = kscl + (int64_t)t * nb;
+                const uint16_t* srow = kscl + (int64_t)t * nsK;
                 for (int e = qk_e0; e < qk_e1; e += 8) {
                     float kv[8];
-                    load8<TK>(row, srow, e, kv);
+                    load8<TK>(row, srow, e, D, kv);
 #pragma unroll
                     for (int h = 0; h < GP; ++h) {
                         if (h < G) {
@@ -152,7 +152,7 @@ __global__ void __launch_bounds__(NT) decode_valu_kernel(DecodeArgs a)
             for (int r = pv_g; r < nt; r += NG) {
                 const int t = t0 + r;
                 float vv[8];
-                load8<TV>(vdata + (int64_t)t * rbV, vscl + (int64_t)t * nb, pv_c * 8, vv);
+                load8<TV>(vdata + (int64_t)t * rbV, vscl + (int64_t)t * nsV, pv_c * 8, D, vv);
 #pragma unroll
                 for (int h = 0; h < GP; ++h) {
                     if (h < G) {
@@ -210,18 +210,29 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s)
     switch (a.tv) {
     case T_F16: return launch_tv<TK, T_F16>(a, s);
     case T_Q8: return launch_tv<TK, T_Q8>(a, s);
-    default: return launch_tv<TK, T_Q4>(a, s);
+    case T_Q4: return launch_tv<TK, T_Q4>(a, s);
+    case T_Q4_1: return launch_tv<TK, T_Q4_1>(a, s);
+    case T_Q5_0: return launch_tv<TK, T_Q5_0>(a, s);
+    case T_Q5_1: return launch_tv<TK, T_Q5_1>(a, s);
+    case T_Q6_0: return launch_tv<TK, T_Q6_0>(a, s);
+    default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
+// Every pair of storage types (K and V chosen independently).
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t s)
 {
     switch (a.tk) {
     case T_F16: return launch_t<T_F16>(a, s);
     case T_Q8: return launch_t<T_Q8>(a, s);
-    default: return launch_t<T_Q4>(a, s);
+    case T_Q4: return launch_t<T_Q4>(a, s);
+    case T_Q4_1: return launch_t<T_Q4_1>(a, s);
+    case T_Q5_0: return launch_t<T_Q5_0>(a, s);
+    case T_Q5_1: return launch_t<T_Q5_1>(a, s);
+    case T_Q6_0: return launch_t<T_Q6_0>(a, s);
+    default: return hipErrorInvalidValue;
     }
 }
 

@@ -10,7 +10,7 @@
 
 namespace {
 
-bool known_type(int t) { return t == KVQ_F16 || t == KVQ_Q8_0 || t == KVQ_Q4_0; }
+bool known_type(int t) { return kvq::valid_type(t); }
 
 bool valid_head_dim(int D) { return D >= 32 && D <= KVQ_MAX_HEAD_DIM && D % 32 == 0; }
 
@@ -105,7 +105,7 @@ size_t kvq_data_row_bytes(int type, int head_dim)
 size_t kvq_scale_row_bytes(int type, int head_dim)
 {
     if (!known_type(type) || head_dim <= 0 || head_dim % 32 != 0) return 0;
-    return type == KVQ_F16 ? 0 : (size_t)(head_dim / 16);
+    return (size_t)(2 * kvq::scales_per_block(type) * (head_dim / 32));
 }
 
 int64_t kvq_tier_cache_bytes(int tier, int64_t n_ctx, int n_layers, int Hkv, int D)
@@ -152,6 +152,7 @@ int kvq_tier_types(int tier, int* type_k, int* type_v)
     case KVQ_TIER_F16: tk = KVQ_F16; tv = KVQ_F16; break;
     case KVQ_TIER_Q8_Q8: tk = KVQ_Q8_0; tv = KVQ_Q8_0; break;
     case KVQ_TIER_Q8_Q4: tk = KVQ_Q8_0; tv = KVQ_Q4_0; break;
+    case KVQ_TIER_Q51_Q4: tk = KVQ_Q5_1; tv = KVQ_Q4_0; break;
     default: return KVQ_ERR_TYPE;
     }
     if (type_k) *type_k = tk;

@@ -7,12 +7,33 @@
 
 namespace kvq {
 
-enum : int { T_F16 = 0, T_Q8 = 1, T_Q4 = 2 };
+// Storage types.  f16, q8_0 and q4_0 are the pages' tiers; q4_1, q5_0, q5_1
+// and q6_0 are the further scalar types of their served pairs (block sizes 20,
+// 22, 24 and 26 bytes per 32 values).
+enum : int { T_F16 = 0, T_Q8 = 1, T_Q4 = 2, T_Q4_1 = 4, T_Q5_0 = 5, T_Q5_1 = 6, T_Q6_0 = 7 };
 
-// Bytes of one data-plane row of D values.
+__host__ __device__ constexpr bool valid_type(int t)
+{
+    return t == T_F16 || t == T_Q8 || t == T_Q4 || t == T_Q4_1 || t == T_Q5_0 || t == T_Q5_1 ||
+           t == T_Q6_0;
+}
+
+// Bytes of one data-plane row of D values: the low nibbles of every block
+// (D/2 bytes) and then, for q5 / q6, every block's high bits (4 or 8 bytes).
 __host__ __device__ constexpr int data_row_bytes(int t, int D)
 {
-    return t == T_F16 ? 2 * D : (t == T_Q8 ? D : D / 2);
+    return t == T_F16 ? 2 * D
+         : t == T_Q8 ? D
+         : (t == T_Q5_0 || t == T_Q5_1) ? D / 2 + D / 8
+         : t == T_Q6_0 ? D / 2 + D / 4
+         : D / 2;
+}
+
+// fp16 entries of the scale plane per 32-value block: the scale d, and for
+// q4_1 / q5_1 the block minimum m after it.
+__host__ __device__ constexpr int scales_per_block(int t)
+{
+    return t == T_F16 ? 0 : (t == T_Q4_1 || t == T_Q5_1) ? 2 : 1;
 }
 
 // Device view of one cache tensor: row index of (sequence b, KV head g, row t)
@@ -50,12 +71,13 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-// Eight consecutive elements [e, e + 8) of a stored row, dequantised to fp32
-// (code * scale is exact in fp32: an 11-bit scale times an integer of at most
-// 8 bits).  `row` points at the row's first data byte, `srow` at its scales.
-// e must be a multiple of 8.
+// Eight consecutive elements [e, e + 8) of a stored row of D values,
+// dequantised to fp32 (code * scale is exact in fp32: an 11-bit scale times an
+// integer of at most 8 bits; the minimum of q4_1 / q5_1 is added with one
+// rounding).  `row` points at the row's first data byte, `srow` at its
+// scales.  e must be a multiple of 8.
 template <int T>
-__device__ __forceinline__ void load8(const uint8_t* row, const uint16_t* srow, int e, float* out)
+__device__ __forceinline__ void load8(const uint8_t* row, const uint16_t* srow, int e, int D, float* out)
 {
     if constexpr (T == T_F16) {
         uint4 u = *reinterpret_cast<const uint4*>(row + 2 * e);
@@ -74,7 +96,7 @@ __device__ __forceinline__ void load8(const uint8_t* row, const uint16_t* srow, 
             int8_t c = (int8_t)((w[i >> 2] >> (8 * (i & 3))) & 0xff);
             out[i] = d * (float)c;
         }
-    } else {
+    } else if constexpr (T == T_Q4) {
         const int blk = e >> 5, p = e & 31;
         uint2 u = *reinterpret_cast<const uint2*>(row + 16 * blk + (p & 15));
         const float d = h2f(srow[blk]);
@@ -84,6 +106,32 @@ __device__ __forceinline__ void load8(const uint8_t* row, const uint16_t* srow, 
         for (int i = 0; i < 8; ++i) {
             int c = (int)((w[i >> 2] >> (8 * (i & 3) + sh)) & 0xf) - 8;
             out[i] = d * (float)c;
+        }
+    } else {
+        // q4_1, q5_0, q5_1, q6_0: low nibbles as q4_0, high bits after all
+        // blocks' nibbles (rows of these types are only 4-byte aligned)
+        const int blk = e >> 5, p = e & 31;
+        const uint32_t* lo = reinterpret_cast<const uint32_t*>(row + 16 * blk + (p & 15));
+        const uint32_t w[2] = {lo[0], lo[1]};
+        const int sh = p < 16 ? 0 : 4;
+        uint64_t hb = 0;
+        if constexpr (T == T_Q5_0 || T == T_Q5_1)
+            hb = *reinterpret_cast<const uint32_t*>(row + D / 2 + 4 * blk) >> p;
+        if constexpr (T == T_Q6_0) {
+            const uint32_t* h = reinterpret_cast<const uint32_t*>(row + D / 2 + 8 * blk);
+            hb = ((uint64_t)h[0] | ((uint64_t)h[1] << 32)) >> (2 * p);
+        }
+        constexpr int HB = (T == T_Q5_0 || T == T_Q5_1) ? 1 : T == T_Q6_0 ? 2 : 0;
+        constexpr int SPB = scales_per_block(T);
+        const float d = h2f(srow[SPB * blk]);
+        const float m = SPB == 2 ? h2f(srow[SPB * blk + 1]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int c = (int)((w[i >> 2] >> (8 * (i & 3) + sh)) & 0xf);
+            if constexpr (HB > 0) c |= (int)((hb >> (HB * i)) & ((1u << HB) - 1)) << 4;
+            if constexpr (T == T_Q5_0) out[i] = d * (float)(c - 16);
+            else if constexpr (T == T_Q6_0) out[i] = d * (float)(c - 32);
+            else out[i] = fmaf(d, (float)c, m);
         }
     }
 }

@@ -102,6 +102,110 @@ __device__ __forceinline__ void quantize_block(const uint16_t* __restrict__ src,
     }
 }
 
+// The further scalar types (q4_1, q5_0, q5_1, q6_0): block blk of a row of D
+// values.  The low nibbles go to row[16*blk ..], the high bits to the word of
+// block blk after all the row's nibbles (row[D/2 + 4*blk] for q5, row[D/2 +
+// 8*blk] for q6), the scale (and minimum) to srow[scales_per_block * blk ..].
+//   q5_0 / q6_0: d = fp16(s / -16 or -32), s the first value of largest
+//     magnitude; code = clamp(round_half_away(x / d), -16..15 / -32..31) +
+//     16 / + 32 (d = 0: every code the offset).
+//   q4_1 / q5_1: m = fp16(min x) (exact: the inputs are fp16), d =
+//     fp16((max x - min x) / 15 or 31); code = clamp(round_half_away((x - m) /
+//     d), 0, 15 or 31) (d = 0: code 0).
+// Binary32 subtraction and division throughout, as the block formats' fixed
+// quantiser prescribes; the minimum and maximum are taken in index order with
+// strict comparisons, so a block mixing +0 and -0 keeps the first one seen.
+template <int T>
+__device__ __forceinline__ void quantize_block_ext(const uint16_t* __restrict__ src, uint8_t* __restrict__ row,
+                                                   uint16_t* __restrict__ srow, int blk, int D)
+{
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 r = reinterpret_cast<const uint4*>(src)[i];
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[8 * i + 2 * j] = h2f((uint16_t)(w[j] & 0xffff));
+            x[8 * i + 2 * j + 1] = h2f((uint16_t)(w[j] >> 16));
+        }
+    }
+    int n[32];
+    if constexpr (T == T_Q5_0 || T == T_Q6_0) {
+        constexpr int HALF = T == T_Q5_0 ? 16 : 32;
+        float amax = 0.0f, smax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const float a = fabsf(x[i]);
+            if (a > amax) { amax = a; smax = x[i]; }
+        }
+        // smax / -HALF as magnitude and sign (|smax| / HALF is exact in
+        // binary32; see the q4_0 scale above for why it is not a product
+        // with -1/HALF)
+        const uint16_t mag16 = f2h_rne(fabsf(smax) * (1.0f / HALF));
+        const uint16_t d16 = (uint16_t)(mag16 | (smax < 0.0f ? 0 : 0x8000));
+        const float d = h2f(d16);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            if (d != 0.0f) {
+                float r = roundf(x[i] / d);
+                r = fminf(fmaxf(r, -(float)HALF), (float)(HALF - 1));
+                n[i] = (int)r + HALF;
+            } else {
+                n[i] = HALF;
+            }
+        }
+        srow[blk] = d16;
+    } else {
+        constexpr float LEVELS = T == T_Q4_1 ? 15.0f : 31.0f;
+        float mn = x[0], mx = x[0];
+#pragma unroll
+        for (int i = 1; i < 32; ++i) {
+            if (x[i] < mn) mn = x[i];
+            if (x[i] > mx) mx = x[i];
+        }
+        const uint16_t d16 = f2h_rne((mx - mn) / LEVELS);
+        const uint16_t m16 = f2h_rne(mn);
+        const float d = h2f(d16), m = h2f(m16);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            if (d != 0.0f) {
+                float r = roundf((x[i] - m) / d);
+                r = fminf(fmaxf(r, 0.0f), LEVELS);
+                n[i] = (int)r;
+            } else {
+                n[i] = 0;
+            }
+        }
+        srow[2 * blk] = d16;
+        srow[2 * blk + 1] = m16;
+    }
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        w[j >> 2] |= (uint32_t)((n[j] & 15) | ((n[j + 16] & 15) << 4)) << (8 * (j & 3));
+    // rows of these types are 4-byte aligned: dword stores
+    uint32_t* lo = reinterpret_cast<uint32_t*>(row + 16 * blk);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) lo[k] = w[k];
+    if constexpr (T == T_Q5_0 || T == T_Q5_1) {
+        uint32_t h = 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) h |= (uint32_t)(n[j] >> 4) << j;
+        *reinterpret_cast<uint32_t*>(row + D / 2 + 4 * blk) = h;
+    } else if constexpr (T == T_Q6_0) {
+        uint32_t h0 = 0, h1 = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            h0 |= (uint32_t)(n[j] >> 4) << (2 * j);
+            h1 |= (uint32_t)(n[j + 16] >> 4) << (2 * j);
+        }
+        uint32_t* h = reinterpret_cast<uint32_t*>(row + D / 2 + 8 * blk);
+        h[0] = h0;
+        h[1] = h1;
+    }
+}
+
 // The same block quantiser with one lane per value: the 32 lanes of an
 // aligned half-wave (j = lane & 31) quantise the block at src together, with
 // the block maximum found by cross-lane exchanges.  Every lane performs the

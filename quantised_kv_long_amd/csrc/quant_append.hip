@@ -35,14 +35,17 @@ __global__ void __launch_bounds__(256) quantize_append_kernel(AppendArgs a)
     const int pos0 = a.positions ? a.positions[b] : a.seq_lens[b] - a.n_new;
     if (pos0 + r < 0) return;  // a sequence shorter than its new rows: nothing before row 0
     const int64_t row = (int64_t)b * P.seq_stride + (int64_t)g * P.head_stride + pos0 + r;
-    uint8_t* dst = P.data + row * data_row_bytes(t, a.D) + (int64_t)blk * data_row_bytes(t, 32);
-    uint16_t* sdst = P.scales + row * nb + blk;
-    if (t == T_F16)
-        quantize_block<T_F16>(src, dst, sdst);
-    else if (t == T_Q8)
-        quantize_block<T_Q8>(src, dst, sdst);
-    else
-        quantize_block<T_Q4>(src, dst, sdst);
+    uint8_t* rowp = P.data + row * data_row_bytes(t, a.D);
+    uint16_t* srow = P.scales + row * nb * scales_per_block(t);
+    switch (t) {
+    case T_F16: quantize_block<T_F16>(src, rowp + 64 * blk, nullptr); break;
+    case T_Q8: quantize_block<T_Q8>(src, rowp + 32 * blk, srow + blk); break;
+    case T_Q4: quantize_block<T_Q4>(src, rowp + 16 * blk, srow + blk); break;
+    case T_Q4_1: quantize_block_ext<T_Q4_1>(src, rowp, srow, blk, a.D); break;
+    case T_Q5_0: quantize_block_ext<T_Q5_0>(src, rowp, srow, blk, a.D); break;
+    case T_Q5_1: quantize_block_ext<T_Q5_1>(src, rowp, srow, blk, a.D); break;
+    default: quantize_block_ext<T_Q6_0>(src, rowp, srow, blk, a.D); break;
+    }
 }
 
 }  // namespace

@@ -58,11 +58,11 @@ def oracle_planes(t, x_u16: np.ndarray, capacity: int | None = None):
     with zero rows to `capacity`: (type name, data, scales) on the host."""
     B, Hkv, L, D = x_u16.shape
     cap = capacity or L
-    name = t if isinstance(t, str) else {0: "f16", 1: "q8_0", 2: "q4_0"}[t]
+    name = t if isinstance(t, str) else {v: k for k, v in O.TYPE_NAMES.items()}[t]
     data, sc = oracle_quantize(name, x_u16.reshape(B * Hkv, L, D))
     rb = data.shape[-1]
     d = np.zeros((B, Hkv, cap, rb), np.uint8)
-    s = np.zeros((B, Hkv, cap, D // 32 if name != "f16" else 0), np.uint16)
+    s = np.zeros((B, Hkv, cap, O.scale_row_bytes(name, D) // 2), np.uint16)
     d[:, :, :L] = data.reshape(B, Hkv, L, rb)
     s[:, :, :L] = sc.reshape(B, Hkv, L, -1)
     return (name, d, s)
@@ -85,7 +85,7 @@ def planes_to_oracle(p: C.CachePlanes):
 
 def upload_oracle_planes(name: str, data: np.ndarray, scales: np.ndarray) -> C.CachePlanes:
     B, Hkv, cap, _ = data.shape
-    D = scales.shape[-1] * 32 if name != "f16" else data.shape[-1] // 2
+    D = scales.shape[-1] * 32 // (O.scale_row_bytes(name, 32) // 2) if name != "f16" else data.shape[-1] // 2
     p = C.CachePlanes.alloc(name, B, Hkv, cap, D)
     p.data.copy_(torch.from_numpy(np.ascontiguousarray(data)))
     if p.scales is not None:

@@ -59,8 +59,22 @@ def test_row_bytes(lib):
         assert _lib.kvq_scale_row_bytes("f16", D) == 0
         assert _lib.kvq_scale_row_bytes("q8_0", D) == D // 16
         assert _lib.kvq_scale_row_bytes("q4_0", D) == D // 16
+        assert _lib.kvq_data_row_bytes("q4_1", D) == D // 2
+        assert _lib.kvq_data_row_bytes("q5_0", D) == _lib.kvq_data_row_bytes("q5_1", D) == 5 * D // 8
+        assert _lib.kvq_data_row_bytes("q6_0", D) == 3 * D // 4
+        assert _lib.kvq_scale_row_bytes("q5_0", D) == _lib.kvq_scale_row_bytes("q6_0", D) == D // 16
+        assert _lib.kvq_scale_row_bytes("q4_1", D) == _lib.kvq_scale_row_bytes("q5_1", D) == D // 8
     assert _lib.kvq_data_row_bytes("q8_0", 48) == 0
-    assert _lib.kvq_data_row_bytes(7, 128) == 0
+    assert _lib.kvq_data_row_bytes(3, 128) == 0
+    assert _lib.kvq_data_row_bytes(8, 128) == 0
+
+
+def test_row_bytes_agree_with_the_oracle():
+    from oracle import oracle as O
+    for t in ("f16", "q8_0", "q4_0", "q4_1", "q5_0", "q5_1", "q6_0"):
+        for D in (32, 128, 512):
+            assert _lib.kvq_data_row_bytes(t, D) == O.data_row_bytes(t, D)
+            assert _lib.kvq_scale_row_bytes(t, D) == O.scale_row_bytes(t, D)
 
 
 @pytest.mark.parametrize("layers,heads,D,tK,tV,tokens,value,unit,cite", ROWS,
@@ -157,7 +171,8 @@ def test_decode_validation(lib):
     assert decode(lib, D=1024) == -2
     assert decode(lib, scale=float("nan")) == -2
     assert decode(lib, max_len=0) == -2
-    assert decode(lib, k=plane(t=5)) == -3
+    assert decode(lib, k=plane(t=8)) == -3
+    assert decode(lib, k=plane(t=3)) == -3                      # 3 names fp32 output, not a storage type
     assert decode(lib, variant=3) == -3
     assert decode(lib, q=A + 4) == -4
     assert decode(lib, po=A + 4) == -4
@@ -206,7 +221,7 @@ def test_decode_step_validation(lib):
     assert step(lib, po=None) == -1
     assert step(lib, Hq=41) == -2
     assert step(lib, D=1024) == -2
-    assert step(lib, k=plane(t=5)) == -3
+    assert step(lib, k=plane(t=8)) == -3
     assert step(lib, max_len=101) == -5
     assert step(lib, split=100) == -6
     # and the step's own arguments

@@ -76,8 +76,9 @@ def test_tier_types_and_errors(lib):
     assert _lib.kvq_tier_types(0) == (_lib.F16, _lib.F16)
     assert _lib.kvq_tier_types(1) == (_lib.Q8_0, _lib.Q8_0)
     assert _lib.kvq_tier_types(2) == (_lib.Q8_0, _lib.Q4_0)
+    assert _lib.kvq_tier_types(3) == (_lib.Q5_1, _lib.Q4_0)
     with pytest.raises(_lib.KVQError):
-        _lib.kvq_tier_types(3)          # q5_1 is counted, not stored, here
+        _lib.kvq_tier_types(4)
     assert _lib.kvq_tier_cache_bytes(4, 1, 1, 1, 128) == -1
     assert _lib.kvq_tier_cache_bytes(0, 1, 1, 1, 100) == -1
     assert lib.kvq_select_kv_tier(0, 48, 8, 128, 1, 0, 0, None, None) == -2
