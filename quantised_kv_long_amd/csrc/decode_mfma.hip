@@ -105,6 +105,14 @@ __device__ __forceinline__ half8 q8_sub8(uint32_t w0, uint32_t w1)
                       __builtin_amdgcn_perm(u1, u1, 0x0C010C00u), __builtin_amdgcn_perm(u1, u1, 0x0C030C02u));
 }
 
+// 8 unsigned bytes (two dwords) as fp16 subnormals of byte * 2^-24, in byte
+// order.
+__device__ __forceinline__ half8 u8_sub8(uint32_t w0, uint32_t w1)
+{
+    return make_half8(__builtin_amdgcn_perm(w0, w0, 0x0C010C00u), __builtin_amdgcn_perm(w0, w0, 0x0C030C02u),
+                      __builtin_amdgcn_perm(w1, w1, 0x0C010C00u), __builtin_amdgcn_perm(w1, w1, 0x0C030C02u));
+}
+
 // 4x4 exchange between the four 16-lane rows: on entry lane row g holds
 // x[w] = X[g][w]; on exit it holds x[w] = X[w][g].
 __device__ __forceinline__ void xpose4(uint32_t& r0, uint32_t& r1, uint32_t& r2, uint32_t& r3)
@@ -157,29 +165,55 @@ struct Cfg {
     static constexpr int RBV = rb(TV, DW);
     static constexpr int RBK_ROW = rb(TK, D);      // bytes of a row (row stride)
     static constexpr int RBV_ROW = rb(TV, D);
-    static constexpr int KU = TK == T_Q4 ? 1 : (TK == T_Q8 ? 2 : 4);   // dwords per lane per block
-    static constexpr int KDW = 4 * KU * NBG;                           // K dwords per lane per subtile
-    static constexpr int V_BYTES = TT * RBV;                           // V tile bytes (slice)
-    static constexpr int V_LOADS = V_BYTES / 1024;                     // 16-byte loads per lane
-    static constexpr int V_DW = 4 * V_LOADS;
+    // storage-type traits: 4-bit low codes (the q4_0 family), high bits per
+    // code (q5: 1, q6: 2, after all of a row's nibbles), a block minimum (q4_1,
+    // q5_1: value = d * code + m), fp16 scale-plane entries per block
+    static constexpr bool KNIB = TK == T_Q4 || TK == T_Q4_1 || TK == T_Q5_0 || TK == T_Q5_1 || TK == T_Q6_0;
+    static constexpr int KHB = (TK == T_Q5_0 || TK == T_Q5_1) ? 1 : (TK == T_Q6_0 ? 2 : 0);
+    static constexpr bool KMIN = TK == T_Q4_1 || TK == T_Q5_1;
+    static constexpr int SPBK = scales_per_block(TK);
+    static constexpr int VHB = (TV == T_Q5_0 || TV == T_Q5_1) ? 1 : (TV == T_Q6_0 ? 2 : 0);
+    static constexpr bool VMIN = TV == T_Q4_1 || TV == T_Q5_1;
+    static constexpr int SPBV = scales_per_block(TV);
+    // V rows of the further types (q4_1, q5_0, q5_1, q6_0) are staged in LDS
+    // as one unsigned code byte per value and take the byte route of PV
+    static constexpr bool VBYTES = TV == T_Q4_1 || TV == T_Q5_0 || TV == T_Q5_1 || TV == T_Q6_0;
+    static constexpr bool NEWT = VBYTES || TK == T_Q4_1 || TK == T_Q5_0 || TK == T_Q5_1 || TK == T_Q6_0;
+    static constexpr int RBV_LDS = VBYTES ? DW : RBV;                  // LDS bytes of a V row (slice)
+    static constexpr int KU = KNIB ? 1 : (TK == T_Q8 ? 2 : 4);         // dwords per lane per block
+    static constexpr int KDW = 4 * KU * NBG;                           // K code dwords per lane per subtile
+    static constexpr int KHW = KHB * NB;                               // K high-bit dwords of a row
+    static constexpr int BBK = KNIB ? 16 : RBK / NB;                   // code bytes of a block (K row)
+    static constexpr int V_BYTES = TT * RBV_LDS;                       // V tile bytes in LDS (slice)
+    static constexpr int V_LOADS = VBYTES ? 0 : V_BYTES / 1024;        // 16-byte loads per lane
+    // byte route: one (row, block) unit per lane and load: 16 nibble bytes
+    // plus the block's high-bit words
+    static constexpr int V_UNITS = VBYTES ? TT * NB / 64 : 0;
+    static constexpr int V_DW = VBYTES ? V_UNITS * (4 + VHB) : 4 * V_LOADS;
     static constexpr int K_SCALE = TK != T_F16;
     static constexpr int V_SCALE = TV != T_F16;
-    static constexpr int S_BYTES = TT * 2 * NB;                        // one scale tile (slice)
-    static constexpr int S_LOADS = S_BYTES / 256;                      // 4-byte loads per lane
-    static constexpr int S_DW = (K_SCALE + V_SCALE) * S_LOADS > 0 ? (K_SCALE + V_SCALE) * S_LOADS : 1;
+    static constexpr int SK_BYTES = TT * 2 * NB * SPBK;                // K scale tile (slice)
+    static constexpr int SV_BYTES = TT * 2 * NB * SPBV;
+    static constexpr int SK_LOADS = SK_BYTES / 256;                    // 4-byte loads per lane
+    static constexpr int SV_LOADS = SV_BYTES / 256;
+    static constexpr int S_DW = SK_LOADS + SV_LOADS > 0 ? SK_LOADS + SV_LOADS : 1;
     static constexpr int KS_OFF = V_BYTES;
-    static constexpr int VS_OFF = V_BYTES + S_BYTES * K_SCALE;
-    static constexpr int BUF = V_BYTES + S_BYTES * (K_SCALE + V_SCALE);
+    static constexpr int VS_OFF = V_BYTES + SK_BYTES;
+    static constexpr int BUF = V_BYTES + SK_BYTES + SV_BYTES;
     static constexpr int NDT = DW / 16;                                // PV output tiles
     // register sets of the load ring: two for 128-column slices (a third,
     // where it fits in 256 registers, measured slower), one for 256 and for
     // f16 rows of a 512-wide head (their registers do not fit twice)
     static constexpr int NSET = DW == 128 && (DS == 1 || (TK != T_F16 && TV != T_F16)) ? 2 : 1;
     static constexpr int SX_FLOATS = DS > 1 ? 2 * WAVES * 64 * 8 : 1;  // partial-score exchange
-    static constexpr float KOFF = TK == T_Q4 ? 8.0f : (TK == T_Q8 ? 128.0f : 0.0f);
-    static constexpr uint32_t VOFF_BITS = TV == T_Q4 ? 0x00080008u : 0x00800080u;
-    static constexpr bool VALID = V_BYTES % 1024 == 0 && S_BYTES % 256 == 0 && V_DW <= (DW == 128 ? 32 : 64) &&
-                                  WAVES * BUF <= 64 * 1024;
+    static constexpr float KOFF = TK == T_Q4 ? 8.0f : TK == T_Q8 ? 128.0f : TK == T_Q5_0 ? 16.0f
+                                : TK == T_Q6_0 ? 32.0f : 0.0f;
+    // the V code offset as an fp16 subnormal pair (0: no offset, min types)
+    static constexpr uint32_t VOFF_BITS = TV == T_Q4 ? 0x00080008u : TV == T_Q8 ? 0x00800080u
+                                        : TV == T_Q5_0 ? 0x00100010u : TV == T_Q6_0 ? 0x00200020u : 0u;
+    static constexpr bool VALID = V_BYTES % 1024 == 0 && SK_BYTES % 256 == 0 && SV_BYTES % 256 == 0 &&
+                                  (!VBYTES || (TT * NB) % 64 == 0) && V_DW <= (DW == 128 ? 32 : 64) &&
+                                  WAVES * BUF <= 64 * 1024 && (!NEWT || (D == 128 && DS == 1));
 };
 
 // Bytes of the four-wave merge area: per wave and score column the running
@@ -203,6 +237,18 @@ __host__ __device__ constexpr size_t merge_lds_bytes(int nc)
 // merge area otherwise).
 // MQ: several query tokens per sequence (a.nq > 1); a separate instance, so
 // that the single-token kernels carry none of its per-column index arithmetic
+// One 32-value block of a new row, quantised by the 32 lanes of an aligned
+// half-wave (j = lane & 31) into row `row` of plane P (a row of D values).
+template <int T, int D>
+__device__ __forceinline__ void write_block_lanes_d(const uint16_t* src, const Plane& P, int64_t row, int blk, int j)
+{
+    if constexpr (T == T_F16 || T == T_Q8 || T == T_Q4)
+        quantize_block_lanes<T>(src, P.data + row * rb(T, D) + blk * rb(T, 32), P.scales + row * (D / 32) + blk, j);
+    else
+        quantize_block_ext_lanes<T>(src, P.data + row * rb(T, D), P.scales + row * (D / 32) * scales_per_block(T),
+                                    blk, D, j);
+}
+
 template <int TK, int TV, int D, bool MQ>
 __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint8_t* const lds_a,
                                           const size_t lds_cap, float* const lds_sx,
@@ -238,9 +284,11 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     const int64_t vrow0 = (int64_t)b * a.v.seq_stride + (int64_t)g * a.v.head_stride;
     const int wsl = C::DS > 1 ? wave : 0;          // this wave's head-dim slice
     const uint8_t* kdata = a.k.data + krow0 * C::RBK_ROW + wsl * C::RBK;
-    const uint8_t* kscl = reinterpret_cast<const uint8_t*>(a.k.scales + krow0 * C::NB_ROW + wsl * C::NB);
+    const uint8_t* kscl =
+        reinterpret_cast<const uint8_t*>(a.k.scales + (krow0 * C::NB_ROW + wsl * C::NB) * C::SPBK);
     const uint8_t* vdata = a.v.data + vrow0 * C::RBV_ROW + wsl * C::RBV;
-    const uint8_t* vscl = reinterpret_cast<const uint8_t*>(a.v.scales + vrow0 * C::NB_ROW + wsl * C::NB);
+    const uint8_t* vscl =
+        reinterpret_cast<const uint8_t*>(a.v.scales + (vrow0 * C::NB_ROW + wsl * C::NB) * C::SPBV);
 
     // ---- decode step with the new tokens: the workgroup whose split holds
     //      row L-1 (multi-query: each workgroup whose split holds some of the
@@ -262,13 +310,8 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
                 const uint16_t* src =
                     (isv ? a.v_new : a.k_new) + (((int64_t)b * NQ + i) * a.Hkv + g) * D + 32 * blk;
                 const int64_t row = (isv ? vrow0 : krow0) + r;
-                if (isv) {
-                    quantize_block_lanes<TV>(src, a.v.data + row * C::RBV_ROW + blk * rb(TV, 32),
-                                             a.v.scales + row * C::NB_ROW + blk, tid & 31);
-                } else {
-                    quantize_block_lanes<TK>(src, a.k.data + row * C::RBK_ROW + blk * rb(TK, 32),
-                                             a.k.scales + row * C::NB_ROW + blk, tid & 31);
-                }
+                if (isv) write_block_lanes_d<TV, D>(src, a.v, row, blk, tid & 31);
+                else write_block_lanes_d<TK, D>(src, a.k, row, blk, tid & 31);
             }
             __builtin_amdgcn_s_waitcnt(VMCNT0);
             __syncthreads();
@@ -280,13 +323,8 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
             const int blk = isv ? blk2 - C::NB_ROW : blk2;
             const uint16_t* src = (isv ? a.v_new : a.k_new) + ((int64_t)b * a.Hkv + g) * D + 32 * blk;
             const int64_t row = (isv ? vrow0 : krow0) + (L - 1);
-            if (isv) {
-                quantize_block_lanes<TV>(src, a.v.data + row * C::RBV_ROW + blk * rb(TV, 32),
-                                         a.v.scales + row * C::NB_ROW + blk, tid & 31);
-            } else {
-                quantize_block_lanes<TK>(src, a.k.data + row * C::RBK_ROW + blk * rb(TK, 32),
-                                         a.k.scales + row * C::NB_ROW + blk, tid & 31);
-            }
+            if (isv) write_block_lanes_d<TV, D>(src, a.v, row, blk, tid & 31);
+            else write_block_lanes_d<TK, D>(src, a.k, row, blk, tid & 31);
         }
         // the row is read back only by this workgroup, whose loads of that
         // tile are issued after the barrier: the stores must be complete
@@ -301,6 +339,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     //      4*lq + {0, 2, 16, 18, 1, 3, 17, 19}, the nibble order of one dword)
     half8 qop[C::NB];
     floatx4 kbias[C::NB];
+    float kmq[C::KMIN ? C::NB : 1];
     // (run after the first tiles' loads are issued, so they overlap)
     auto init_q = [&]() {
         const int c = min(ln, NC - 1);
@@ -310,7 +349,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
 #pragma unroll
         for (int kb = 0; kb < C::NB; ++kb) {
             uint32_t w[4];
-            if constexpr (TK == T_Q4) {
+            if constexpr (C::KNIB) {
                 const u32x2 ra = *reinterpret_cast<const u32x2*>(qh + 32 * kb + 4 * lq);
                 const u32x2 rb = *reinterpret_cast<const u32x2*>(qh + 32 * kb + 4 * lq + 16);
                 w[0] = __builtin_amdgcn_perm((uint32_t)ra[1], (uint32_t)ra[0], 0x05040100u);
@@ -330,8 +369,12 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
             }
             qop[kb] = make_half8(w[0], w[1], w[2], w[3]);
             // the accumulator's start removes the code offset exactly once
-            const float bias = -C::KOFF * TWOM24 * xsum4(part);
+            const float qsum = xsum4(part);
+            const float bias = -C::KOFF * TWOM24 * qsum;
             kbias[kb] = floatx4{bias, bias, bias, bias};
+            // block minimum m: the score gains m * sum(q over the block), in
+            // the MFMA sums' units (2^-24)
+            if constexpr (C::KMIN) kmq[kb] = qsum * TWOM24;
         }
     };
 
@@ -365,13 +408,15 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     //   q8_0 / q4_0: 16-byte loads stay coalesced: lane row lq loads the whole
     //   of block 4*bg + lq (BB bytes), and a 4x4 exchange between lane rows
     //   (xpose4) then gives each lane row its quarter of every block.
+    //   q5 / q6 high bits: every lane loads its row's high-bit words whole.
     constexpr int QB = 4 * C::KU;                  // bytes of a block quarter
-    constexpr int BB = C::RBK / C::NB;             // bytes of a block
+    constexpr int BB = C::BBK;                     // code bytes of a block
     constexpr bool KDIRECT = C::KU == 4;
+    constexpr int KR = C::KDW + C::KHW;            // K dwords per lane and row
     const int krow_rel0 = 8 * (ln >> 2) + (ln & 3);
     const uint32_t kpart = (uint32_t)(lq * (KDIRECT ? QB : BB));
-    const uint32_t klane0 = (uint32_t)(krow_rel0 * C::RBK_ROW) + kpart;
-    const uint32_t klane1 = (uint32_t)((krow_rel0 + 4) * C::RBK_ROW) + kpart;
+    const uint32_t krow0o = (uint32_t)(krow_rel0 * C::RBK_ROW);
+    const uint32_t krow1o = (uint32_t)((krow_rel0 + 4) * C::RBK_ROW);
     // V row chunks and scale words of a tile: 16-byte chunk k*64 + lane of the
     // slice is row c16 / (RBV/16), column c16 % (RBV/16); scale word k*64 +
     // lane is row c4 / (NB/2), word c4 % (NB/2)
@@ -381,14 +426,19 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
         if constexpr (C::DS == 1) return (uint32_t)(16 * lane + 1024 * k);
         else return (uint32_t)((c16 / (C::RBV / 16)) * C::RBV_ROW + 16 * (c16 % (C::RBV / 16)));
     };
-    auto soff = [&](int k) -> uint32_t {
-        const int c4 = k * 64 + lane;
-        if constexpr (C::DS == 1) return (uint32_t)(4 * lane + 256 * k);
-        else return (uint32_t)((c4 / (C::NB / 2)) * (2 * C::NB_ROW) + 4 * (c4 % (C::NB / 2)));
-    };
 
-    // one K row's share of this lane (p: the row start plus kpart)
-    auto load_k_row = [&](const uint8_t* p, uint32_t (&x)[C::KDW]) {
+    // one K row's share of this lane (rowp: the row start)
+    auto load_k_row = [&](const uint8_t* rowp, uint32_t (&x)[KR]) {
+        const uint8_t* p = rowp + kpart;
+        if constexpr (C::KHB > 0) {
+            // the row's high-bit words, after its D/2 nibble bytes
+#pragma unroll
+            for (int u = 0; u < C::KHW / 4; ++u) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(rowp + C::DW / 2 + 16 * u);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) x[C::KDW + 4 * u + c] = v[c];
+            }
+        }
         if constexpr (KDIRECT) {
 #pragma unroll
             for (int kb = 0; kb < C::NB; ++kb) {
@@ -414,23 +464,99 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     //      below L is one contiguous range per plane, addressed as a uniform
     //      tile base plus a per-lane offset; only a split's last tile clamps
     //      its rows to L - 1 (rows past L are masked out of the softmax).
-    auto issue_k = [&](int it, uint32_t (&kr)[2][C::KDW]) {
+    auto issue_k = [&](int it, uint32_t (&kr)[2][KR]) {
         const int t0 = t_begin + it * TT;
         if (t0 + TT <= L) {
             const uint8_t* base = kdata + (uint32_t)(t0 * C::RBK_ROW);
-            load_k_row(base + klane0, kr[0]);
-            load_k_row(base + klane1, kr[1]);
+            load_k_row(base + krow0o, kr[0]);
+            load_k_row(base + krow1o, kr[1]);
         } else {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int tok = min(t0 + krow_rel0 + 4 * j, L - 1);
-                load_k_row(kdata + (uint32_t)(tok * C::RBK_ROW) + kpart, kr[j]);
+                load_k_row(kdata + (uint32_t)(tok * C::RBK_ROW), kr[j]);
             }
+        }
+    };
+    // scale words of a tile: the K and V scale planes have SPBK / SPBV fp16
+    // entries per block (scale, then minimum), so a row of the slice has
+    // NB * SPB / 2 words; word k*64 + lane of a plane's tile is row c4 / (NB *
+    // SPB / 2), word c4 % (NB * SPB / 2)
+    // (full: every row of the tile lies below L)
+    auto load_scales = [&](int t0, bool full, const uint8_t* scl, int spb, uint32_t* dst, int nloads) {
+        const int wpr = C::NB * spb / 2;           // words per row (slice)
+        const int wpr_row = C::NB_ROW * spb / 2;   // words per row (whole row)
+        if (full) {
+            const uint32_t sbase = (uint32_t)(t0 * (4 * wpr_row));
+#pragma unroll
+            for (int k = 0; k < nloads; ++k) {
+                const int c4 = k * 64 + lane;
+                const uint32_t o = C::DS == 1 ? (uint32_t)(4 * c4)
+                                              : (uint32_t)((c4 / wpr) * (4 * wpr_row) + 4 * (c4 % wpr));
+                dst[k] = *reinterpret_cast<const uint32_t*>(scl + sbase + o);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < nloads; ++k) {
+                const int c4 = k * 64 + lane;
+                const int tok = min(t0 + c4 / wpr, L - 1);
+                dst[k] = *reinterpret_cast<const uint32_t*>(scl + (uint32_t)(tok * (4 * wpr_row)) +
+                                                            4 * (c4 % wpr));
+            }
+        }
+    };
+    auto load_all_scales = [&](int t0, bool full, uint32_t (&sr)[C::S_DW]) {
+        if constexpr (C::K_SCALE && C::V_SCALE && C::SPBK == C::SPBV) {
+            // both planes alike: one loop, K and V words interleaved
+            const int wpr = C::NB * C::SPBK / 2, wpr_row = C::NB_ROW * C::SPBK / 2;
+            if (full) {
+                const uint32_t sbase = (uint32_t)(t0 * (4 * wpr_row));
+#pragma unroll
+                for (int k = 0; k < C::SK_LOADS; ++k) {
+                    const int c4 = k * 64 + lane;
+                    const uint32_t o = C::DS == 1 ? (uint32_t)(4 * c4)
+                                                  : (uint32_t)((c4 / wpr) * (4 * wpr_row) + 4 * (c4 % wpr));
+                    sr[k] = *reinterpret_cast<const uint32_t*>(kscl + sbase + o);
+                    sr[C::SK_LOADS + k] = *reinterpret_cast<const uint32_t*>(vscl + sbase + o);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < C::SK_LOADS; ++k) {
+                    const int c4 = k * 64 + lane;
+                    const int tok = min(t0 + c4 / wpr, L - 1);
+                    const uint32_t off = (uint32_t)(tok * (4 * wpr_row)) + 4 * (c4 % wpr);
+                    sr[k] = *reinterpret_cast<const uint32_t*>(kscl + off);
+                    sr[C::SK_LOADS + k] = *reinterpret_cast<const uint32_t*>(vscl + off);
+                }
+            }
+        } else {
+            if constexpr (C::K_SCALE) load_scales(t0, full, kscl, C::SPBK, sr, C::SK_LOADS);
+            if constexpr (C::V_SCALE) load_scales(t0, full, vscl, C::SPBV, sr + C::SK_LOADS, C::SV_LOADS);
         }
     };
     auto issue_vs = [&](int it, uint32_t (&vr)[C::V_DW], uint32_t (&sr)[C::S_DW]) {
         const int t0 = t_begin + it * TT;
-        if (t0 + TT <= L) {
+        if constexpr (C::VBYTES) {
+            // unit k*64 + lane = (row u / NB, block u % NB): its 16 nibble
+            // bytes and its high-bit words
+#pragma unroll
+            for (int k = 0; k < C::V_UNITS; ++k) {
+                const int u = k * 64 + lane;
+                const int tok = min(t0 + u / C::NB, L - 1);
+                const uint8_t* rowp = vdata + (uint32_t)(tok * C::RBV_ROW);
+                const u32x4 v = *reinterpret_cast<const u32x4*>(rowp + 16 * (u % C::NB));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) vr[k * (4 + C::VHB) + c] = v[c];
+                if constexpr (C::VHB == 1) {
+                    vr[k * 5 + 4] = *reinterpret_cast<const uint32_t*>(rowp + C::DW / 2 + 4 * (u % C::NB));
+                } else if constexpr (C::VHB == 2) {
+                    const u32x2 h = *reinterpret_cast<const u32x2*>(rowp + C::DW / 2 + 8 * (u % C::NB));
+                    vr[k * 6 + 4] = h[0];
+                    vr[k * 6 + 5] = h[1];
+                }
+            }
+            load_all_scales(t0, t0 + TT <= L, sr);
+        } else if (t0 + TT <= L) {
             const uint8_t* vbase = vdata + (uint32_t)(t0 * C::RBV_ROW);
 #pragma unroll
             for (int k = 0; k < C::V_LOADS; ++k) {
@@ -438,14 +564,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
 #pragma unroll
                 for (int c = 0; c < 4; ++c) vr[4 * k + c] = v[c];
             }
-            const uint32_t sbase = (uint32_t)(t0 * (2 * C::NB_ROW));
-#pragma unroll
-            for (int k = 0; k < C::S_LOADS; ++k) {
-                if constexpr (C::K_SCALE) sr[k] = *reinterpret_cast<const uint32_t*>(kscl + sbase + soff(k));
-                if constexpr (C::V_SCALE)
-                    sr[C::K_SCALE * C::S_LOADS + k] =
-                        *reinterpret_cast<const uint32_t*>(vscl + sbase + soff(k));
-            }
+            load_all_scales(t0, true, sr);
         } else {
 #pragma unroll
             for (int k = 0; k < C::V_LOADS; ++k) {
@@ -456,48 +575,81 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
 #pragma unroll
                 for (int c = 0; c < 4; ++c) vr[4 * k + c] = v[c];
             }
+            load_all_scales(t0, false, sr);
+        }
+    };
+
+    // one (row, block) unit of a further type as 32 unsigned code bytes
+    // (element j at byte j): the low nibbles (byte j of the block holds
+    // elements j and j+16), plus the high bits moved to bit 4 of each byte
+    auto unit_bytes = [&](const uint32_t* x, uint32_t (&o)[8]) {
 #pragma unroll
-            for (int k = 0; k < C::S_LOADS; ++k) {
-                const int c4 = k * 64 + lane;
-                const int tok = min(t0 + c4 / (C::NB / 2), L - 1);
-                const uint32_t off = (uint32_t)(tok * (2 * C::NB_ROW)) + 4 * (c4 % (C::NB / 2));
-                if constexpr (C::K_SCALE) sr[k] = *reinterpret_cast<const uint32_t*>(kscl + off);
-                if constexpr (C::V_SCALE)
-                    sr[C::K_SCALE * C::S_LOADS + k] = *reinterpret_cast<const uint32_t*>(vscl + off);
+        for (int m = 0; m < 4; ++m) {
+            o[m] = x[m] & 0x0F0F0F0Fu;               // elements 4m .. 4m+3
+            o[m + 4] = (x[m] >> 4) & 0x0F0F0F0Fu;    // elements 16+4m .. 16+4m+3
+        }
+        if constexpr (C::VHB == 1) {
+            // bit e of the word is bit 4 of element e: four bits to the four
+            // bytes' bit 4 (the multiply spreads 4 bits 8 apart, no carries)
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const uint32_t f = __builtin_amdgcn_ubfe(x[4], 4 * m, 4);
+                o[m] |= ((f * 0x00204081u) & 0x01010101u) << 4;
+            }
+        } else if constexpr (C::VHB == 2) {
+            // bits 2e, 2e+1 of the 64-bit word are bits 4, 5 of element e:
+            // the two-bit fields of four elements go to bits 4-5 of the four
+            // bytes (even and odd fields spread separately, no carries)
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const uint32_t f = __builtin_amdgcn_ubfe(x[4 + (m >> 2)], 8 * (m & 3), 8);
+                const uint32_t ev = ((f & 0x33u) * 0x1001u) & 0x00030003u;          // fields 0, 2 -> 0, 16
+                const uint32_t od = (((f >> 2) & 0x33u) * 0x1001u) & 0x00030003u;   // fields 1, 3 -> 0, 16
+                o[m] |= (ev | (od << 8)) << 4;
             }
         }
     };
 
-    // ---- copy the staged V rows (natural order, [32 rows][row bytes]) and the
-    //      scale rows (transposed to [block][32 rows]) to the wave's LDS buffer
+    // ---- copy the staged V rows (natural order, [32 rows][row bytes]; the
+    //      further types as code bytes) and the scale rows (transposed to
+    //      [entry][32 rows], entry = block * SPB + (0: scale, 1: minimum)) to
+    //      the wave's LDS buffer
+    auto stage_scales = [&](const uint32_t* src, int spb, int nloads, uint16_t* st) {
+        const int wpr = C::NB * spb / 2;
+        for (int k = 0; k < nloads; ++k) {
+            const int c4 = k * 64 + lane;
+            const int tok = c4 / wpr, e = 2 * (c4 % wpr);
+            st[e * TT + tok] = (uint16_t)(src[k] & 0xffff);
+            st[(e + 1) * TT + tok] = (uint16_t)(src[k] >> 16);
+        }
+    };
     auto stage = [&](const uint32_t (&vr)[C::V_DW], const uint32_t (&sr)[C::S_DW]) {
         uint8_t* vb = wbuf;
+        if constexpr (C::VBYTES) {
 #pragma unroll
-        for (int k = 0; k < C::V_LOADS; ++k) {
-            const u32x4 v = {vr[4 * k], vr[4 * k + 1], vr[4 * k + 2], vr[4 * k + 3]};
-            *reinterpret_cast<u32x4*>(vb + 1024 * k + 16 * lane) = v;
-        }
-#pragma unroll
-        for (int k = 0; k < C::S_LOADS; ++k) {
-            const int c4 = k * 64 + lane;
-            const int tok = c4 / (C::NB / 2), blk = 2 * (c4 % (C::NB / 2));
-            if constexpr (C::K_SCALE) {
-                const uint32_t w = sr[k];
-                uint16_t* st = reinterpret_cast<uint16_t*>(vb + C::KS_OFF);
-                st[blk * TT + tok] = (uint16_t)(w & 0xffff);
-                st[(blk + 1) * TT + tok] = (uint16_t)(w >> 16);
+            for (int k = 0; k < C::V_UNITS; ++k) {
+                const int u = k * 64 + lane;
+                uint32_t o[8];
+                unit_bytes(vr + k * (4 + C::VHB), o);
+                uint8_t* dst = vb + (u / C::NB) * C::RBV_LDS + 32 * (u % C::NB);
+                *reinterpret_cast<u32x4*>(dst) = u32x4{o[0], o[1], o[2], o[3]};
+                *reinterpret_cast<u32x4*>(dst + 16) = u32x4{o[4], o[5], o[6], o[7]};
             }
-            if constexpr (C::V_SCALE) {
-                const uint32_t w = sr[C::K_SCALE * C::S_LOADS + k];
-                uint16_t* st = reinterpret_cast<uint16_t*>(vb + C::VS_OFF);
-                st[blk * TT + tok] = (uint16_t)(w & 0xffff);
-                st[(blk + 1) * TT + tok] = (uint16_t)(w >> 16);
+        } else {
+#pragma unroll
+            for (int k = 0; k < C::V_LOADS; ++k) {
+                const u32x4 v = {vr[4 * k], vr[4 * k + 1], vr[4 * k + 2], vr[4 * k + 3]};
+                *reinterpret_cast<u32x4*>(vb + 1024 * k + 16 * lane) = v;
             }
         }
+        if constexpr (C::K_SCALE)
+            stage_scales(sr, C::SPBK, C::SK_LOADS, reinterpret_cast<uint16_t*>(vb + C::KS_OFF));
+        if constexpr (C::V_SCALE)
+            stage_scales(sr + C::SK_LOADS, C::SPBV, C::SV_LOADS, reinterpret_cast<uint16_t*>(vb + C::VS_OFF));
     };
 
     // ---- compute tile `it` whose K rows are in kr and V rows / scales in LDS
-    auto compute = [&](int it, uint32_t (&kr)[2][C::KDW], int next_it) {
+    auto compute = [&](int it, uint32_t (&kr)[2][KR], int next_it) {
         const int t0 = t_begin + it * TT;
         const uint8_t* vb = wbuf;
         const uint16_t* kst = reinterpret_cast<const uint16_t*>(vb + C::KS_OFF);
@@ -530,9 +682,37 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
                     const int kb = 4 * bg + kb4;
                     const uint32_t* q = x + bg * 4 * C::KU + kb4 * C::KU;
                     half8 av;
-                    if constexpr (TK == T_Q4) av = q4_sub8(q[0]);
-                    else if constexpr (TK == T_Q8) av = q8_sub8(q[0], q[1]);
-                    else av = make_half8(q[0], q[1], q[2], q[3]);
+                    if constexpr (C::KHB > 0) {
+                        // nibble pair k of the dword is elements (e0_k, e1_k) of
+                        // quarter lq: e0 = 4lq + {0, 16, 1, 17}[k], e1 = e0 + 2;
+                        // their high bits go to bits 4 and 20 (bit 4 of each half)
+                        const uint32_t w = q[0];
+                        uint32_t d[4];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const int e0 = 4 * lq + ((k & 1) ? 16 : 0) + (k >> 1);
+                            uint32_t h0, h1;
+                            if constexpr (C::KHB == 1) {
+                                const uint32_t hw = x[C::KDW + kb];
+                                h0 = __builtin_amdgcn_ubfe(hw, e0, 1);
+                                h1 = __builtin_amdgcn_ubfe(hw, e0 + 2, 1);
+                            } else {
+                                // element e's two bits are bits 2e, 2e+1 of the
+                                // block's 64-bit word (e0, e0 + 2 in one half)
+                                const uint32_t hw = x[C::KDW + 2 * kb + (e0 >> 4)];
+                                h0 = __builtin_amdgcn_ubfe(hw, 2 * (e0 & 15), 2);
+                                h1 = __builtin_amdgcn_ubfe(hw, 2 * ((e0 + 2) & 15), 2);
+                            }
+                            d[k] = ((w >> (4 * k)) & 0x000F000Fu) | (h0 << 4) | (h1 << 20);
+                        }
+                        av = make_half8(d[0], d[1], d[2], d[3]);
+                    } else if constexpr (C::KNIB) {
+                        av = q4_sub8(q[0]);
+                    } else if constexpr (TK == T_Q8) {
+                        av = q8_sub8(q[0], q[1]);
+                    } else {
+                        av = make_half8(q[0], q[1], q[2], q[3]);
+                    }
                     cb[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qop[kb], kbias[kb], 0, 0, 0);
                 }
             }
@@ -542,7 +722,8 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
                 // contiguous fp16 values per block in the transposed tile
 #pragma unroll
                 for (int kb = 0; kb < C::NB; ++kb) {
-                    const u32x2 sw = *reinterpret_cast<const u32x2*>(kst + kb * TT + 8 * lq + 4 * j);
+                    const u32x2 sw =
+                        *reinterpret_cast<const u32x2*>(kst + (kb * C::SPBK) * TT + 8 * lq + 4 * j);
                     // the element is copied out first: hipcc (clang) bit-casts
                     // a vector-element lvalue from the vector's first element
                     const half2v s01 = __builtin_bit_cast(half2v, (uint32_t)sw[0]);
@@ -551,6 +732,17 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
                     sc[1] = fmaf(cb[kb][1], (float)s01[1], sc[1]);
                     sc[2] = fmaf(cb[kb][2], (float)s23[0], sc[2]);
                     sc[3] = fmaf(cb[kb][3], (float)s23[1], sc[3]);
+                    if constexpr (C::KMIN) {
+                        // + m * sum(q over the block), m of each row
+                        const u32x2 mw =
+                            *reinterpret_cast<const u32x2*>(kst + (kb * 2 + 1) * TT + 8 * lq + 4 * j);
+                        const half2v m01 = __builtin_bit_cast(half2v, (uint32_t)mw[0]);
+                        const half2v m23 = __builtin_bit_cast(half2v, (uint32_t)mw[1]);
+                        sc[0] = fmaf((float)m01[0], kmq[kb], sc[0]);
+                        sc[1] = fmaf((float)m01[1], kmq[kb], sc[1]);
+                        sc[2] = fmaf((float)m23[0], kmq[kb], sc[2]);
+                        sc[3] = fmaf((float)m23[1], kmq[kb], sc[3]);
+                    }
                 }
             } else {
 #pragma unroll
@@ -627,7 +819,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
         // P' for block kb: p times the V scale of each of this lane row's
         // rows 8*lq + e (eight contiguous fp16 values of the transposed tile)
         auto pscaled = [&](int kb) -> half8 {
-            const u32x4 sv4 = *reinterpret_cast<const u32x4*>(vst + kb * TT + 8 * lq);
+            const u32x4 sv4 = *reinterpret_cast<const u32x4*>(vst + (kb * C::SPBV) * TT + 8 * lq);
             return make_half8(pk_mul_h(pp[0], sv4[0]), pk_mul_h(pp[1], sv4[1]),
                               pk_mul_h(pp[2], sv4[2]), pk_mul_h(pp[3], sv4[3]));
         };
@@ -655,11 +847,12 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
                                                                          oacc[2 * c2 + 1], 0, 0, 0);
                 bacc[c2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(voff, bv, bacc[c2], 0, 0, 0);
             }
-        } else if constexpr (TV == T_Q8) {
+        } else if constexpr (TV == T_Q8 || C::VBYTES) {
             // column tile t = chunks 2t, 2t+1; lane r addresses row 8*lq + r/2,
-            // chunk 2t + (r&1)
+            // chunk 2t + (r&1).  q8_0: signed bytes (+128 for the subnormal
+            // codes); the further types: unsigned code bytes
             const int r = ln;
-            const LDS_AS uint8_t* tbase = vl + (8 * lq + (r >> 1)) * C::RBV + 8 * (r & 1);
+            const LDS_AS uint8_t* tbase = vl + (8 * lq + (r >> 1)) * C::RBV_LDS + 8 * (r & 1);
 #pragma unroll
             for (int kb = 0; kb < C::NB; ++kb) {
                 const half8 bv = pscaled(kb);
@@ -667,10 +860,23 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
                 for (int h = 0; h < 2; ++h) {
                     const int t = 2 * kb + h;
                     const int2v w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS int2v*)(tbase + 16 * t));
-                    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(q8_sub8((uint32_t)w[0], (uint32_t)w[1]),
-                                                                    bv, oacc[t], 0, 0, 0);
+                    const half8 av = C::VBYTES ? u8_sub8((uint32_t)w[0], (uint32_t)w[1])
+                                               : q8_sub8((uint32_t)w[0], (uint32_t)w[1]);
+                    oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, oacc[t], 0, 0, 0);
                 }
-                bacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(voff, bv, bacc[kb], 0, 0, 0);
+                if constexpr (C::VOFF_BITS != 0)
+                    bacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(voff, bv, bacc[kb], 0, 0, 0);
+            }
+            if constexpr (C::VMIN) {
+                // sum over the tile's rows of p * m per block: A row b (lane b
+                // < NB) holds block b's minima of this lane row's eight rows,
+                // B the unscaled p; row b of the result is block b
+                const int e = ln < C::NB ? 2 * ln + 1 : 1;
+                const u32x4 mv = *reinterpret_cast<const u32x4*>(vst + e * TT + 8 * lq);
+                const half8 am = ln < C::NB ? make_half8(mv[0], mv[1], mv[2], mv[3])
+                                            : make_half8(0u, 0u, 0u, 0u);
+                bacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am, make_half8(pp[0], pp[1], pp[2], pp[3]),
+                                                                 bacc[0], 0, 0, 0);
             }
         } else {
             // column tile t = chunks 4t..4t+3 (4 halves each); two reads of 4
@@ -706,7 +912,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     constexpr int W = C::DS > 1 ? 1 : WAVES;
     constexpr int NS = C::NSET;
     int it = C::DS > 1 ? 0 : wave;
-    uint32_t krs[NS][2][C::KDW];
+    uint32_t krs[NS][2][KR];
     uint32_t vrs[NS][C::V_DW];
     uint32_t srs[NS][C::S_DW];
     if (it < ntiles) {
@@ -792,7 +998,12 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     if (lq == 0) {
         mw[wave * 16 + ln] = m_ref;
         lw[wave * 16 + ln] = l_head;
-        if constexpr (C::V_SCALE) {
+        if constexpr (C::VMIN) {
+            // the minima's sum enters with the opposite sign of an offset, in
+            // the units of the other accumulators (2^-24)
+#pragma unroll
+            for (int kb = 0; kb < C::NB; ++kb) bw[(wave * 16 + ln) * C::NB + kb] = -bacc[0][kb] * TWOM24;
+        } else if constexpr (C::V_SCALE) {
 #pragma unroll
             for (int kb = 0; kb < C::NB; ++kb) bw[(wave * 16 + ln) * C::NB + kb] = bacc[kb][0];
         }
@@ -944,9 +1155,51 @@ hipError_t launch3(const DecodeArgs& a, hipStream_t s)
 {
     if constexpr (!Cfg<TK, TV, D>::VALID) {
         return hipErrorInvalidConfiguration;
+    } else if constexpr (Cfg<TK, TV, D>::NEWT) {
+        // the further types: single-token decode only
+        return a.nq > 1 ? hipErrorInvalidConfiguration : launch4<TK, TV, D, false>(a, s);
     } else {
         return a.nq > 1 ? launch4<TK, TV, D, true>(a, s) : launch4<TK, TV, D, false>(a, s);
     }
+}
+
+// The pairs with the further storage types built for the matrix cores
+// (head_dim 128, one query token): the pages' served pairs that use them and
+// the tier ladder's last rung.
+#define KVQ_NEW_PAIRS(X)  \
+    X(T_Q8, T_Q6_0)       \
+    X(T_Q8, T_Q5_0)       \
+    X(T_Q6_0, T_Q6_0)     \
+    X(T_Q6_0, T_Q4)       \
+    X(T_Q5_0, T_Q5_0)     \
+    X(T_Q5_1, T_Q5_1)     \
+    X(T_Q4_1, T_Q4_1)     \
+    X(T_Q5_1, T_Q4)
+
+bool new_pair(int tk, int tv)
+{
+#define KVQ_X(K, V) if (tk == K && tv == V) return true;
+    KVQ_NEW_PAIRS(KVQ_X)
+#undef KVQ_X
+    return false;
+}
+
+bool new_supports(const DecodeArgs& a)
+{
+    if (a.D != 128 || a.nq != 1) return false;
+#define KVQ_X(K, V) \
+    if (a.tk == K && a.tv == V) return cfg_valid<K, V, 128>() && lds_bytes<K, V, 128>(a.G) <= 160 * 1024;
+    KVQ_NEW_PAIRS(KVQ_X)
+#undef KVQ_X
+    return false;
+}
+
+hipError_t new_launch(const DecodeArgs& a, hipStream_t s)
+{
+#define KVQ_X(K, V) if (a.tk == K && a.tv == V) return launch3<K, V, 128>(a, s);
+    KVQ_NEW_PAIRS(KVQ_X)
+#undef KVQ_X
+    return hipErrorInvalidConfiguration;
 }
 
 template <int TK, int TV, int D>
@@ -1055,9 +1308,16 @@ bool supports1(const DecodeArgs& a)
 
 bool decode_mfma_supports(const DecodeArgs& a)
 {
-    // the matrix-core kernel is built for f16, q8_0 and q4_0 rows
+    // the matrix-core kernel is built for f16, q8_0 and q4_0 rows, and for the
+    // listed pairs with the further types
     auto built = [](int t) { return t == T_F16 || t == T_Q8 || t == T_Q4; };
-    if (!built(a.tk) || !built(a.tv)) return false;
+    if (!built(a.tk) || !built(a.tv)) {
+        if (!new_pair(a.tk, a.tv)) return false;
+        const int64_t rows = a.max_seq_len;
+        if (rows * (int64_t)data_row_bytes(a.tk, a.D) >= (1LL << 31)) return false;
+        if (rows * (int64_t)data_row_bytes(a.tv, a.D) >= (1LL << 31)) return false;
+        return a.G >= 1 && new_supports(a);
+    }
     if (a.D != 128 && a.D != 256 && a.D != 512) return false;
     if (a.G < 1 || a.nq < 1 || a.nq * a.G > 16) return false;
     // rows read are below max_seq_len; their offsets inside one (sequence,
@@ -1098,6 +1358,7 @@ hipError_t launch_decode_mfma_dual(const DecodeArgs& t, const DecodeArgs& w, hip
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s)
 {
+    if (new_pair(a.tk, a.tv)) return new_launch(a, s);
     switch (a.tk) {
     case T_F16: return launch1<T_F16>(a, s);
     case T_Q8: return launch1<T_Q8>(a, s);

@@ -550,7 +550,8 @@ int kvq_decode_step(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     hipError_t e;
-    if (kvq::decode_mfma_supports(a)) {
+    const bool mfma = kvq::decode_mfma_supports(a);
+    if (mfma && kvq::decode_mfma_writes_new_rows(a)) {
         // the attention kernel writes the new row itself
         a.k_new = static_cast<const uint16_t*>(k_new);
         a.v_new = static_cast<const uint16_t*>(v_new);
@@ -575,7 +576,7 @@ int kvq_decode_step(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache
         ap.Hkv = Hkv;
         ap.D = D;
         e = kvq::launch_quantize_append(ap, s);
-        if (e == hipSuccess) e = kvq::launch_decode_valu(a, s);
+        if (e == hipSuccess) e = mfma ? kvq::launch_decode_mfma(a, s) : kvq::launch_decode_valu(a, s);
     }
     if (e != hipSuccess) return KVQ_ERR_LAUNCH;
 

@@ -84,6 +84,9 @@ hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
 bool decode_mfma_supports(const DecodeArgs& a);
+// whether the matrix-core kernel writes the new rows of a decode step itself
+// (every type it is built for)
+inline bool decode_mfma_writes_new_rows(const DecodeArgs&) { return true; }
 // the tail (quantised K and V) and the fp16 window of a mixed cache in one launch
 hipError_t launch_decode_mfma_dual(const DecodeArgs& tail, const DecodeArgs& window, hipStream_t s);
 bool decode_mfma_dual_supports(const DecodeArgs& tail, const DecodeArgs& window);

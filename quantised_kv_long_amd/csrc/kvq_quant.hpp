@@ -275,4 +275,109 @@ __device__ __forceinline__ void quantize_block_lanes(const uint16_t* __restrict_
     }
 }
 
+// The further types with one lane per value, bit-identical to
+// quantize_block_ext: the 32 lanes of an aligned half-wave (j = lane & 31)
+// quantise block blk of a row of D values together (data row `row`, scale
+// row `srow`, as in quantize_block_ext).  The block's extremes are found by
+// cross-lane exchanges with the sequential fold's tie rules (first index on
+// equal values, so a mix of +0 and -0 keeps the first); the high bits are
+// gathered with wave ballots.  All 32 lanes of the half-wave must call it.
+template <int T>
+__device__ __forceinline__ void quantize_block_ext_lanes(const uint16_t* __restrict__ src,
+                                                         uint8_t* __restrict__ row,
+                                                         uint16_t* __restrict__ srow, int blk, int D, int j)
+{
+    const float x = h2f(src[j]);
+    int n;
+    if constexpr (T == T_Q5_0 || T == T_Q6_0) {
+        constexpr int HALF = T == T_Q5_0 ? 16 : 32;
+        // first value of largest magnitude (as quantize_block_lanes for q4_0)
+        const float ax = fabsf(x);
+        float a = ax > 0.0f ? ax : 0.0f;
+        int idx = a > 0.0f ? j : 32;
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) {
+            const float a2 = __shfl_xor(a, off, 32);
+            const int i2 = __shfl_xor(idx, off, 32);
+            if (a2 > a || (a2 == a && i2 < idx)) {
+                a = a2;
+                idx = i2;
+            }
+        }
+        const float xs = __shfl(x, idx & 31, 32);
+        const float smax = idx < 32 ? xs : 0.0f;
+        const uint16_t mag16 = f2h_rne(fabsf(smax) * (1.0f / HALF));
+        const uint16_t d16 = (uint16_t)(mag16 | (smax < 0.0f ? 0 : 0x8000));
+        const float d = h2f(d16);
+        n = HALF;
+        if (d != 0.0f) {
+            float r = roundf(x / d);
+            r = fminf(fmaxf(r, -(float)HALF), (float)(HALF - 1));
+            n = (int)r + HALF;
+        }
+        if (j == 0) srow[blk] = d16;
+    } else {
+        constexpr float LEVELS = T == T_Q4_1 ? 15.0f : 31.0f;
+        // minimum and maximum, the lower index winning on equal values
+        float mn = x, mx = x;
+        int imn = j, imx = j;
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) {
+            const float m2 = __shfl_xor(mn, off, 32), x2 = __shfl_xor(mx, off, 32);
+            const int in2 = __shfl_xor(imn, off, 32), ix2 = __shfl_xor(imx, off, 32);
+            if (m2 < mn || (m2 == mn && in2 < imn)) {
+                mn = m2;
+                imn = in2;
+            }
+            if (x2 > mx || (x2 == mx && ix2 < imx)) {
+                mx = x2;
+                imx = ix2;
+            }
+        }
+        // the extremes themselves, bit for bit (a -0 / +0 pair compares equal)
+        mn = __shfl(x, imn, 32);
+        mx = __shfl(x, imx, 32);
+        const uint16_t d16 = f2h_rne((mx - mn) / LEVELS);
+        const uint16_t m16 = f2h_rne(mn);
+        const float d = h2f(d16), m = h2f(m16);
+        n = 0;
+        if (d != 0.0f) {
+            float r = roundf((x - m) / d);
+            r = fminf(fmaxf(r, 0.0f), LEVELS);
+            n = (int)r;
+        }
+        if (j == 0) {
+            srow[2 * blk] = d16;
+            srow[2 * blk + 1] = m16;
+        }
+    }
+    // low nibbles: byte j (< 16) holds elements j and j+16
+    const uint32_t lo = (uint32_t)(n & 15);
+    const uint32_t byte = lo | (__shfl_down(lo, 16, 32) << 4);
+    const uint32_t w = (byte & 0xff) | ((__shfl_down(byte, 1, 32) & 0xff) << 8) |
+                       ((__shfl_down(byte, 2, 32) & 0xff) << 16) | ((__shfl_down(byte, 3, 32) & 0xff) << 24);
+    if (j < 16 && (j & 3) == 0) *reinterpret_cast<uint32_t*>(row + 16 * blk + j) = w;
+    // high bits: bit j of a half-wave's ballot is element j's bit
+    const int hsh = threadIdx.x & 32;
+    if constexpr (T == T_Q5_0 || T == T_Q5_1) {
+        const uint32_t h4 = (uint32_t)(__builtin_amdgcn_ballot_w64(((n >> 4) & 1) != 0) >> hsh);
+        if (j == 0) *reinterpret_cast<uint32_t*>(row + D / 2 + 4 * blk) = h4;
+    } else if constexpr (T == T_Q6_0) {
+        const uint32_t h4 = (uint32_t)(__builtin_amdgcn_ballot_w64(((n >> 4) & 1) != 0) >> hsh);
+        const uint32_t h5 = (uint32_t)(__builtin_amdgcn_ballot_w64(((n >> 5) & 1) != 0) >> hsh);
+        // interleave: bits 2e, 2e+1 of the 64-bit word are bits 4, 5 of
+        // element e; lanes 0 and 1 write the low and high halves
+        const uint32_t lo16 = j == 0 ? (h4 & 0xffff) : (h4 >> 16);
+        const uint32_t hi16 = j == 0 ? (h5 & 0xffff) : (h5 >> 16);
+        auto spread = [](uint32_t v) {   // bit i of v (i < 16) to bit 2i
+            v = (v | (v << 8)) & 0x00FF00FFu;
+            v = (v | (v << 4)) & 0x0F0F0F0Fu;
+            v = (v | (v << 2)) & 0x33333333u;
+            v = (v | (v << 1)) & 0x55555555u;
+            return v;
+        };
+        if (j < 2) *reinterpret_cast<uint32_t*>(row + D / 2 + 8 * blk + 4 * j) = spread(lo16) | (spread(hi16) << 1);
+    }
+}
+
 }  // namespace kvq

@@ -122,18 +122,31 @@ CASES = [
 ]
 
 
+# pairs with the further types that the matrix-core kernel is built for
+# (head_dim 128, one query token)
+MFMA_PAIRS = {("q8_0", "q6_0"), ("q8_0", "q5_0"), ("q6_0", "q6_0"), ("q6_0", "q4_0"), ("q5_0", "q5_0"),
+              ("q5_1", "q5_1"), ("q4_1", "q4_1"), ("q5_1", "q4_0")}
+
+
+@pytest.mark.parametrize("variant", ["valu", "mfma"])
 @pytest.mark.parametrize("tk,tv", PAIRS)
 @pytest.mark.parametrize("case", range(len(CASES)))
-def test_decode_matches_oracle(tk, tv, case):
+def test_decode_matches_oracle(tk, tv, case, variant):
     B, Hkv, G, D, lens, st = CASES[case]
-    note(f"decode {tk}/{tv} B={B} Hkv={Hkv} G={G} D={D} lens={lens} split={st}")
+    covered = (tk, tv) in MFMA_PAIRS and D == 128
+    note(f"decode {variant} {tk}/{tv} B={B} Hkv={Hkv} G={G} D={D} lens={lens} split={st}")
     dev = "cuda"
     seed = 3300 + case
     cap = max(lens) + 9
     kc, vc = fill_pair(tk, tv, synth.normal_f16((B, Hkv, cap, D), seed, dev),
                        synth.normal_f16((B, Hkv, cap, D), seed + 1, dev))
     q = synth.normal_f16((B, Hkv * G, D), seed + 2, dev)
-    out, lse, (po, pl) = run_decode(kc, vc, q, lens, st)
+    if variant == "mfma" and not covered:
+        with pytest.raises(_lib.KVQError) as e:
+            run_decode(kc, vc, q, lens, st, variant="mfma")
+        assert e.value.status == -2
+        return
+    out, lse, (po, pl) = run_decode(kc, vc, q, lens, st, variant=variant)
     ref, ref_lse = O.attend(to_host_u16(q), planes_to_oracle(kc), planes_to_oracle(vc), lens, Hkv,
                             1 / math.sqrt(D), nthreads=oracle_threads())
     live = [b for b, L in enumerate(lens) if L > 0]
@@ -150,14 +163,22 @@ def test_decode_matches_oracle(tk, tv, case):
     assert np.all(np.abs(po - ro) <= 2e-3 + 1e-2 * np.abs(ro))
 
 
-def test_matrix_core_variant_reports_what_it_does_not_cover():
+def test_matrix_core_kernel_reports_what_it_does_not_cover():
+    """The further types on the matrix cores: head_dim 128 and one query token
+    only (KVQ_ERR_SHAPE otherwise; kvq_decode_attn falls back to the vector
+    ALUs for single-token decode)."""
     dev = "cuda"
-    kc, vc = fill_pair("q5_1", "q4_0", synth.normal_f16((1, 1, 64, 128), 1, dev),
-                       synth.normal_f16((1, 1, 64, 128), 2, dev))
-    q = synth.normal_f16((1, 5, 128), 3, dev)
-    with pytest.raises(_lib.KVQError) as e:
-        run_decode(kc, vc, q, [64], 64, variant="mfma")
-    assert e.value.status == -2
+    for D, nq in ((256, 1), (128, 2)):
+        kc, vc = fill_pair("q5_1", "q4_0", synth.normal_f16((1, 1, 64, D), 1, dev),
+                           synth.normal_f16((1, 1, 64, D), 2, dev))
+        with pytest.raises(_lib.KVQError) as e:
+            if nq == 1:
+                run_decode(kc, vc, synth.normal_f16((1, 5, D), 3, dev), [64], 64, variant="mfma")
+            else:
+                part = C.Partials(1, nq * 5, D, 64, 64)
+                C.decode_multi(kc, vc, synth.normal_f16((1, nq, 5, D), 3, dev),
+                               torch.tensor([64], dtype=torch.int32, device=dev), 64, part, 0.1)
+        assert e.value.status == -2
 
 
 @pytest.mark.parametrize("tk,tv", [("q5_1", "q4_0"), ("q6_0", "q6_0")])
@@ -250,3 +271,45 @@ def test_ladder_last_rung_full_size_64k():
                                 sub(planes_to_oracle(vc)), [L], 1, 1 / math.sqrt(D),
                                 nthreads=oracle_threads())
         assert_close(out[:, h:h + 1], lse[:, h:h + 1], ref, ref_lse, f"head {h}")
+
+
+@pytest.mark.parametrize("t", NEW)
+def test_fused_step_rows_bit_exact(t):
+    """The decode step writes the new row from the attention kernel (32 lanes
+    per block, cross-lane extremes and ballots for the high bits): the stored
+    bytes equal the oracle's quantiser on rows of every kind -- zeros, a mix
+    of +0 and -0, exact ties, tiny and huge values, an offset range."""
+    dev = "cuda"
+    B, Hkv, G, D = 7, 2, 5, 128
+    cap, L = 96, 90
+    note(f"fused step rows {t}")
+    x = synth.normal_f16((B, Hkv, D), 91, dev).float()
+    x[0] = 0.0
+    x[1] = torch.where(torch.arange(D, device=dev) % 3 == 0, torch.tensor(-0.0, device=dev),
+                       torch.tensor(0.0, device=dev)).expand(Hkv, D)
+    x[1, :, 5::32] = 1.0                                   # one nonzero per block among signed zeros
+    x[2] = torch.randint(-20, 20, (Hkv, D), device=dev).float() / 8.0
+    x[3] *= 1e-5
+    x[4] *= 3000.0
+    x[5] = 7.0 + x[5].abs()
+    kn = x.half()
+    vn = synth.normal_f16((B, Hkv, D), 92, dev)
+    lens = [L] * B
+    lt = torch.tensor(lens, dtype=torch.int32, device=dev)
+    kc = sentinel_planes(t, B, Hkv, cap, D)
+    vc = sentinel_planes(t, B, Hkv, cap, D)
+    # the rows the attention reads before the new one: any valid codes
+    base = synth.normal_f16((B, L - 1, Hkv, D), 93, dev)
+    C.append(kc, vc, base, base, torch.zeros(B, dtype=torch.int32, device=dev), L - 1)
+    part = C.Partials(B, Hkv * G, D, cap, 64)
+    out = torch.empty((B, Hkv * G, D), dtype=torch.float32, device=dev)
+    C.decode_step(kc, vc, kn, vn, synth.normal_f16((B, Hkv * G, D), 94, dev), lt, cap, part,
+                  1 / math.sqrt(D), out)
+    torch.cuda.synchronize()
+    for planes, src in ((kc, kn), (vc, vn)):
+        qd, qs = O.quantize(t, to_host_u16(src))            # (B, Hkv, ...)
+        d = planes.data.cpu().numpy()[:, :, L - 1]
+        s = planes.scales.cpu().numpy().view(np.uint16)[:, :, L - 1]
+        assert np.array_equal(d, qd), "data"
+        assert np.array_equal(s, qs), "scales"
+    assert np.all(np.isfinite(out.cpu().numpy()))
