@@ -120,6 +120,15 @@ WORKLOADS = {
         "layer append one token then attend; N(0,1)",
         layers=48, B=1, Hq=40, Hkv=8, D=128, ctx=65536,
         arms=[("f16", "f16"), ("q8_0", "q4_0"), ("q4_0", "q4_0")], seed=1003, split_tokens=1024),
+    "stack48_d128_ctx64k_types": Workload(
+        "stack48_d128_ctx64k_types",
+        "the 48-layer 64k decode stack of stack48_d128_ctx64k with the further scalar types: "
+        "the pages' served pairs with q4_1 / q5_0 / q5_1 / q6_0 and the tier ladder's q5_1 K + "
+        "q4_0 V, q8_0 K + q4_0 V for reference; N(0,1)",
+        layers=48, B=1, Hq=40, Hkv=8, D=128, ctx=65536,
+        arms=[("q8_0", "q4_0"), ("q5_1", "q4_0"), ("q4_1", "q4_1"), ("q5_0", "q5_0"), ("q5_1", "q5_1"),
+              ("q6_0", "q6_0"), ("q6_0", "q4_0"), ("q8_0", "q5_0"), ("q8_0", "q6_0")],
+        seed=1003, split_tokens=1024),
     "long_d128_ctx256k": Workload(
         "long_d128_ctx256k",
         "one layer, 40 query / 8 KV heads, head_dim 128, ctx 262144, batch 1; keys N(0,1) with "
