@@ -1155,17 +1155,14 @@ hipError_t launch3(const DecodeArgs& a, hipStream_t s)
 {
     if constexpr (!Cfg<TK, TV, D>::VALID) {
         return hipErrorInvalidConfiguration;
-    } else if constexpr (Cfg<TK, TV, D>::NEWT) {
-        // the further types: single-token decode only
-        return a.nq > 1 ? hipErrorInvalidConfiguration : launch4<TK, TV, D, false>(a, s);
     } else {
         return a.nq > 1 ? launch4<TK, TV, D, true>(a, s) : launch4<TK, TV, D, false>(a, s);
     }
 }
 
 // The pairs with the further storage types built for the matrix cores
-// (head_dim 128, one query token): the pages' served pairs that use them and
-// the tier ladder's last rung.
+// (head_dim 128): the pages' served pairs that use them and the tier ladder's
+// last rung.
 #define KVQ_NEW_PAIRS(X)  \
     X(T_Q8, T_Q6_0)       \
     X(T_Q8, T_Q5_0)       \
@@ -1186,9 +1183,9 @@ bool new_pair(int tk, int tv)
 
 bool new_supports(const DecodeArgs& a)
 {
-    if (a.D != 128 || a.nq != 1) return false;
+    if (a.D != 128) return false;
 #define KVQ_X(K, V) \
-    if (a.tk == K && a.tv == V) return cfg_valid<K, V, 128>() && lds_bytes<K, V, 128>(a.G) <= 160 * 1024;
+    if (a.tk == K && a.tv == V) return cfg_valid<K, V, 128>() && lds_bytes<K, V, 128>(a.nq * a.G) <= 160 * 1024;
     KVQ_NEW_PAIRS(KVQ_X)
 #undef KVQ_X
     return false;
@@ -1316,7 +1313,7 @@ bool decode_mfma_supports(const DecodeArgs& a)
         const int64_t rows = a.max_seq_len;
         if (rows * (int64_t)data_row_bytes(a.tk, a.D) >= (1LL << 31)) return false;
         if (rows * (int64_t)data_row_bytes(a.tv, a.D) >= (1LL << 31)) return false;
-        return a.G >= 1 && new_supports(a);
+        return a.G >= 1 && a.nq >= 1 && a.nq * a.G <= 16 && new_supports(a);
     }
     if (a.D != 128 && a.D != 256 && a.D != 512) return false;
     if (a.G < 1 || a.nq < 1 || a.nq * a.G > 16) return false;

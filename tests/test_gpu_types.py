@@ -164,11 +164,11 @@ def test_decode_matches_oracle(tk, tv, case, variant):
 
 
 def test_matrix_core_kernel_reports_what_it_does_not_cover():
-    """The further types on the matrix cores: head_dim 128 and one query token
-    only (KVQ_ERR_SHAPE otherwise; kvq_decode_attn falls back to the vector
-    ALUs for single-token decode)."""
+    """The further types on the matrix cores: head_dim 128 only (KVQ_ERR_SHAPE
+    otherwise, also for multi-query decode; kvq_decode_attn falls back to the
+    vector ALUs for single-token decode)."""
     dev = "cuda"
-    for D, nq in ((256, 1), (128, 2)):
+    for D, nq in ((256, 1), (256, 2)):
         kc, vc = fill_pair("q5_1", "q4_0", synth.normal_f16((1, 1, 64, D), 1, dev),
                            synth.normal_f16((1, 1, 64, D), 2, dev))
         with pytest.raises(_lib.KVQError) as e:
@@ -313,3 +313,45 @@ def test_fused_step_rows_bit_exact(t):
         assert np.array_equal(d, qd), "data"
         assert np.array_equal(s, qs), "scales"
     assert np.all(np.isfinite(out.cpu().numpy()))
+
+
+@pytest.mark.parametrize("tk,tv", sorted(MFMA_PAIRS))
+def test_multi_query_decode_matches_oracle(tk, tv):
+    """Multi-query decode (n_q tokens, causal among them) of the further types on
+    the matrix cores against the oracle, token by token; and the fused
+    multi-query step equals append + attention + merge bit for bit."""
+    from .test_gpu_multi import oracle_multi, run_multi
+    dev = "cuda"
+    B, Hkv, G, D, nq, st = 2, 2, 5, 128, 3, 64
+    lens = [300, 130]                      # the second: query tokens across a split boundary
+    note(f"multi {tk}/{tv}")
+    cap = max(lens)
+    kc, vc = fill_pair(tk, tv, synth.normal_f16((B, Hkv, cap, D), 61, dev),
+                       synth.normal_f16((B, Hkv, cap, D), 62, dev))
+    q = synth.normal_f16((B, nq, Hkv * G, D), 63, dev)
+    out, lse = run_multi(kc, vc, q, lens, st)
+    ref, ref_lse = oracle_multi(kc, vc, q, lens)
+    assert_close(out.reshape(B, -1, D), lse.reshape(B, -1), ref.reshape(B, -1, D), ref_lse.reshape(B, -1),
+                 f"multi {tk}/{tv}")
+    k_new = synth.normal_f16((B, nq, Hkv, D), 64, dev)
+    v_new = synth.normal_f16((B, nq, Hkv, D), 65, dev)
+    lt = torch.tensor(lens, dtype=torch.int32, device=dev)
+    res = []
+    for fused in (True, False):
+        k2, v2 = fill_pair(tk, tv, synth.normal_f16((B, Hkv, cap, D), 61, dev),
+                           synth.normal_f16((B, Hkv, cap, D), 62, dev))
+        part = C.Partials(B, nq * Hkv * G, D, cap, st)
+        o = torch.empty((B, nq * Hkv * G, D), dtype=torch.float32, device=dev)
+        ls = torch.empty((B, nq * Hkv * G), dtype=torch.float32, device=dev)
+        if fused:
+            C.decode_step_multi(k2, v2, k_new, v_new, q, lt, cap, part, 1 / math.sqrt(D), o, ls)
+        else:
+            C.append(k2, v2, k_new, v_new, lt - nq, cap)
+            C.decode_multi(k2, v2, q, lt, cap, part, 1 / math.sqrt(D))
+            C.combine(part, lt, o, ls)
+        torch.cuda.synchronize()
+        res.append((k2, v2, o, ls))
+    (a1, b1, o1, l1), (a2, b2, o2, l2) = res
+    assert torch.equal(a1.data, a2.data) and torch.equal(a1.scales, a2.scales)
+    assert torch.equal(b1.data, b2.data) and torch.equal(b1.scales, b2.scales)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
