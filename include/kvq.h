@@ -272,7 +272,7 @@ int kvq_decode_attn(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache
  *   The partials merge with kvq_combine called with n_q * Hq heads, giving
  *   out [B][n_q][Hq][D].  Other arguments as for kvq_decode_attn.
  *   KVQ_ERR_SHAPE if n_q < 1, n_q * Hq / Hkv > 16, or the matrix-core kernel
- *   does not cover D (128, 256, 512) and the types.
+ *   does not cover D and the types (see KVQ_VARIANT_MFMA).
  */
 int kvq_decode_attn_multi(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache,
                           const void* q, const int32_t* seq_lens, int B, int n_q, int Hq, int Hkv,
@@ -300,7 +300,13 @@ int kvq_decode_step_multi(const kvq_plane_desc* k_cache, const kvq_plane_desc* v
                           float* part_o, float* part_lse, int out_type, void* out, float* lse_out,
                           void* stream);
 
-/* Kernel family for kvq_decode_attn_variant. */
+/* Kernel family for kvq_decode_attn_variant.  The matrix-core kernel covers
+ * every pair of f16, q8_0 and q4_0 at D = 128, 256 and 512 (except f16 V
+ * with a quantised K at D = 256, whose LDS tiles do not fit), and
+ * at D = 128 the pairs q8_0/q6_0, q8_0/q5_0, q6_0/q6_0, q6_0/q4_0,
+ * q5_0/q5_0, q5_1/q5_1, q4_1/q4_1 and q5_1/q4_0.  The vector-ALU kernel
+ * covers every pair of types at every valid D; AUTO picks the matrix cores
+ * where they cover the call. */
 enum {
     KVQ_VARIANT_AUTO = 0, /* what kvq_decode_attn uses                         */
     KVQ_VARIANT_VALU = 1, /* dot products on the vector ALUs                   */
@@ -309,7 +315,9 @@ enum {
 
 /*
  * kvq_decode_attn with an explicit kernel family; same arguments and results
- * (within floating-point rounding).  KVQ_ERR_TYPE for an unknown variant.
+ * (within floating-point rounding).  KVQ_ERR_TYPE for an unknown variant;
+ * KVQ_ERR_SHAPE for KVQ_VARIANT_MFMA where the matrix cores do not cover the
+ * call.
  */
 int kvq_decode_attn_variant(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache,
                             const void* q, const int32_t* seq_lens, int B, int Hq, int Hkv,
@@ -424,10 +432,10 @@ int kvq_combine_regions(int n_regions, const float* const* part_o, const float* 
  * seq_lens[b] - 1) followed by kvq_decode_attn and kvq_combine with the same
  * arguments: the cache rows are bit-identical, the split partials are the
  * same, and out / lse_out agree within floating-point rounding.  Where the
- * matrix-core kernel covers the shape (D = 128, 256 or 512) the step is two
+ * matrix-core kernel covers the call (see KVQ_VARIANT_MFMA) the step is two
  * kernel launches: the attention kernel's workgroup whose split holds row
  * seq_lens[b] - 1 writes that row before it reads it, then the merge runs.
- * Other shapes run the three kernels in order.
+ * Other calls run the three kernels in order.
  *
  *   k_new, v_new : device, [B][Hkv][D] binary16: the new token's K and V rows.
  *   seq_lens     : device, [B] int32: lengths *including* the new token,
