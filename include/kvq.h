@@ -352,7 +352,8 @@ int kvq_combine(const float* part_o, const float* part_lse, const int32_t* seq_l
  * tail_* splits and partials) followed by kvq_decode_attn over the window
  * (k_win / v_win, fp16, win_lens, win_* splits and partials) with the same q,
  * and bit-identical to it.  Where the matrix-core kernel covers the shape
- * (tail K and V of q8_0 / q4_0, D = 128, 256 or 512) both regions run in one
+ * (tail K and V of q8_0 / q4_0 at D = 128, 256 or 512, or a pair with the
+ * further types that KVQ_VARIANT_MFMA lists at D = 128) both regions run in one
  * launch: a small window then costs its bytes, not a second launch's start
  * and end.  Otherwise the two launches are made.  The partials merge with
  * kvq_combine_regions.

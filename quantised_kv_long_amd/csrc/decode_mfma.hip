@@ -1247,6 +1247,11 @@ bool dual_supports2(const DecodeArgs& t)
     if (t.tk == T_Q8 && t.tv == T_Q4) return dual_supports3<T_Q8, T_Q4, D>(t);
     if (t.tk == T_Q4 && t.tv == T_Q8) return dual_supports3<T_Q4, T_Q8, D>(t);
     if (t.tk == T_Q4 && t.tv == T_Q4) return dual_supports3<T_Q4, T_Q4, D>(t);
+    if constexpr (D == 128) {
+#define KVQ_X(K, V) if (t.tk == K && t.tv == V) return dual_supports3<K, V, 128>(t);
+        KVQ_NEW_PAIRS(KVQ_X)
+#undef KVQ_X
+    }
     return false;
 }
 
@@ -1257,6 +1262,11 @@ hipError_t launch_dual2(const DecodeArgs& t, const DecodeArgs& w, hipStream_t s)
     if (t.tk == T_Q8 && t.tv == T_Q4) return launch_dual3<T_Q8, T_Q4, D>(t, w, s);
     if (t.tk == T_Q4 && t.tv == T_Q8) return launch_dual3<T_Q4, T_Q8, D>(t, w, s);
     if (t.tk == T_Q4 && t.tv == T_Q4) return launch_dual3<T_Q4, T_Q4, D>(t, w, s);
+    if constexpr (D == 128) {
+#define KVQ_X(K, V) if (t.tk == K && t.tv == V) return launch_dual3<K, V, 128>(t, w, s);
+        KVQ_NEW_PAIRS(KVQ_X)
+#undef KVQ_X
+    }
     return hipErrorInvalidConfiguration;
 }
 

@@ -74,7 +74,8 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0"), ("q8_0", "q8_0"), ("f16", "q4_0")])
+@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0"), ("q8_0", "q8_0"), ("f16", "q4_0"),
+                                   ("q5_1", "q4_0"), ("q6_0", "q6_0")])
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_regions_match_oracle(tk, tv, case):
     B, Hkv, G, D, tl, tcap, wl, wcap, st_t, st_w = CASES[case]
@@ -96,7 +97,8 @@ def test_regions_match_oracle(tk, tv, case):
         assert_close(out[live], lse[live], ref[live], ref_lse[live], f"mixed {tk}/{tv} case {case}")
 
 
-@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0"), ("f16", "q4_0")])
+@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0"), ("f16", "q4_0"), ("q5_1", "q4_0"),
+                                   ("q4_1", "q4_1")])
 @pytest.mark.parametrize("case", [0, 2, 3, 4])
 def test_mixed_call_is_the_two_calls_bit_for_bit(tk, tv, case):
     """kvq_decode_attn_mixed (one launch where the matrix-core kernel covers the
