@@ -217,14 +217,14 @@ struct Cfg {
 };
 
 // Bytes of the four-wave merge area: per wave and score column the running
-// max, sum and weight, the V offset sums per block, the corrections, and the
-// nc x D accumulators of every wave (nc = query tokens x heads per KV head).
+// max and sum, the V offset sums per block, and the nc x D accumulators of
+// every wave (nc = query tokens x heads per KV head).
 template <int TK, int TV, int D>
 __host__ __device__ constexpr size_t merge_lds_bytes(int nc)
 {
     return Cfg<TK, TV, D>::DS > 1 ? 0
-                                  : sizeof(float) * ((size_t)WAVES * 16 * 3 + (size_t)WAVES * 16 * (D / 32) +
-                                                     16 * (D / 32) + (size_t)WAVES * nc * D);
+                                  : sizeof(float) * ((size_t)WAVES * 16 * 2 + (size_t)WAVES * 16 * (D / 32) +
+                                                     (size_t)WAVES * nc * D);
 }
 
 // 128-column slices are built for two waves per SIMD (at most 256
@@ -983,18 +983,17 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     }
 
     // ---- merge the four waves: (m, l, O) per head through LDS.  Each lane
-    //      stores its raw accumulators; one thread per head then forms the
-    //      waves' weights (and the V code-offset correction per block), and
-    //      every output column is a four-term weighted sum.
+    //      stores its raw accumulators; after one barrier every thread of the
+    //      output loop forms its head's four wave weights itself (and the V
+    //      code-offset correction of its block), so each output column is a
+    //      four-term weighted sum with no second barrier.
     const float l_head = xsum4(l_part);
     __syncthreads();
     uint8_t* marea = merge_lds_bytes<TK, TV, D>(NC) <= lds_cap ? lds_a : lds_merge_dyn;
     float* mw = reinterpret_cast<float*>(marea);          // [WAVES][16]   running max
     float* lw = mw + WAVES * 16;                          // [WAVES][16]   running sum
-    float* fw = lw + WAVES * 16;                          // [WAVES][16]   merge weights
-    float* bw = fw + WAVES * 16;                          // [WAVES][16][NB] V offset sums
-    float* corr = bw + WAVES * 16 * C::NB;                // [16][NB]      corrections
-    float* ow = corr + 16 * C::NB;                        // [WAVES][NC][D] accumulators
+    float* bw = lw + WAVES * 16;                          // [WAVES][16][NB] V offset sums
+    float* ow = bw + WAVES * 16 * C::NB;                  // [WAVES][NC][D] accumulators
     if (lq == 0) {
         mw[wave * 16 + ln] = m_ref;
         lw[wave * 16 + ln] = l_head;
@@ -1022,8 +1021,8 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
             }
     }
     __syncthreads();
-    if (tid < NC) {
-        const int n = tid;
+    for (int idx = tid; idx < NC * (D / 4); idx += NT) {
+        const int n = idx / (D / 4), c4 = idx % (D / 4);
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mw[w * 16 + n]);
@@ -1036,40 +1035,26 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
         // quantised V: O = (acc - offset sum) * 2^24 (no row at all: o = 0,
         // lse = -inf)
         const float inv = lsum > 0.0f ? (C::V_SCALE ? TWO24 : 1.0f) / lsum : 0.0f;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) fw[w * 16 + n] = f[w] * inv;
-        if constexpr (C::V_SCALE) {
-#pragma unroll
-            for (int kb = 0; kb < C::NB; ++kb) {
-                float c = 0.0f;
-#pragma unroll
-                for (int w = 0; w < WAVES; ++w) c += f[w] * inv * bw[(w * 16 + n) * C::NB + kb];
-                corr[n * C::NB + kb] = c;
-            }
-        }
-        pl[crow(n) * a.max_splits] = (M + log2f(lsum)) * 0.69314718055994531f;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < NC * (D / 4); idx += NT) {
-        const int n = idx / (D / 4), c4 = idx % (D / 4);
         float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        float c = 0.0f;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
-            const float f = fw[w * 16 + n];
+            const float fwi = f[w] * inv;
             const float4 v = reinterpret_cast<const float4*>(ow + (w * NC + n) * D)[c4];
-            o.x = fmaf(f, v.x, o.x);
-            o.y = fmaf(f, v.y, o.y);
-            o.z = fmaf(f, v.z, o.z);
-            o.w = fmaf(f, v.w, o.w);
+            o.x = fmaf(fwi, v.x, o.x);
+            o.y = fmaf(fwi, v.y, o.y);
+            o.z = fmaf(fwi, v.z, o.z);
+            o.w = fmaf(fwi, v.w, o.w);
+            if constexpr (C::V_SCALE) c = fmaf(fwi, bw[(w * 16 + n) * C::NB + c4 / 8], c);
         }
         if constexpr (C::V_SCALE) {
-            const float c = corr[n * C::NB + c4 / 8];
             o.x -= c;
             o.y -= c;
             o.z -= c;
             o.w -= c;
         }
         reinterpret_cast<float4*>(po + crow(n) * ho_stride)[c4] = o;
+        if (c4 == 0) pl[crow(n) * a.max_splits] = (M + log2f(lsum)) * 0.69314718055994531f;
     }
 }
 
