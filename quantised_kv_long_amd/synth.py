@@ -107,7 +107,7 @@ WORKLOADS = {
         "one layer, batch 1, 40 query / 8 KV heads, head_dim 128, ctx 4096, K q8_0 + V q4_0, "
         "K, V, Q ~ N(0,1)",
         layers=1, B=1, Hq=40, Hkv=8, D=128, ctx=4096, arms=[("q8_0", "q4_0")], seed=1001,
-        split_tokens=256),
+        split_tokens=128),
     "hybrid_d256_ctx32k": Workload(
         "hybrid_d256_ctx32k",
         "hybrid-model full-attention layer: 16 query / 2 KV heads, head_dim 256, ctx 32768, "
