@@ -481,6 +481,60 @@ def probe_read_bandwidth(nbytes=4 << 30, reps=4):
     return best
 
 
+def probe_same_bytes_us(nbytes, reps=5):
+    """Per-launch time of the plain read kernel of libkvq_probe.so over
+    exactly `nbytes` (the attention launch's stored bytes): launches over
+    distinct buffers (>= 1 GiB in all, so the last-level cache cannot serve
+    them), captured in one graph, best over a few grid sizes.  What a launch of
+    that many bytes costs with no attention work: the start and the end of a
+    launch included.  None when the probe library is not built."""
+    import ctypes
+
+    import torch
+
+    from quantised_kv_long_amd import build as B
+
+    if not os.path.exists(B.PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.kvq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_int, ctypes.c_void_p]
+    lib.kvq_probe_stream_read.restype = ctypes.c_int
+    nbytes = (nbytes + 15) // 16 * 16
+    nbuf = max(2, math.ceil((1 << 30) / nbytes))
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda:0") for _ in range(nbuf)]
+    grids = (512, 1024, 2048)
+    sink = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda:0")
+    s = torch.cuda.Stream()
+    best = None
+    for blocks in grids:
+        def launch_all():
+            for b in bufs:
+                rc = lib.kvq_probe_stream_read(b.data_ptr(), nbytes, sink.data_ptr(), blocks, s.cuda_stream)
+                assert rc == 0, rc
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            launch_all()                       # eager warm-up
+            s.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                launch_all()
+        torch.cuda.synchronize()
+        for i in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(s):
+                e0.record(s)
+                g.replay()
+                e1.record(s)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / nbuf
+            if i and (best is None or us < best):
+                best = us
+        del g
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return best
+
+
 def cpu_baseline(arm, budget_s):
     """The oracle, as it stands, on a bounded sample of the same step: whole
     layers (quantise the new row, fp64 attention per split, exact combine) of
@@ -627,13 +681,21 @@ def main():
     probe = probe_read_bandwidth()
     probe = round(probe, 1) if probe else None
     log(f"probe read bandwidth {probe} GB/s")
+    same = probe_same_bytes_us(head_arm.stored_bytes_layer)
+    same = round(same, 3) if same else None
+    log(f"plain read of the launch's {head_arm.stored_bytes_layer} bytes: {same} us per launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": ("decode_mfma_dual_kernel" if args.window and args.variant == "auto"
                            else "decode_mfma_kernel"), "avg_launch_us": dec_us,
                 "algorithmic_bytes_per_launch": head_arm.stored_bytes_layer,
                 "probe_read_GBps": probe,
-                "frac_of_probe": round(achieved / probe, 4) if probe else None}
+                "frac_of_probe": round(achieved / probe, 4) if probe else None,
+                # the same bytes read by the plain read kernel, one launch per
+                # buffer: the time a launch of this size takes with no
+                # attention work, and the attention launch's fraction of it
+                "probe_same_bytes_us": same,
+                "frac_of_same_bytes_probe": round(same / dec_us, 4) if same else None}
     line = {
         "metric": METRIC,
         "value": h["GBps"],
