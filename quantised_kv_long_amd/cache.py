@@ -117,10 +117,10 @@ def decode_step_mixed(tail, win, k_new: torch.Tensor, v_new: torch.Tensor, q: to
 
 
 # Workgroups of the matrix-core decode kernel resident at once on the 256
-# compute units: two per CU where a wave fits in 256 registers (two waves per
-# SIMD), one at head_dim 256 (one wave per SIMD).
+# compute units: every instance runs two waves per SIMD (eight per CU), in
+# workgroups of two waves at head_dim 256 and of four otherwise.
 def resident_workgroups(D: int, cus: int = 256) -> int:
-    return cus * (1 if D == 256 else 2)
+    return cus * (4 if D == 256 else 2)
 
 
 def mixed_splits(tail_len: int, win_len: int, tail_row_bytes: int, win_row_bytes: int, B: int,

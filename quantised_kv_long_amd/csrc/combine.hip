@@ -2,31 +2,50 @@
 // "per-layer KV compression study", section 5 P2 read path: regions are merged
 // by an exact online-softmax combine; here the regions are the splits).
 //
-// One workgroup (256 threads) per (sequence, query head); the merge itself is
-// combine_rows() in kvq_combine.hpp.
+// One workgroup (256 threads) per (sequence, query head, chunk of at most
+// 128 columns); the merge itself is combine_fold_src() / combine_finish() in
+// kvq_combine.hpp.  A chunk of W columns gives its 256 threads 1024 / W
+// residue classes of the splits (8 for 128 columns), so one batch of loads
+// covers 8 or 16 splits per class whatever the head dimension; every chunk
+// reads all the lse values and writes its own columns (the first chunk also
+// writes the LSE).
 #include "kvq_combine.hpp"
 #include "kvq_internal.hpp"
 
 namespace kvq {
 namespace {
 
+// Columns of one merge workgroup: the whole row up to 128 columns, else the
+// largest multiple of 32 up to 128 that divides the row (D is a multiple of 32).
+__host__ __device__ inline int chunk_cols(int D)
+{
+    if (D <= 128) return D;
+    for (int w = 128; w > 32; w -= 32)
+        if (D % w == 0) return w;
+    return 32;
+}
+
 __global__ void __launch_bounds__(CMB_NT) combine_kernel(CombineArgs a)
 {
     __shared__ CombineLds sm;
     const int h = blockIdx.x, b = blockIdx.y;
+    const int W = chunk_cols(a.D), c0 = blockIdx.z * W;
     const int L = a.seq_lens[b];
     const int S = L > 0 ? min((L + a.split_tokens - 1) / a.split_tokens, a.max_splits) : 0;
     const int64_t bh = (int64_t)b * a.Hq + h;
-    void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh * a.D)
-                          : (void*)(reinterpret_cast<float*>(a.out) + bh * a.D);
+    void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh * a.D + c0)
+                          : (void*)(reinterpret_cast<float*>(a.out) + bh * a.D + c0);
     const float* pl = a.part_lse + bh * a.max_splits;
-    const float* po = a.part_o + bh * a.max_splits * a.D;
-    float* lse = a.lse_out ? a.lse_out + bh : nullptr;
-    // one batch of loads covers S <= 8 * (256 / (D / 4)) splits with U = 8
-    if (S <= 8 * (CMB_NT / (a.D / 4)))
-        combine_rows<8>(pl, po, S, a.D, a.out_f16, out, lse, sm);
+    const CombineSrc1 src{pl, reinterpret_cast<const float4*>(a.part_o + bh * a.max_splits * a.D + c0),
+                          a.D >> 2};
+    float* lse = a.lse_out && blockIdx.z == 0 ? a.lse_out + bh : nullptr;
+    // one batch of loads covers S <= 8 * (256 / (W / 4)) splits with U = 8
+    CombineState st = combine_init();
+    if (S <= 8 * (CMB_NT / (W / 4)))
+        combine_fold_src<8>(src, S, W, st);
     else
-        combine_rows<16>(pl, po, S, a.D, a.out_f16, out, lse, sm);
+        combine_fold_src<16>(src, S, W, st);
+    combine_finish(st, W, a.out_f16, out, lse, sm);
 }
 
 // The splits of all regions of one (sequence, query head) as one list:
@@ -64,12 +83,13 @@ __global__ void __launch_bounds__(CMB_NT) combine_regions_kernel(CombineRegionsA
 {
     __shared__ CombineLds sm;
     const int h = blockIdx.x, b = blockIdx.y;
+    const int W = chunk_cols(a.D), c0 = blockIdx.z * W;
     const int64_t bh = (int64_t)b * a.Hq + h;
-    void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh * a.D)
-                          : (void*)(reinterpret_cast<float*>(a.out) + bh * a.D);
+    void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh * a.D + c0)
+                          : (void*)(reinterpret_cast<float*>(a.out) + bh * a.D + c0);
     CombineSrcN src;
     src.n = a.n;
-    src.D4 = a.D >> 2;
+    src.D4 = a.D >> 2;                 // row stride in float4 (each row starts at column c0)
     int S = 0;
 #pragma unroll
     for (int i = 0; i < MAX_REGIONS; ++i) {
@@ -78,28 +98,28 @@ __global__ void __launch_bounds__(CMB_NT) combine_regions_kernel(CombineRegionsA
         const int L = a.seq_lens[i][b];
         S += L > 0 ? min((L + a.split_tokens[i] - 1) / a.split_tokens[i], a.max_splits[i]) : 0;
         src.pl[i] = a.part_lse[i] + bh * a.max_splits[i];
-        src.po4[i] = reinterpret_cast<const float4*>(a.part_o[i] + bh * a.max_splits[i] * a.D);
+        src.po4[i] = reinterpret_cast<const float4*>(a.part_o[i] + bh * a.max_splits[i] * a.D + c0);
     }
     CombineState st = combine_init();
-    if (S <= 8 * (CMB_NT / (a.D / 4)))
-        combine_fold_src<8>(src, S, a.D, st);
+    if (S <= 8 * (CMB_NT / (W / 4)))
+        combine_fold_src<8>(src, S, W, st);
     else
-        combine_fold_src<16>(src, S, a.D, st);
-    combine_finish(st, a.D, a.out_f16, out, a.lse_out ? a.lse_out + bh : nullptr, sm);
+        combine_fold_src<16>(src, S, W, st);
+    combine_finish(st, W, a.out_f16, out, a.lse_out && blockIdx.z == 0 ? a.lse_out + bh : nullptr, sm);
 }
 
 }  // namespace
 
 hipError_t launch_combine_regions(const CombineRegionsArgs& a, hipStream_t s)
 {
-    dim3 grid(a.Hq, a.B);
+    dim3 grid(a.Hq, a.B, a.D / chunk_cols(a.D));
     hipLaunchKernelGGL(combine_regions_kernel, grid, dim3(CMB_NT), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s)
 {
-    dim3 grid(a.Hq, a.B);
+    dim3 grid(a.Hq, a.B, a.D / chunk_cols(a.D));
     hipLaunchKernelGGL(combine_kernel, grid, dim3(CMB_NT), 0, s, a);
     return hipGetLastError();
 }

@@ -59,7 +59,6 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int WAVES = 4;
-constexpr int NT = 64 * WAVES;
 constexpr int TT = 32;                 // rows per tile
 constexpr float TAU = 8.0f;            // lazy rescale threshold, log2 units
 constexpr float TWO24 = 16777216.0f;   // 2^24
@@ -152,11 +151,13 @@ __device__ __forceinline__ float xsum4(float v)
 
 template <int TK, int TV, int D>
 struct Cfg {
-    // head_dim 512: the four waves of a workgroup walk the same tiles, each
-    // owning one 128-column slice of the head dimension (partial scores are
-    // summed through LDS); otherwise each wave walks its own tiles over the
-    // full head dimension
-    static constexpr int DS = D == 512 ? 4 : 1;    // waves sharing a tile
+    // head_dim 256 / 512: the two / four waves of a workgroup walk the same
+    // tiles, each owning one 128-column slice of the head dimension (partial
+    // scores are summed through LDS); otherwise the four waves each walk their
+    // own tiles over the full head dimension
+    static constexpr int DS = D == 512 ? 4 : (D == 256 ? 2 : 1);   // waves sharing a tile
+    static constexpr int WV = DS > 1 ? DS : WAVES;                   // waves per workgroup
+    static constexpr int NTH = 64 * WV;                              // threads per workgroup
     static constexpr int DW = D / DS;              // head-dim slice of a wave
     static constexpr int NB = DW / 32;             // blocks per slice
     static constexpr int NBG = DW / 128;           // groups of 4 blocks
@@ -201,11 +202,11 @@ struct Cfg {
     static constexpr int VS_OFF = V_BYTES + SK_BYTES;
     static constexpr int BUF = V_BYTES + SK_BYTES + SV_BYTES;
     static constexpr int NDT = DW / 16;                                // PV output tiles
-    // register sets of the load ring: two for 128-column slices (a third,
-    // where it fits in 256 registers, measured slower), one for 256 and for
-    // f16 rows of a 512-wide head (their registers do not fit twice)
+    // register sets of the load ring: two (a third, where it fits in 256
+    // registers, measured slower), one where a slice shared by several waves
+    // has f16 rows (their registers do not fit twice)
     static constexpr int NSET = DW == 128 && (DS == 1 || (TK != T_F16 && TV != T_F16)) ? 2 : 1;
-    static constexpr int SX_FLOATS = DS > 1 ? 2 * WAVES * 64 * 8 : 1;  // partial-score exchange
+    static constexpr int SX_FLOATS = DS > 1 ? 2 * WV * 64 * 8 : 1;     // partial-score exchange
     static constexpr float KOFF = TK == T_Q4 ? 8.0f : TK == T_Q8 ? 128.0f : TK == T_Q5_0 ? 16.0f
                                 : TK == T_Q6_0 ? 32.0f : 0.0f;
     // the V code offset as an fp16 subnormal pair (0: no offset, min types)
@@ -213,7 +214,7 @@ struct Cfg {
                                         : TV == T_Q5_0 ? 0x00100010u : TV == T_Q6_0 ? 0x00200020u : 0u;
     static constexpr bool VALID = V_BYTES % 1024 == 0 && SK_BYTES % 256 == 0 && SV_BYTES % 256 == 0 &&
                                   (!VBYTES || (TT * NB) % 64 == 0) && V_DW <= (DW == 128 ? 32 : 64) &&
-                                  WAVES * BUF <= 64 * 1024 && (!NEWT || (D == 128 && DS == 1));
+                                  WV * BUF <= 64 * 1024 && (!NEWT || (D == 128 && DS == 1));
 };
 
 // Bytes of the four-wave merge area: per wave and score column the running
@@ -227,8 +228,8 @@ __host__ __device__ constexpr size_t merge_lds_bytes(int nc)
                                                      (size_t)WAVES * nc * D);
 }
 
-// 128-column slices are built for two waves per SIMD (at most 256
-// registers); head_dim 256 needs more and runs one
+// Every instance is built for two waves per SIMD (at most 256 registers):
+// each wave holds a 128-column slice of the head dimension.
 // The work of one workgroup: split s of (sequence blockIdx.z, KV head
 // blockIdx.y).  LDS: lds_a, lds_cap bytes (at least WAVES * BUF: one buffer
 // per wave, the V rows of the current tile, then the K and V scale tiles
@@ -275,7 +276,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     auto crow = [&](int c) -> int64_t { return MQ ? (int64_t)(c / G) * a.Hq + c % G : (int64_t)c; };
 
     if (t_begin >= t_end) {
-        for (int i = tid; i < NC * D; i += NT) po[crow(i / D) * ho_stride + (i % D)] = 0.0f;
+        for (int i = tid; i < NC * D; i += C::NTH) po[crow(i / D) * ho_stride + (i % D)] = 0.0f;
         if (tid < NC) pl[crow(tid) * a.max_splits] = -INFINITY;
         return;
     }
@@ -301,7 +302,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
         if (a.k_new != nullptr && nrows > 0) {
             // nrows * 2*NB_ROW blocks (per row: K then V), one aligned
             // half-wave of 32 lanes per block
-            for (int it = tid >> 5; it < nrows * 2 * C::NB_ROW; it += NT / 32) {
+            for (int it = tid >> 5; it < nrows * 2 * C::NB_ROW; it += C::NTH / 32) {
                 const int r = r_lo + it / (2 * C::NB_ROW);
                 const int blk2 = it % (2 * C::NB_ROW);
                 const bool isv = blk2 >= C::NB_ROW;
@@ -318,13 +319,44 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
         }
     } else if (a.k_new != nullptr && t_end == L) {
         // 2*NB_ROW blocks (K then V), one aligned half-wave of 32 lanes per block
-        for (int blk2 = tid >> 5; blk2 < 2 * C::NB_ROW; blk2 += NT / 32) {
-            const bool isv = blk2 >= C::NB_ROW;
-            const int blk = isv ? blk2 - C::NB_ROW : blk2;
-            const uint16_t* src = (isv ? a.v_new : a.k_new) + ((int64_t)b * a.Hkv + g) * D + 32 * blk;
-            const int64_t row = (isv ? vrow0 : krow0) + (L - 1);
-            if (isv) write_block_lanes_d<TV, D>(src, a.v, row, blk, tid & 31);
-            else write_block_lanes_d<TK, D>(src, a.k, row, blk, tid & 31);
+        if constexpr (C::NEWT) {
+            for (int blk2 = tid >> 5; blk2 < 2 * C::NB_ROW; blk2 += C::NTH / 32) {
+                const bool isv = blk2 >= C::NB_ROW;
+                const int blk = isv ? blk2 - C::NB_ROW : blk2;
+                const uint16_t* src = (isv ? a.v_new : a.k_new) + ((int64_t)b * a.Hkv + g) * D + 32 * blk;
+                const int64_t row = (isv ? vrow0 : krow0) + (L - 1);
+                if (isv) write_block_lanes_d<TV, D>(src, a.v, row, blk, tid & 31);
+                else write_block_lanes_d<TK, D>(src, a.k, row, blk, tid & 31);
+            }
+        } else {
+            // each half-wave loads its value of every block it handles first,
+            // so the loads are in flight together, then quantises them
+            constexpr int HW = C::NTH / 32, NIT = (2 * C::NB_ROW + HW - 1) / HW;
+            uint16_t xh[NIT];
+#pragma unroll
+            for (int k = 0; k < NIT; ++k) {
+                const int blk2 = (tid >> 5) + k * HW;
+                if (blk2 < 2 * C::NB_ROW) {
+                    const bool isv = blk2 >= C::NB_ROW;
+                    const int blk = isv ? blk2 - C::NB_ROW : blk2;
+                    xh[k] = ((isv ? a.v_new : a.k_new) + ((int64_t)b * a.Hkv + g) * D + 32 * blk)[tid & 31];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < NIT; ++k) {
+                const int blk2 = (tid >> 5) + k * HW;
+                if (blk2 < 2 * C::NB_ROW) {
+                    const bool isv = blk2 >= C::NB_ROW;
+                    const int blk = isv ? blk2 - C::NB_ROW : blk2;
+                    const int64_t row = (isv ? vrow0 : krow0) + (L - 1);
+                    if (isv)
+                        quantize_block_lanes_v<TV>(xh[k], a.v.data + row * rb(TV, D) + blk * rb(TV, 32),
+                                                   a.v.scales + row * (D / 32) + blk, tid & 31);
+                    else
+                        quantize_block_lanes_v<TK>(xh[k], a.k.data + row * rb(TK, D) + blk * rb(TK, 32),
+                                                   a.k.scales + row * (D / 32) + blk, tid & 31);
+                }
+            }
         }
         // the row is read back only by this workgroup, whose loads of that
         // tile are issued after the barrier: the stores must be complete
@@ -757,14 +789,14 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
             // each wave holds the scores over its head-dim slice: sum the
             // four in a fixed order, so every wave gets the same bits (one
             // barrier per tile; the two halves of lds_sx alternate by tile)
-            float* mine = lds_sx + ((it & 1) * WAVES + wave) * 512 + lane * 8;
+            float* mine = lds_sx + ((it & 1) * C::WV + wave) * 512 + lane * 8;
             *reinterpret_cast<floatx4*>(mine) = sacc[0];
             *reinterpret_cast<floatx4*>(mine + 4) = sacc[1];
             __syncthreads();
             floatx4 f0 = {0.0f, 0.0f, 0.0f, 0.0f}, f1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int w = 0; w < WAVES; ++w) {
-                const float* theirs = lds_sx + ((it & 1) * WAVES + w) * 512 + lane * 8;
+            for (int w = 0; w < C::WV; ++w) {
+                const float* theirs = lds_sx + ((it & 1) * C::WV + w) * 512 + lane * 8;
                 f0 += *reinterpret_cast<const floatx4*>(theirs);
                 f1 += *reinterpret_cast<const floatx4*>(theirs + 4);
             }
@@ -1021,7 +1053,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
             }
     }
     __syncthreads();
-    for (int idx = tid; idx < NC * (D / 4); idx += NT) {
+    for (int idx = tid; idx < NC * (D / 4); idx += C::NTH) {
         const int n = idx / (D / 4), c4 = idx % (D / 4);
         float M = -INFINITY;
 #pragma unroll
@@ -1059,11 +1091,11 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
 }
 
 template <int TK, int TV, int D, bool MQ>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
+__global__ void __launch_bounds__((Cfg<TK, TV, D>::NTH)) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mfma_kernel(DecodeArgs a)
 {
     using C = Cfg<TK, TV, D>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[WAVES * C::BUF];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_a[C::WV * C::BUF];
     __shared__ __attribute__((aligned(16))) float lds_sx[C::SX_FLOATS];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
     decode_wg<TK, TV, D, MQ>(a, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn);
@@ -1079,13 +1111,13 @@ template <int TK, int TV, int D>
 struct DualCfg {
     using T = Cfg<TK, TV, D>;
     using F = Cfg<T_F16, T_F16, D>;
-    static constexpr int BUF = WAVES * (T::BUF > F::BUF ? T::BUF : F::BUF);
+    static constexpr int BUF = T::WV * (T::BUF > F::BUF ? T::BUF : F::BUF);
     static constexpr int SX = T::SX_FLOATS > F::SX_FLOATS ? T::SX_FLOATS : F::SX_FLOATS;
     static constexpr bool VALID = T::VALID && F::VALID;
 };
 
 template <int TK, int TV, int D>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
+__global__ void __launch_bounds__((Cfg<TK, TV, D>::NTH)) __attribute__((amdgpu_waves_per_eu(2)))
 decode_mfma_dual_kernel(DecodeArgs t, DecodeArgs w)
 {
     using DC = DualCfg<TK, TV, D>;
@@ -1109,14 +1141,14 @@ size_t dyn_lds_bytes(int nc)
 {
     using C = Cfg<TK, TV, D>;
     const size_t merge = merge_lds_bytes<TK, TV, D>(nc);
-    return merge <= (size_t)WAVES * C::BUF ? 0 : merge;
+    return merge <= (size_t)C::WV * C::BUF ? 0 : merge;
 }
 
 template <int TK, int TV, int D>
 size_t lds_bytes(int nc)
 {
     using C = Cfg<TK, TV, D>;
-    return (size_t)WAVES * C::BUF + sizeof(float) * C::SX_FLOATS + dyn_lds_bytes<TK, TV, D>(nc);
+    return (size_t)C::WV * C::BUF + sizeof(float) * C::SX_FLOATS + dyn_lds_bytes<TK, TV, D>(nc);
 }
 
 template <int TK, int TV, int D, bool MQ>
@@ -1131,7 +1163,7 @@ hipError_t launch4(const DecodeArgs& a, hipStream_t s)
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((decode_mfma_kernel<TK, TV, D, MQ>), grid, dim3(NT), dyn, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<TK, TV, D, MQ>), grid, dim3(Cfg<TK, TV, D>::NTH), dyn, s, a);
     return hipGetLastError();
 }
 
@@ -1219,7 +1251,7 @@ hipError_t launch_dual3(const DecodeArgs& t, const DecodeArgs& w, hipStream_t s)
             if (e != hipSuccess) return e;
         }
         dim3 grid(grid_splits(t) + grid_splits(w), t.Hkv, t.B);
-        hipLaunchKernelGGL((decode_mfma_dual_kernel<TK, TV, D>), grid, dim3(NT), dyn, s, t, w);
+        hipLaunchKernelGGL((decode_mfma_dual_kernel<TK, TV, D>), grid, dim3(Cfg<TK, TV, D>::NTH), dyn, s, t, w);
         return hipGetLastError();
     }
 }

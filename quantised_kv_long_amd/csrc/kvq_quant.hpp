@@ -211,16 +211,18 @@ __device__ __forceinline__ void quantize_block_ext(const uint16_t* __restrict__ 
 // the block maximum found by cross-lane exchanges.  Every lane performs the
 // same float operations on its value as quantize_block does, so the bytes are
 // identical.  All 32 lanes of the half-wave must call it together.
+// quantize_block_lanes_v takes the lane's value xh (element j of the block,
+// fp16 bits) already loaded, so a caller can issue the loads of several
+// blocks before quantising any of them.
 template <int T>
-__device__ __forceinline__ void quantize_block_lanes(const uint16_t* __restrict__ src,
-                                                     uint8_t* __restrict__ dst,
-                                                     uint16_t* __restrict__ sdst, int j)
+__device__ __forceinline__ void quantize_block_lanes_v(uint16_t xh, uint8_t* __restrict__ dst,
+                                                       uint16_t* __restrict__ sdst, int j)
 {
     if constexpr (T == T_F16) {
-        if (j < 4) reinterpret_cast<uint4*>(dst)[j] = reinterpret_cast<const uint4*>(src)[j];
+        reinterpret_cast<uint16_t*>(dst)[j] = xh;
         return;
     } else {
-        const float x = h2f(src[j]);
+        const float x = h2f(xh);
         if constexpr (T == T_Q8) {
             float amax = fmaxf(0.0f, fabsf(x));   // as the sequential fold from 0 (NaN drops out)
 #pragma unroll
@@ -272,6 +274,18 @@ __device__ __forceinline__ void quantize_block_lanes(const uint16_t* __restrict_
             if (j < 16 && (j & 3) == 0) *reinterpret_cast<uint32_t*>(dst + j) = w;
             if (j == 0) *sdst = d16;
         }
+    }
+}
+
+template <int T>
+__device__ __forceinline__ void quantize_block_lanes(const uint16_t* __restrict__ src,
+                                                     uint8_t* __restrict__ dst,
+                                                     uint16_t* __restrict__ sdst, int j)
+{
+    if constexpr (T == T_F16) {
+        if (j < 4) reinterpret_cast<uint4*>(dst)[j] = reinterpret_cast<const uint4*>(src)[j];
+    } else {
+        quantize_block_lanes_v<T>(src[j], dst, sdst, j);
     }
 }
 

@@ -66,6 +66,8 @@ SMALL = [
     (2, 1, 16, 64, [64, 63], 64),
     (1, 2, 1, 512, [300], 64),
     (3, 2, 4, 32, [1, 129, 200], 64),
+    # head_dim 192: the vector-ALU kernel, and a merge in two 96-column chunks
+    (1, 1, 3, 192, [500], 128),
 ]
 
 
@@ -132,14 +134,17 @@ def test_partials_past_max_seq_len_untouched(variant):
                  variant)
 
 
-def test_combine_alone_on_oracle_partials():
+@pytest.mark.parametrize("D", [32, 128, 160, 192, 256, 512])
+@pytest.mark.parametrize("S", [40, 300])
+def test_combine_alone_on_oracle_partials(D, S):
     """K3 fed the oracle's split partials (rounded to fp32) reproduces the
-    oracle's exact merge."""
-    note("combine on oracle partials")
-    rng = np.random.default_rng(3)
-    B, Hq, D, st = 3, 6, 128, 64
-    lens = [1, 1000, 64 * 40]
-    S = 40
+    oracle's exact merge: rows of up to 128 columns in one workgroup, wider
+    rows in column chunks (160: five of 32, 192: two of 96, 256 / 512: two /
+    four of 128); 300 splits take several batches of loads."""
+    note(f"combine on oracle partials D={D} S={S}")
+    rng = np.random.default_rng(3 + D + S)
+    B, Hq, st = 3, 6, 64
+    lens = [1, 1000, 64 * S]
     po = rng.standard_normal((B, Hq, S, D))
     pl = rng.standard_normal((B, Hq, S)) * 5
     for b in range(B):
