@@ -3,33 +3,40 @@
 // by an exact online-softmax combine; here the regions are the splits).
 //
 // One workgroup (256 threads) per (sequence, query head, chunk of at most
-// 128 columns); the merge itself is combine_fold_src() / combine_finish() in
-// kvq_combine.hpp.  A chunk of W columns gives its 256 threads 1024 / W
-// residue classes of the splits (8 for 128 columns), so one batch of loads
-// covers 8 or 16 splits per class whatever the head dimension; every chunk
-// reads all the lse values and writes its own columns (the first chunk also
-// writes the LSE).
+// 128 columns, chosen by chunk_cols); the merge itself is combine_fold_src() /
+// combine_finish() in kvq_combine.hpp.  A chunk of W columns gives its 256
+// threads 256 / (W / 4) residue classes of the splits (8 for 128 columns),
+// each folding its splits in batches of 8 or 16 loads; every chunk reads all
+// the lse values and writes its own columns (the first chunk also writes the
+// LSE).
 #include "kvq_combine.hpp"
 #include "kvq_internal.hpp"
 
 namespace kvq {
 namespace {
 
-// Columns of one merge workgroup: the whole row up to 128 columns, else the
-// largest multiple of 32 up to 128 that divides the row (D is a multiple of 32).
-__host__ __device__ inline int chunk_cols(int D)
+// Columns of one merge workgroup for rows of D columns (a multiple of 32) and
+// up to S splits: the whole row up to 128 columns, else the largest multiple
+// of 32 up to 128 that divides it; then narrower divisors while a thread
+// would fold more than 16 splits (one batch of loads), since a chunk of w
+// columns has 256 / (w / 4) residue classes.
+inline int chunk_cols(int D, int S)
 {
-    if (D <= 128) return D;
-    for (int w = 128; w > 32; w -= 32)
-        if (D % w == 0) return w;
-    return 32;
+    auto next_down = [D](int w) {
+        for (int v = w - 32; v >= 32; v -= 32)
+            if (D % v == 0) return v;
+        return 32;
+    };
+    int w = D <= 128 ? D : next_down(160);
+    while (w > 32 && (S + CMB_NT / (w / 4) - 1) / (CMB_NT / (w / 4)) > 16) w = next_down(w);
+    return w;
 }
 
 __global__ void __launch_bounds__(CMB_NT) combine_kernel(CombineArgs a)
 {
     __shared__ CombineLds sm;
     const int h = blockIdx.x, b = blockIdx.y;
-    const int W = chunk_cols(a.D), c0 = blockIdx.z * W;
+    const int W = a.D / (int)gridDim.z, c0 = blockIdx.z * W;
     const int L = a.seq_lens[b];
     const int S = L > 0 ? min((L + a.split_tokens - 1) / a.split_tokens, a.max_splits) : 0;
     const int64_t bh = (int64_t)b * a.Hq + h;
@@ -83,7 +90,7 @@ __global__ void __launch_bounds__(CMB_NT) combine_regions_kernel(CombineRegionsA
 {
     __shared__ CombineLds sm;
     const int h = blockIdx.x, b = blockIdx.y;
-    const int W = chunk_cols(a.D), c0 = blockIdx.z * W;
+    const int W = a.D / (int)gridDim.z, c0 = blockIdx.z * W;
     const int64_t bh = (int64_t)b * a.Hq + h;
     void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh * a.D + c0)
                           : (void*)(reinterpret_cast<float*>(a.out) + bh * a.D + c0);
@@ -112,14 +119,16 @@ __global__ void __launch_bounds__(CMB_NT) combine_regions_kernel(CombineRegionsA
 
 hipError_t launch_combine_regions(const CombineRegionsArgs& a, hipStream_t s)
 {
-    dim3 grid(a.Hq, a.B, a.D / chunk_cols(a.D));
+    int S = 0;
+    for (int i = 0; i < a.n; ++i) S += a.max_splits[i];
+    dim3 grid(a.Hq, a.B, a.D / chunk_cols(a.D, S));
     hipLaunchKernelGGL(combine_regions_kernel, grid, dim3(CMB_NT), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s)
 {
-    dim3 grid(a.Hq, a.B, a.D / chunk_cols(a.D));
+    dim3 grid(a.Hq, a.B, a.D / chunk_cols(a.D, a.max_splits));
     hipLaunchKernelGGL(combine_kernel, grid, dim3(CMB_NT), 0, s, a);
     return hipGetLastError();
 }
