@@ -95,6 +95,8 @@ def parse():
                         "and the rest in the arm's types (kvq_decode_attn_mixed and "
                         "kvq_combine_regions)")
     p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--no-long-ctx", dest="long_ctx", action="store_false",
+                   help="skip the 262144-row layer that the default 64k run also times")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline (0 disables it)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -535,45 +537,108 @@ def probe_same_bytes_us(nbytes, reps=5):
     return best
 
 
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty if unreadable)."""
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(arm, budget_s):
     """The oracle, as it stands, on a bounded sample of the same step: whole
     layers (quantise the new row, fp64 attention per split, exact combine) of
-    the same cache bytes, timed on this host's cores."""
+    the same cache bytes, timed on every core this process may run on, then
+    one layer on a single thread."""
     import numpy as np
     import torch
 
     from oracle import oracle as O
 
     wl = arm.wl
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads = len(os.sched_getaffinity(0))
     u16 = lambda t: t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-    done, elapsed = 0, 0.0
-    for L in arm.layers[: wl.layers]:
+    name = {0: "f16", 1: "q8_0", 2: "q4_0"}
+
+    def host_layer(L):
         kc, vc = L["kc"], L["vc"]
-        name = {0: "f16", 1: "q8_0", 2: "q4_0"}
         kp = (name[kc.type], kc.data.cpu().numpy(),
               kc.scales.cpu().numpy().view(np.uint16) if kc.scales is not None else None)
         vp = (name[vc.type], vc.data.cpu().numpy(),
               vc.scales.cpu().numpy().view(np.uint16) if vc.scales is not None else None)
-        q = u16(L["q"])
-        knew, vnew = u16(L["knew"]), u16(L["vnew"])
+        return kp, vp, u16(L["q"]), u16(L["knew"]), u16(L["vnew"])
+
+    def one_layer(kp, vp, q, knew, vnew, nthreads):
         t0 = time.perf_counter()
         O.quantize(kp[0], knew)
         O.quantize(vp[0], vnew)
         po, pl = O.attend_split(q, kp, vp, arm.lens, wl.Hkv, 1 / math.sqrt(wl.D),
-                                arm.part.split_tokens, arm.part.max_splits, nthreads=threads)
+                                arm.part.split_tokens, arm.part.max_splits, nthreads=nthreads)
         O.combine(po, pl)
-        elapsed += time.perf_counter() - t0
+        return time.perf_counter() - t0
+
+    done, elapsed = 0, 0.0
+    for L in arm.layers[: wl.layers]:
+        elapsed += one_layer(*host_layer(L), threads)
         done += 1
         if elapsed >= budget_s:
             break
     s_per_layer = elapsed / done
     gbs = arm.stored_bytes_layer / s_per_layer / 1e9
+    s1 = one_layer(*host_layer(arm.layers[0]), 1)
     sample = (f"{done} of {wl.layers} layer(s) of {wl.name}, {arm.tk}/{arm.tv}: quantise the new "
               f"row, fp64 attention over {arm.part.max_splits} splits of {arm.part.split_tokens} "
-              f"rows, exact combine; {s_per_layer * 1e3:.1f} ms per layer")
+              f"rows, exact combine; {s_per_layer * 1e3:.1f} ms per layer on {threads} threads, "
+              f"{s1 * 1e3:.1f} ms for one layer on 1 thread; per-step figures scaled to "
+              f"{wl.layers} layers")
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "us_per_step_scaled": round(s_per_layer * wl.layers * 1e6, 1)}
+            "sample": sample, "cpu_model": cpu_model(),
+            "us_per_step_scaled": round(s_per_layer * wl.layers * 1e6, 1),
+            "one_thread": {"value": round(arm.stored_bytes_layer / s1 / 1e9, 4), "unit": "GB/s",
+                           "us_per_step_scaled": round(s1 * wl.layers * 1e6, 1)}}
+
+
+def arm_ratios(results):
+    """Speed-ups between the arms of one workload (median single steps and
+    their p10-p90 separation where sampled)."""
+    ratios = {}
+    if "q4_0/q4_0" in results and "q8_0/q4_0" in results:
+        ratios["q4q4_over_q8q4_speedup"] = round(results["q8_0/q4_0"]["us_per_step"] /
+                                                 results["q4_0/q4_0"]["us_per_step"], 3)
+        a, b = results["q8_0/q4_0"], results["q4_0/q4_0"]
+        ratios["q4q4_over_q8q4_attention_speedup"] = round(a["decode_only_us_per_launch"] /
+                                                           b["decode_only_us_per_launch"], 3)
+        if "single_step_us_p10_p50_p90" in a and "single_step_us_p10_p50_p90" in b:
+            pa, pb = a["single_step_us_p10_p50_p90"], b["single_step_us_p10_p50_p90"]
+            ratios["q4q4_over_q8q4_median_single_step"] = round(pa[1] / pb[1], 3)
+            ratios["q4q4_p90_below_q8q4_p10"] = pb[2] < pa[0]
+    if "f16/f16" in results and "q8_0/q4_0" in results:
+        ratios["q8q4_over_f16_speedup"] = round(results["f16/f16"]["us_per_step"] /
+                                                results["q8_0/q4_0"]["us_per_step"], 3)
+    return ratios
+
+
+def run_long_context(args, dev):
+    """The 262144-row layer (40 query / 8 KV heads, head_dim 128, one planted
+    needle per KV head) timed the same way, so one default run covers both ends
+    of the 64k-256k range; its attention launch's fraction of peak is reported
+    per arm."""
+    import torch
+
+    from quantised_kv_long_amd import synth
+
+    wl = synth.WORKLOADS["long_d128_ctx256k"]
+    arms = [("q8_0", "q4_0"), ("q4_0", "q4_0")]
+    res, arm = run_arms(wl, arms, arms[0], wl.split_tokens, args, dev)
+    del arm
+    torch.cuda.empty_cache()
+    for r in res.values():
+        r["decode_only_frac_of_peak"] = round(r["decode_only_GBps"] / HBM_PEAK_GBS, 4)
+    return {"workload": wl.name, "ctx": wl.ctx, "layers": wl.layers, "split_tokens": wl.split_tokens,
+            "arms": res, "ratios": arm_ratios(res)}
 
 
 def main():
@@ -610,67 +675,14 @@ def main():
     split_tokens = args.split_tokens or wl.split_tokens
     headline = ("q8_0", "q4_0") if ("q8_0", "q4_0") in arms else arms[0]
 
-    results = {}
-    head_arm = None
-    for tk, tv in arms:
-        per_layer = sum(wl.lengths()) * wl.Hkv * (
-            kvq.kvq_data_row_bytes(tk, wl.D) + kvq.kvq_scale_row_bytes(tk, wl.D) +
-            kvq.kvq_data_row_bytes(tv, wl.D) + kvq.kvq_scale_row_bytes(tv, wl.D))
-        reps = args.replicas or max(1, math.ceil(1.0e9 / (per_layer * wl.layers)))
-        log(f"arm {tk}/{tv}: building {wl.layers} layer(s) x {reps} replica(s)")
-        arm = Arm(wl, tk, tv, args.split_tokens if args.window else split_tokens, reps, dev, args.queries,
-                  args.window)
-        log(f"arm {tk}/{tv}: timing {args.steps} steps")
-        ms, samples = time_arm(arm, args.steps, args.warmup, not args.no_graph, args.variant)
-        per_launch = {m: ms[m] / wl.layers for m in MODES}
-        evict_us = time_evictions(arm) if args.window else None
-        results[f"{tk}/{tv}"] = {
-            "us_per_step": round(ms["step"] * 1e3, 2),
-            "stored_bytes_per_step": arm.stored_bytes_step,
-            "GBps": round(arm.stored_bytes_step / (ms["step"] * 1e-3) / 1e9, 1),
-            "frac_of_peak": round(arm.stored_bytes_step / (ms["step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "step_us_per_layer": round(per_launch["step"] * 1e3, 3),
-            "three_call_us_per_step": round(ms["three"] * 1e3, 2),
-            "decode_only_us_per_launch": round(per_launch["decode"] * 1e3, 3),
-            "split_tokens": arm.split_tokens,
-            **({"window_split_tokens": arm.win_split_tokens} if args.window else {}),
-            "decode_only_GBps": round(arm.stored_bytes_layer / (per_launch["decode"] * 1e-3) / 1e9, 1),
-            "replicas": reps,
-        }
-        if args.queries > 1:
-            results[f"{tk}/{tv}"]["tokens_per_step"] = args.queries
-            results[f"{tk}/{tv}"]["us_per_token_per_layer"] = round(per_launch["step"] * 1e3 / args.queries, 3)
-        if evict_us is not None:
-            # once every WINDOW steps per layer: quantise the window into the tail
-            results[f"{tk}/{tv}"]["eviction_us_per_layer"] = round(evict_us, 3)
-            results[f"{tk}/{tv}"]["eviction_us_per_step_layer_amortised"] = round(evict_us / args.window, 4)
-        if samples:
-            results[f"{tk}/{tv}"]["single_step_us_p10_p50_p90"] = [
-                round(percentile(samples, q), 2) for q in (0.1, 0.5, 0.9)]
-        log(f"arm {tk}/{tv}: {results[f'{tk}/{tv}']}")
-        if (tk, tv) == headline:
-            head_arm = arm
-        else:
-            del arm
-            torch.cuda.empty_cache()
-
+    results, head_arm = run_arms(wl, arms, headline, args.split_tokens if args.window else split_tokens,
+                                 args, dev)
     h = results[f"{headline[0]}/{headline[1]}"]
     cpu = None
     if args.cpu_seconds > 0 and args.queries == 1 and not args.window:
         log("oracle CPU baseline")
         cpu = cpu_baseline(head_arm, args.cpu_seconds)
-    ratios = {}
-    if "q4_0/q4_0" in results and "q8_0/q4_0" in results:
-        ratios["q4q4_over_q8q4_speedup"] = round(results["q8_0/q4_0"]["us_per_step"] /
-                                                 results["q4_0/q4_0"]["us_per_step"], 3)
-        a, b = results["q8_0/q4_0"], results["q4_0/q4_0"]
-        if "single_step_us_p10_p50_p90" in a and "single_step_us_p10_p50_p90" in b:
-            pa, pb = a["single_step_us_p10_p50_p90"], b["single_step_us_p10_p50_p90"]
-            ratios["q4q4_over_q8q4_median_single_step"] = round(pa[1] / pb[1], 3)
-            ratios["q4q4_p90_below_q8q4_p10"] = pb[2] < pa[0]
-    if "f16/f16" in results and "q8_0/q4_0" in results:
-        ratios["q8q4_over_f16_speedup"] = round(results["f16/f16"]["us_per_step"] /
-                                                results["q8_0/q4_0"]["us_per_step"], 3)
+    ratios = arm_ratios(results)
     dec_us = h["decode_only_us_per_launch"]
     achieved = head_arm.stored_bytes_layer / (dec_us * 1e-6) / 1e9
     rec = traffic_record(workload_key(wl.name, args), headline[0], headline[1])
@@ -707,7 +719,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # the contractions take f16 operands (the codes as exact f16 values,
+        # Q, and p times the V scale) on the matrix cores with fp32
+        # accumulation; block scales, softmax and merge are fp32
+        "dtype": "f16 MFMA operands, fp32 accumulate/softmax",
         "data": "synthetic",
         "config": {"workload": workload_key(wl.name, args), "arm": f"{headline[0]}K/{headline[1]}V",
                    "queries": args.queries, "window": args.window,
@@ -722,6 +737,11 @@ def main():
         "arms": results,
         "ratios": ratios,
     }
+    if args.long_ctx and args.workload == "stack48_d128_ctx64k" and args.queries == 1 and not args.window:
+        del head_arm
+        torch.cuda.empty_cache()
+        log("long-context layer (262144 rows)")
+        line["long_ctx"] = run_long_context(args, dev)
     print(json.dumps(line), flush=True)
 
 

@@ -228,19 +228,21 @@ int kvq_quantize_rows(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cac
  * Sequence b attends over its rows [0, seq_lens[b]) with no mask.  The rows
  * are cut into splits of split_tokens rows; split s of sequence b covers rows
  * [s*split_tokens, min((s+1)*split_tokens, L_b)).  For every (b, h, s) with
- * s < ceil(max_seq_len / split_tokens) the call writes, in fp32,
- *   part_lse[b][h][s]   = ln sum_t exp(score_t)   (-inf for an empty split)
- *   part_o[b][h][s][:]  = sum_t exp(score_t - part_lse) * v_t   (0 if empty)
+ * s < S_b = ceil(L_b / split_tokens) (the splits that hold a row) the call
+ * writes, in fp32,
+ *   part_lse[b][h][s]   = ln sum_t exp(score_t)
+ *   part_o[b][h][s][:]  = sum_t exp(score_t - part_lse) * v_t
  * with score_t = softmax_scale * sum_d q[b][h][d] * k_t[d] and k_t, v_t the
- * dequantised rows (code * scale, exactly).  Splits from there up to
- * max_splits are left as they are: every length is at most max_seq_len, so
- * no merge reads them, and the launch does not spend workgroups on them
- * (partials sized for the cache's capacity cost nothing while the sequences
- * are shorter).
+ * dequantised rows (code * scale, exactly).  Splits from S_b up to
+ * max_splits hold no row and are left as they are: kvq_combine reads only
+ * the first S_b splits of sequence b (a caller merging partials itself knows
+ * S_b from L_b), and the launch spends no workgroups on splits from
+ * ceil(max_seq_len / split_tokens) on.
  *
  *   q              : device, [B][Hq][D] binary16.
  *   seq_lens       : device, [B] int32, 0 <= L_b <= max_seq_len <= capacity
- *                    (L_b = 0: every split of b is empty).
+ *                    (L_b = 0: no split of b holds a row; nothing is written
+ *                    for b).
  *   max_seq_len    : host, an upper bound of every L_b.
  *   split_tokens   : host, a positive multiple of KVQ_SPLIT_GRANULE.
  *   max_splits     : host, >= ceil(max_seq_len / split_tokens).

@@ -64,6 +64,9 @@ constexpr float TAU = 8.0f;            // lazy rescale threshold, log2 units
 constexpr float TWO24 = 16777216.0f;   // 2^24
 constexpr float TWOM24 = 1.0f / 16777216.0f;
 constexpr int VMCNT0 = 0x0F70;         // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
+#ifndef KVQ_RING
+#define KVQ_RING 2                     // register sets of the quantised head_dim-128 load ring
+#endif
 
 __host__ __device__ constexpr int rb(int t, int D) { return data_row_bytes(t, D); }
 
@@ -205,7 +208,8 @@ struct Cfg {
     // register sets of the load ring: two (a third, where it fits in 256
     // registers, measured slower), one where a slice shared by several waves
     // has f16 rows (their registers do not fit twice)
-    static constexpr int NSET = DW == 128 && (DS == 1 || (TK != T_F16 && TV != T_F16)) ? 2 : 1;
+    static constexpr int NSET = DW == 128 && (DS == 1 || (TK != T_F16 && TV != T_F16))
+                                    ? (DS == 1 && TK != T_F16 && TV != T_F16 ? KVQ_RING : 2) : 1;
     static constexpr int SX_FLOATS = DS > 1 ? 2 * WV * 64 * 8 : 1;     // partial-score exchange
     static constexpr float KOFF = TK == T_Q4 ? 8.0f : TK == T_Q8 ? 128.0f : TK == T_Q5_0 ? 16.0f
                                 : TK == T_Q6_0 ? 32.0f : 0.0f;
@@ -257,7 +261,10 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
 {
     using C = Cfg<TK, TV, D>;
     const int g = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // the wave index is uniform across a wave: held in a scalar register, the
+    // tile loop and the tile base addresses are scalar work
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ln = lane & 15, lq = lane >> 4;       // column / lane row of the 16x16 layouts
     const int G = a.G;
     // score columns: NQ query tokens x G heads; column c is token c / G (the
@@ -275,21 +282,32 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     // partial row of column c, relative to (b, h0)
     auto crow = [&](int c) -> int64_t { return MQ ? (int64_t)(c / G) * a.Hq + c % G : (int64_t)c; };
 
-    if (t_begin >= t_end) {
-        for (int i = tid; i < NC * D; i += C::NTH) po[crow(i / D) * ho_stride + (i % D)] = 0.0f;
-        if (tid < NC) pl[crow(tid) * a.max_splits] = -INFINITY;
-        return;
-    }
+    // a split at or past ceil(L / split_tokens) holds no row: the merge never
+    // reads its partials, so nothing is written
+    if (t_begin >= t_end) return;
 
     const int64_t krow0 = (int64_t)b * a.k.seq_stride + (int64_t)g * a.k.head_stride;
     const int64_t vrow0 = (int64_t)b * a.v.seq_stride + (int64_t)g * a.v.head_stride;
     const int wsl = C::DS > 1 ? wave : 0;          // this wave's head-dim slice
-    const uint8_t* kdata = a.k.data + krow0 * C::RBK_ROW + wsl * C::RBK;
-    const uint8_t* kscl =
-        reinterpret_cast<const uint8_t*>(a.k.scales + (krow0 * C::NB_ROW + wsl * C::NB) * C::SPBK);
-    const uint8_t* vdata = a.v.data + vrow0 * C::RBV_ROW + wsl * C::RBV;
-    const uint8_t* vscl =
-        reinterpret_cast<const uint8_t*>(a.v.scales + (vrow0 * C::NB_ROW + wsl * C::NB) * C::SPBV);
+    // Each plane of (sequence b, KV head g) is read through a buffer resource
+    // that covers its rows [0, L): a load of a row at or past L returns zeros
+    // without a memory access, so a split's last tile and a prefetch past a
+    // wave's last tile need neither a clamp nor a branch, and every tile's
+    // loads are one scalar tile offset plus per-lane offsets fixed for the
+    // whole loop.  (Offsets are 32-bit: rows below max_seq_len span < 2^31
+    // bytes per plane.)
+    auto make_rsrc = [](const void* p, int64_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k.data + krow0 * C::RBK_ROW, (int64_t)L * C::RBK_ROW);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v.data + vrow0 * C::RBV_ROW, (int64_t)L * C::RBV_ROW);
+    constexpr int SRK = 2 * C::NB_ROW * C::SPBK, SRV = 2 * C::NB_ROW * C::SPBV;   // scale-row bytes
+    const __amdgpu_buffer_rsrc_t rks =
+        make_rsrc(C::K_SCALE ? (const void*)(a.k.scales + krow0 * C::NB_ROW * C::SPBK) : (const void*)a.k.data,
+                  C::K_SCALE ? (int64_t)L * SRK : 0);
+    const __amdgpu_buffer_rsrc_t rvs =
+        make_rsrc(C::V_SCALE ? (const void*)(a.v.scales + vrow0 * C::NB_ROW * C::SPBV) : (const void*)a.v.data,
+                  C::V_SCALE ? (int64_t)L * SRV : 0);
 
     // ---- decode step with the new tokens: the workgroup whose split holds
     //      row L-1 (multi-query: each workgroup whose split holds some of the
@@ -372,26 +390,43 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     half8 qop[C::NB];
     floatx4 kbias[C::NB];
     float kmq[C::KMIN ? C::NB : 1];
-    // (run after the first tiles' loads are issued, so they overlap)
-    auto init_q = [&]() {
+    // Q is loaded before the first tiles (load_q) and formed into operands
+    // after they are issued (init_q), so the tiles' loads stay in flight while
+    // it is waited for
+    uint32_t qraw[C::NB][4];
+    auto load_q = [&]() {
         const int c = min(ln, NC - 1);
         const uint16_t* qh = MQ ? a.q + (((int64_t)b * NQ + c / G) * a.Hq + h0 + c % G) * D + wsl * C::DW
                                 : a.q + ((int64_t)b * a.Hq + h0 + c) * D + wsl * C::DW;
+#pragma unroll
+        for (int kb = 0; kb < C::NB; ++kb) {
+            if constexpr (C::KNIB) {
+                const u32x2 ra = *reinterpret_cast<const u32x2*>(qh + 32 * kb + 4 * lq);
+                const u32x2 rb = *reinterpret_cast<const u32x2*>(qh + 32 * kb + 4 * lq + 16);
+                qraw[kb][0] = ra[0];
+                qraw[kb][1] = ra[1];
+                qraw[kb][2] = rb[0];
+                qraw[kb][3] = rb[1];
+            } else {
+                const u32x4 r = *reinterpret_cast<const u32x4*>(qh + 32 * kb + 8 * lq);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) qraw[kb][c] = r[c];
+            }
+        }
+    };
+    auto init_q = [&]() {
         const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
         for (int kb = 0; kb < C::NB; ++kb) {
             uint32_t w[4];
             if constexpr (C::KNIB) {
-                const u32x2 ra = *reinterpret_cast<const u32x2*>(qh + 32 * kb + 4 * lq);
-                const u32x2 rb = *reinterpret_cast<const u32x2*>(qh + 32 * kb + 4 * lq + 16);
-                w[0] = __builtin_amdgcn_perm((uint32_t)ra[1], (uint32_t)ra[0], 0x05040100u);
-                w[1] = __builtin_amdgcn_perm((uint32_t)rb[1], (uint32_t)rb[0], 0x05040100u);
-                w[2] = __builtin_amdgcn_perm((uint32_t)ra[1], (uint32_t)ra[0], 0x07060302u);
-                w[3] = __builtin_amdgcn_perm((uint32_t)rb[1], (uint32_t)rb[0], 0x07060302u);
+                w[0] = __builtin_amdgcn_perm(qraw[kb][1], qraw[kb][0], 0x05040100u);
+                w[1] = __builtin_amdgcn_perm(qraw[kb][3], qraw[kb][2], 0x05040100u);
+                w[2] = __builtin_amdgcn_perm(qraw[kb][1], qraw[kb][0], 0x07060302u);
+                w[3] = __builtin_amdgcn_perm(qraw[kb][3], qraw[kb][2], 0x07060302u);
             } else {
-                const u32x4 r = *reinterpret_cast<const u32x4*>(qh + 32 * kb + 8 * lq);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) w[c] = (uint32_t)r[c];
+                for (int c = 0; c < 4; ++c) w[c] = qraw[kb][c];
             }
             float part = 0.0f;
 #pragma unroll
@@ -432,6 +467,13 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     const int t_lim = MQ ? min(t_end, L - NQ + 1) : t_end;
 
     const int ntiles = (t_end - t_begin + TT - 1) / TT;
+    // Every prefetch is issued on every path, so the compiler's wait counts
+    // are exact and a wait never drains the loads issued after the one it
+    // needs: a prefetch past this wave's last tile reads only out-of-range
+    // rows (zeros, no memory access), and its registers are never read.
+    // First row of tile `it`; a tile past the wave's last one reads rows from
+    // L on, which are all out of range.
+    auto tile_row = [&](int it) -> int { return it < ntiles ? t_begin + it * TT : L; };
     // K row of subtile j read by this lane (tile-relative): rows of the A
     // operand are ordered so that the score layout gives lane row lq the rows
     // 8*lq .. 8*lq+7 of the tile.  Lane (ln, lq) needs k-slots 8*lq .. 8*lq+7
@@ -447,34 +489,42 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     constexpr int KR = C::KDW + C::KHW;            // K dwords per lane and row
     const int krow_rel0 = 8 * (ln >> 2) + (ln & 3);
     const uint32_t kpart = (uint32_t)(lq * (KDIRECT ? QB : BB));
-    const uint32_t krow0o = (uint32_t)(krow_rel0 * C::RBK_ROW);
-    const uint32_t krow1o = (uint32_t)((krow_rel0 + 4) * C::RBK_ROW);
-    // V row chunks and scale words of a tile: 16-byte chunk k*64 + lane of the
-    // slice is row c16 / (RBV/16), column c16 % (RBV/16); scale word k*64 +
-    // lane is row c4 / (NB/2), word c4 % (NB/2)
-    // (whole rows, DS == 1: one contiguous tile, offsets 16*c16 and 4*c4)
+    // Per-lane byte offsets inside a tile (the tile's first row is added per
+    // tile).  V row chunks and scale words of a tile: 16-byte chunk k*64 +
+    // lane of the slice is row c16 / (RBV/16), column c16 % (RBV/16); scale
+    // word k*64 + lane is row c4 / wpr, word c4 % wpr (wpr: words per row of
+    // the slice).  Whole rows (DS == 1) make one contiguous tile: offsets
+    // 16*c16 and 4*c4.
     auto voff = [&](int k) -> uint32_t {
         const int c16 = k * 64 + lane;
         if constexpr (C::DS == 1) return (uint32_t)(16 * lane + 1024 * k);
-        else return (uint32_t)((c16 / (C::RBV / 16)) * C::RBV_ROW + 16 * (c16 % (C::RBV / 16)));
+        else return (uint32_t)((c16 / (C::RBV / 16)) * C::RBV_ROW + wsl * C::RBV + 16 * (c16 % (C::RBV / 16)));
     };
+    auto soff = [&](int k, int spb, int srow) -> uint32_t {
+        const int wpr = C::NB * spb / 2;
+        const int c4 = k * 64 + lane;
+        if constexpr (C::DS == 1) return (uint32_t)(4 * c4);
+        else return (uint32_t)((c4 / wpr) * srow + wsl * C::NB * spb * 2 + 4 * (c4 % wpr));
+    };
+    const uint32_t krow_off[2] = {(uint32_t)(krow_rel0 * C::RBK_ROW + wsl * C::RBK),
+                                  (uint32_t)((krow_rel0 + 4) * C::RBK_ROW + wsl * C::RBK)};
 
-    // one K row's share of this lane (rowp: the row start)
-    auto load_k_row = [&](const uint8_t* rowp, uint32_t (&x)[KR]) {
-        const uint8_t* p = rowp + kpart;
+    // one K row's share of this lane (ro: the row's byte offset in the plane)
+    auto load_k_row = [&](uint32_t ro, uint32_t (&x)[KR]) {
         if constexpr (C::KHB > 0) {
             // the row's high-bit words, after its D/2 nibble bytes
 #pragma unroll
             for (int u = 0; u < C::KHW / 4; ++u) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(rowp + C::DW / 2 + 16 * u);
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rk, ro + C::DW / 2 + 16 * u, 0, 0);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) x[C::KDW + 4 * u + c] = v[c];
             }
         }
+        const uint32_t p = ro + kpart;
         if constexpr (KDIRECT) {
 #pragma unroll
             for (int kb = 0; kb < C::NB; ++kb) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(p + kb * BB);
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rk, p + kb * BB, 0, 0);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) x[4 * kb + c] = v[c];
             }
@@ -483,7 +533,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
             for (int bg = 0; bg < C::NBG; ++bg)
 #pragma unroll
                 for (int u = 0; u < C::KU; ++u) {
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(p + bg * 4 * BB + 16 * u);
+                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rk, p + bg * 4 * BB + 16 * u, 0, 0);
 #pragma unroll
                     for (int c = 0; c < 4; ++c) x[(bg * C::KU + u) * 4 + c] = v[c];
                 }
@@ -492,123 +542,58 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
 
     // ---- global loads of tile `it` into registers: K rows in the MFMA layout
     //      (issue_k), and the V rows and scale rows (issue_vs) that stage()
-    //      then copies to this wave's LDS buffer.  A tile whose rows all lie
-    //      below L is one contiguous range per plane, addressed as a uniform
-    //      tile base plus a per-lane offset; only a split's last tile clamps
-    //      its rows to L - 1 (rows past L are masked out of the softmax).
+    //      then copies to this wave's LDS buffer
     auto issue_k = [&](int it, uint32_t (&kr)[2][KR]) {
-        const int t0 = t_begin + it * TT;
-        if (t0 + TT <= L) {
-            const uint8_t* base = kdata + (uint32_t)(t0 * C::RBK_ROW);
-            load_k_row(base + krow0o, kr[0]);
-            load_k_row(base + krow1o, kr[1]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int tok = min(t0 + krow_rel0 + 4 * j, L - 1);
-                load_k_row(kdata + (uint32_t)(tok * C::RBK_ROW), kr[j]);
-            }
-        }
+        const uint32_t tb = (uint32_t)tile_row(it) * C::RBK_ROW;
+        load_k_row(tb + krow_off[0], kr[0]);
+        load_k_row(tb + krow_off[1], kr[1]);
     };
     // scale words of a tile: the K and V scale planes have SPBK / SPBV fp16
-    // entries per block (scale, then minimum), so a row of the slice has
-    // NB * SPB / 2 words; word k*64 + lane of a plane's tile is row c4 / (NB *
-    // SPB / 2), word c4 % (NB * SPB / 2)
-    // (full: every row of the tile lies below L)
-    auto load_scales = [&](int t0, bool full, const uint8_t* scl, int spb, uint32_t* dst, int nloads) {
-        const int wpr = C::NB * spb / 2;           // words per row (slice)
-        const int wpr_row = C::NB_ROW * spb / 2;   // words per row (whole row)
-        if (full) {
-            const uint32_t sbase = (uint32_t)(t0 * (4 * wpr_row));
+    // entries per block (scale, then minimum)
+    auto load_all_scales = [&](int t0, uint32_t (&sr)[C::S_DW]) {
+        if constexpr (C::K_SCALE) {
+            const uint32_t tb = (uint32_t)t0 * SRK;
 #pragma unroll
-            for (int k = 0; k < nloads; ++k) {
-                const int c4 = k * 64 + lane;
-                const uint32_t o = C::DS == 1 ? (uint32_t)(4 * c4)
-                                              : (uint32_t)((c4 / wpr) * (4 * wpr_row) + 4 * (c4 % wpr));
-                dst[k] = *reinterpret_cast<const uint32_t*>(scl + sbase + o);
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < nloads; ++k) {
-                const int c4 = k * 64 + lane;
-                const int tok = min(t0 + c4 / wpr, L - 1);
-                dst[k] = *reinterpret_cast<const uint32_t*>(scl + (uint32_t)(tok * (4 * wpr_row)) +
-                                                            4 * (c4 % wpr));
-            }
+            for (int k = 0; k < C::SK_LOADS; ++k)
+                sr[k] = __builtin_amdgcn_raw_buffer_load_b32(rks, tb + soff(k, C::SPBK, SRK), 0, 0);
         }
-    };
-    auto load_all_scales = [&](int t0, bool full, uint32_t (&sr)[C::S_DW]) {
-        if constexpr (C::K_SCALE && C::V_SCALE && C::SPBK == C::SPBV) {
-            // both planes alike: one loop, K and V words interleaved
-            const int wpr = C::NB * C::SPBK / 2, wpr_row = C::NB_ROW * C::SPBK / 2;
-            if (full) {
-                const uint32_t sbase = (uint32_t)(t0 * (4 * wpr_row));
+        if constexpr (C::V_SCALE) {
+            const uint32_t tb = (uint32_t)t0 * SRV;
 #pragma unroll
-                for (int k = 0; k < C::SK_LOADS; ++k) {
-                    const int c4 = k * 64 + lane;
-                    const uint32_t o = C::DS == 1 ? (uint32_t)(4 * c4)
-                                                  : (uint32_t)((c4 / wpr) * (4 * wpr_row) + 4 * (c4 % wpr));
-                    sr[k] = *reinterpret_cast<const uint32_t*>(kscl + sbase + o);
-                    sr[C::SK_LOADS + k] = *reinterpret_cast<const uint32_t*>(vscl + sbase + o);
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < C::SK_LOADS; ++k) {
-                    const int c4 = k * 64 + lane;
-                    const int tok = min(t0 + c4 / wpr, L - 1);
-                    const uint32_t off = (uint32_t)(tok * (4 * wpr_row)) + 4 * (c4 % wpr);
-                    sr[k] = *reinterpret_cast<const uint32_t*>(kscl + off);
-                    sr[C::SK_LOADS + k] = *reinterpret_cast<const uint32_t*>(vscl + off);
-                }
-            }
-        } else {
-            if constexpr (C::K_SCALE) load_scales(t0, full, kscl, C::SPBK, sr, C::SK_LOADS);
-            if constexpr (C::V_SCALE) load_scales(t0, full, vscl, C::SPBV, sr + C::SK_LOADS, C::SV_LOADS);
+            for (int k = 0; k < C::SV_LOADS; ++k)
+                sr[C::SK_LOADS + k] = __builtin_amdgcn_raw_buffer_load_b32(rvs, tb + soff(k, C::SPBV, SRV), 0, 0);
         }
     };
     auto issue_vs = [&](int it, uint32_t (&vr)[C::V_DW], uint32_t (&sr)[C::S_DW]) {
-        const int t0 = t_begin + it * TT;
+        const int t0 = tile_row(it);
         if constexpr (C::VBYTES) {
             // unit k*64 + lane = (row u / NB, block u % NB): its 16 nibble
             // bytes and its high-bit words
 #pragma unroll
             for (int k = 0; k < C::V_UNITS; ++k) {
                 const int u = k * 64 + lane;
-                const int tok = min(t0 + u / C::NB, L - 1);
-                const uint8_t* rowp = vdata + (uint32_t)(tok * C::RBV_ROW);
-                const u32x4 v = *reinterpret_cast<const u32x4*>(rowp + 16 * (u % C::NB));
+                const uint32_t ro = (uint32_t)(t0 + u / C::NB) * C::RBV_ROW;
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rv, ro + 16 * (u % C::NB), 0, 0);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) vr[k * (4 + C::VHB) + c] = v[c];
                 if constexpr (C::VHB == 1) {
-                    vr[k * 5 + 4] = *reinterpret_cast<const uint32_t*>(rowp + C::DW / 2 + 4 * (u % C::NB));
+                    vr[k * 5 + 4] = __builtin_amdgcn_raw_buffer_load_b32(rv, ro + C::DW / 2 + 4 * (u % C::NB), 0, 0);
                 } else if constexpr (C::VHB == 2) {
-                    const u32x2 h = *reinterpret_cast<const u32x2*>(rowp + C::DW / 2 + 8 * (u % C::NB));
+                    const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(rv, ro + C::DW / 2 + 8 * (u % C::NB), 0, 0);
                     vr[k * 6 + 4] = h[0];
                     vr[k * 6 + 5] = h[1];
                 }
             }
-            load_all_scales(t0, t0 + TT <= L, sr);
-        } else if (t0 + TT <= L) {
-            const uint8_t* vbase = vdata + (uint32_t)(t0 * C::RBV_ROW);
-#pragma unroll
-            for (int k = 0; k < C::V_LOADS; ++k) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(vbase + voff(k));
-#pragma unroll
-                for (int c = 0; c < 4; ++c) vr[4 * k + c] = v[c];
-            }
-            load_all_scales(t0, true, sr);
         } else {
+            const uint32_t tb = (uint32_t)t0 * C::RBV_ROW;
 #pragma unroll
             for (int k = 0; k < C::V_LOADS; ++k) {
-                const int c16 = k * 64 + lane;
-                const int tok = min(t0 + c16 / (C::RBV / 16), L - 1);
-                const u32x4 v = *reinterpret_cast<const u32x4*>(
-                    vdata + (uint32_t)(tok * C::RBV_ROW) + 16 * (c16 % (C::RBV / 16)));
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rv, tb + voff(k), 0, 0);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) vr[4 * k + c] = v[c];
             }
-            load_all_scales(t0, false, sr);
         }
+        load_all_scales(t0, sr);
     };
 
     // one (row, block) unit of a further type as 32 unsigned code bytes
@@ -783,7 +768,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
             sacc[j] = sc;
         }
         // the K registers are free: start loading the next tile's K rows
-        if (next_it < ntiles) issue_k(next_it, kr);
+        issue_k(next_it, kr);
 
         if constexpr (C::DS > 1) {
             // each wave holds the scores over its head-dim slice: sum the
@@ -947,35 +932,35 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     uint32_t krs[NS][2][KR];
     uint32_t vrs[NS][C::V_DW];
     uint32_t srs[NS][C::S_DW];
+    load_q();
     if (it < ntiles) {
 #pragma unroll
-        for (int x = 0; x < NS; ++x)
-            if (it + x * W < ntiles) {
-                issue_k(it + x * W, krs[x]);
-                issue_vs(it + x * W, vrs[x], srs[x]);
-            }
+        for (int x = 0; x < NS; ++x) {
+            issue_k(it + x * W, krs[x]);
+            issue_vs(it + x * W, vrs[x], srs[x]);
+        }
     }
     init_q();
     if (it < ntiles) {
         stage(vrs[0], srs[0]);
-        if (it + NS * W < ntiles) issue_vs(it + NS * W, vrs[0], srs[0]);
+        issue_vs(it + NS * W, vrs[0], srs[0]);
     }
     // tile it uses K set x; V of tile it is in LDS, V of the next tile in set
-    // (x + 1) % NS
-    bool done = it >= ntiles;
-    while (!done) {
+    // (x + 1) % NS.  The loop runs whole rounds of the ring with no branch
+    // around a load, so the compiler's wait before each use counts exactly
+    // the loads issued after it.  A slot past the wave's last tile (at most
+    // NS - 1 per wave) runs on rows at or past L: its loads are out of range
+    // (zeros, no memory access) and every row is masked out of the softmax.
+    if (it < ntiles) {
+        const int rounds = ((ntiles - it + W - 1) / W + NS - 1) / NS;
+        for (int r = 0; r < rounds; ++r) {
 #pragma unroll
-        for (int x = 0; x < NS; ++x) {
-            if (!done) {
+            for (int x = 0; x < NS; ++x) {
                 compute(it, krs[x], it + NS * W);
-                if (it + W >= ntiles) {
-                    done = true;
-                } else {
-                    const int y = (x + 1) % NS;
-                    stage(vrs[y], srs[y]);
-                    if (it + (NS + 1) * W < ntiles) issue_vs(it + (NS + 1) * W, vrs[y], srs[y]);
-                    it += W;
-                }
+                const int y = (x + 1) % NS;
+                stage(vrs[y], srs[y]);
+                issue_vs(it + (NS + 1) * W, vrs[y], srs[y]);
+                it += W;
             }
         }
     }

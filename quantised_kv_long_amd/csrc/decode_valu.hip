@@ -41,11 +41,9 @@ __global__ void __launch_bounds__(NT) decode_valu_kernel(DecodeArgs a)
     float* po = a.part_o + (((int64_t)b * a.Hq + h0) * a.max_splits + s) * D;
     float* pl = a.part_lse + ((int64_t)b * a.Hq + h0) * a.max_splits + s;
 
-    if (t_begin >= t_end) {
-        for (int i = tid; i < G * D; i += NT) po[(i / D) * ho_stride + (i % D)] = 0.0f;
-        if (tid < G) pl[(int64_t)tid * a.max_splits] = -INFINITY;
-        return;
-    }
+    // a split at or past ceil(L / split_tokens) holds no row: the merge never
+    // reads its partials, so nothing is written
+    if (t_begin >= t_end) return;
 
     extern __shared__ float smem[];
     float* qs = smem;                // [GP][D]   Q * scale * log2(e)

@@ -11,7 +11,7 @@ import pytest
 
 from oracle import oracle as O
 
-from .gpu_util import (assert_close, fill_pair, note, oracle_threads, planes_to_oracle, require_gpu,
+from .gpu_util import (assert_close, assert_partials, fill_pair, note, oracle_threads, planes_to_oracle,
                        run_decode, to_host_u16)
 from .test_oracle_quant_n3 import WORKED as WORKED_N3
 
@@ -157,10 +157,7 @@ def test_decode_matches_oracle(tk, tv, case, variant):
     # the split partials too
     ro, rl = O.attend_split(to_host_u16(q), planes_to_oracle(kc), planes_to_oracle(vc), lens, Hkv,
                             1 / math.sqrt(D), st, po.shape[2])
-    live = np.isfinite(rl)
-    assert np.array_equal(np.isfinite(pl), live)
-    assert np.all(np.abs(pl[live] - rl[live]) <= 1e-4)
-    assert np.all(np.abs(po - ro) <= 2e-3 + 1e-2 * np.abs(ro))
+    assert_partials(po, pl, ro, rl, lens, st)
 
 
 def test_matrix_core_kernel_reports_what_it_does_not_cover():
