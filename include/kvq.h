@@ -97,7 +97,8 @@ enum {
  *     b * seq_stride_rows + g * head_stride_rows + t
  * in both planes; rows t in [0, capacity) are addressable.  The usual layout
  * is head_stride_rows = capacity, seq_stride_rows = Hkv * capacity.
- * Alignment: data and scales must be 16-byte aligned.
+ * Alignment: the data plane must be 16-byte aligned, the scale plane 4-byte
+ * aligned.
  */
 typedef struct {
     int32_t type;             /* kvq_type                                   */
@@ -303,8 +304,7 @@ int kvq_decode_step_multi(const kvq_plane_desc* k_cache, const kvq_plane_desc* v
                           void* stream);
 
 /* Kernel family for kvq_decode_attn_variant.  The matrix-core kernel covers
- * every pair of f16, q8_0 and q4_0 at D = 128, 256 and 512 (except f16 V
- * with a quantised K at D = 256, whose LDS tiles do not fit), and
+ * every pair of f16, q8_0 and q4_0 at D = 128, 256 and 512, and
  * at D = 128 the pairs q8_0/q6_0, q8_0/q5_0, q6_0/q6_0, q6_0/q4_0,
  * q5_0/q5_0, q5_1/q5_1, q4_1/q4_1 and q5_1/q4_0.  The vector-ALU kernel
  * covers every pair of types at every valid D; AUTO picks the matrix cores
@@ -433,12 +433,17 @@ int kvq_combine_regions(int n_regions, const float* const* part_o, const float* 
  *
  * Results equal kvq_quantize_append (one new row per sequence, written at row
  * seq_lens[b] - 1) followed by kvq_decode_attn and kvq_combine with the same
- * arguments: the cache rows are bit-identical, the split partials are the
- * same, and out / lse_out agree within floating-point rounding.  Where the
- * matrix-core kernel covers the call (see KVQ_VARIANT_MFMA) the step is two
- * kernel launches: the attention kernel's workgroup whose split holds row
- * seq_lens[b] - 1 writes that row before it reads it, then the merge runs.
- * Other calls run the three kernels in order.
+ * arguments: the cache rows are bit-identical, and the split partials and
+ * out / lse_out agree within floating-point rounding.  Where the matrix-core
+ * kernel covers the call (see KVQ_VARIANT_MFMA) the step is two kernel
+ * launches: attention, then the merge.  The attention kernel's workgroup whose
+ * split holds row seq_lens[b] - 1 writes that row; at head_dim 128 (types
+ * f16, q8_0, q4_0) it takes the row's decoded values straight from its
+ * quantiser as one more term of its split, with an fp32 weight where the
+ * three calls round that row's weight to fp16 for the matrix cores (the two
+ * differ by at most 2^-11 of the weight times the row's largest value); at
+ * other head dims it reads the row back after writing it.  Other calls run
+ * the three kernels in order.
  *
  *   k_new, v_new : device, [B][Hkv][D] binary16: the new token's K and V rows.
  *   seq_lens     : device, [B] int32: lengths *including* the new token,

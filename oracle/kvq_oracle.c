@@ -410,7 +410,11 @@ static double deq(int type, const uint8_t* data, const uint16_t* scales,
     int b = i / 32, e = i % 32;
     uint8_t byte = data[r * (D / 2) + 16 * b + (e % 16)];
     int n = e < 16 ? (byte & 0x0f) : (byte >> 4);
+#if KVO_MUTANT == 12
+    return d * (double)(n - 7);                   /* planted: q4_0 offset off by one */
+#else
     return d * (double)(n - 8);
+#endif
 }
 
 /* Whole row r dequantised into out[0..D) (the same values as deq()). */
@@ -457,7 +461,11 @@ typedef struct {
 static void attend_region(const attn_job* J, int b, int h, int t0, int t1,
                           double* o, double* lse, double* s, double* row)
 {
+#if KVO_MUTANT == 9
+    int D = J->D, g = h % J->Hkv;                 /* planted: heads interleaved over KV heads */
+#else
     int D = J->D, G = J->Hq / J->Hkv, g = h / G;
+#endif
     int64_t row0 = ((int64_t)b * J->Hkv + g) * J->capacity;
     for (int i = 0; i < D; ++i) o[i] = 0.0;
     if (t1 <= t0) { *lse = -INFINITY; return; }
@@ -469,14 +477,22 @@ static void attend_region(const attn_job* J, int b, int h, int t0, int t1,
         deq_row(J->tK, J->k_data, J->k_scales, row0 + t, D, row);
         double acc = 0.0;
         for (int i = 0; i < D; ++i) acc += qd[i] * row[i];
+#if KVO_MUTANT == 10
+        s[t - t0] = acc;                          /* planted: softmax scale dropped */
+#else
         s[t - t0] = J->scale * acc;
+#endif
         if (s[t - t0] > m) m = s[t - t0];
     }
     double l = 0.0;
     for (int t = t0; t < t1; ++t) {
         double p = exp(s[t - t0] - m);
         l += p;
+#if KVO_MUTANT == 11
+        deq_row(J->tK, J->k_data, J->k_scales, row0 + t, D, row);   /* planted: V read from K */
+#else
         deq_row(J->tV, J->v_data, J->v_scales, row0 + t, D, row);
+#endif
         for (int i = 0; i < D; ++i) o[i] += p * row[i];
     }
     for (int i = 0; i < D; ++i) o[i] /= l;

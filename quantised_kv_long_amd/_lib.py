@@ -311,3 +311,4 @@ def kvq_decode_step(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, k_new, v_n
                                 _ptr(part_o), _ptr(part_lse), ot, _ptr(out),
                                 _ptr(lse_out), _stream(stream))
     return _check("kvq_decode_step", rc)
+

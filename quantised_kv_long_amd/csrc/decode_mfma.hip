@@ -216,6 +216,9 @@ struct Cfg {
     // the V code offset as an fp16 subnormal pair (0: no offset, min types)
     static constexpr uint32_t VOFF_BITS = TV == T_Q4 ? 0x00080008u : TV == T_Q8 ? 0x00800080u
                                         : TV == T_Q5_0 ? 0x00100010u : TV == T_Q6_0 ? 0x00200020u : 0u;
+    // a decode step's new row merged from registers (whole 128-wide rows of
+    // the base types: one value per thread, 2 * NB_ROW blocks of 32)
+    static constexpr bool NEWROW = DS == 1 && !NEWT && NTH == 2 * NB_ROW * 32;
     static constexpr bool VALID = V_BYTES % 1024 == 0 && SK_BYTES % 256 == 0 && SV_BYTES % 256 == 0 &&
                                   (!VBYTES || (TT * NB) % 64 == 0) && V_DW <= (DW == 128 ? 32 : 64) &&
                                   WV * BUF <= 64 * 1024 && (!NEWT || (D == 128 && DS == 1));
@@ -257,7 +260,7 @@ __device__ __forceinline__ void write_block_lanes_d(const uint16_t* src, const P
 template <int TK, int TV, int D, bool MQ>
 __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint8_t* const lds_a,
                                           const size_t lds_cap, float* const lds_sx,
-                                          uint8_t* const lds_merge_dyn)
+                                          uint8_t* const lds_merge_dyn, float* const lds_new)
 {
     using C = Cfg<TK, TV, D>;
     const int g = blockIdx.y, b = blockIdx.z;
@@ -273,7 +276,15 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     const int NQ = MQ ? a.nq : 1, NC = NQ * G;
     const int L = a.seq_lens[b];
     const int t_begin = s * a.split_tokens;
-    const int t_end = min(t_begin + a.split_tokens, L);
+    const int t_end_all = min(t_begin + a.split_tokens, L);
+    // Decode step with one new token over whole 128-wide rows (NEWROW): the
+    // workgroup whose split holds row L-1 leaves that row out of its tiles,
+    // quantises the new row into it after its tile loop, and merges the row's
+    // decoded values as one more term, so no load waits for those stores.
+    constexpr bool NEWROW_OK = C::NEWROW && !MQ;
+    const bool newrow = NEWROW_OK && a.k_new != nullptr && t_end_all == L;
+    const int Lr = newrow ? L - 1 : L;             // rows the tiles read
+    const int t_end = min(t_begin + a.split_tokens, Lr);
     const int h0 = g * G;
     const int64_t ho_stride = (int64_t)a.max_splits * D;
     const int64_t HQT = (int64_t)NQ * a.Hq;        // rows of the partials' head axis
@@ -284,7 +295,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
 
     // a split at or past ceil(L / split_tokens) holds no row: the merge never
     // reads its partials, so nothing is written
-    if (t_begin >= t_end) return;
+    if (t_begin >= t_end_all) return;
 
     const int64_t krow0 = (int64_t)b * a.k.seq_stride + (int64_t)g * a.k.head_stride;
     const int64_t vrow0 = (int64_t)b * a.v.seq_stride + (int64_t)g * a.v.head_stride;
@@ -299,15 +310,15 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     auto make_rsrc = [](const void* p, int64_t bytes) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
     };
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k.data + krow0 * C::RBK_ROW, (int64_t)L * C::RBK_ROW);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v.data + vrow0 * C::RBV_ROW, (int64_t)L * C::RBV_ROW);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k.data + krow0 * C::RBK_ROW, (int64_t)Lr * C::RBK_ROW);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v.data + vrow0 * C::RBV_ROW, (int64_t)Lr * C::RBV_ROW);
     constexpr int SRK = 2 * C::NB_ROW * C::SPBK, SRV = 2 * C::NB_ROW * C::SPBV;   // scale-row bytes
     const __amdgpu_buffer_rsrc_t rks =
         make_rsrc(C::K_SCALE ? (const void*)(a.k.scales + krow0 * C::NB_ROW * C::SPBK) : (const void*)a.k.data,
-                  C::K_SCALE ? (int64_t)L * SRK : 0);
+                  C::K_SCALE ? (int64_t)Lr * SRK : 0);
     const __amdgpu_buffer_rsrc_t rvs =
         make_rsrc(C::V_SCALE ? (const void*)(a.v.scales + vrow0 * C::NB_ROW * C::SPBV) : (const void*)a.v.data,
-                  C::V_SCALE ? (int64_t)L * SRV : 0);
+                  C::V_SCALE ? (int64_t)Lr * SRV : 0);
 
     // ---- decode step with the new tokens: the workgroup whose split holds
     //      row L-1 (multi-query: each workgroup whose split holds some of the
@@ -335,7 +346,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
             __builtin_amdgcn_s_waitcnt(VMCNT0);
             __syncthreads();
         }
-    } else if (a.k_new != nullptr && t_end == L) {
+    } else if (!NEWROW_OK && a.k_new != nullptr && t_end == L) {
         // 2*NB_ROW blocks (K then V), one aligned half-wave of 32 lanes per block
         if constexpr (C::NEWT) {
             for (int blk2 = tid >> 5; blk2 < 2 * C::NB_ROW; blk2 += C::NTH / 32) {
@@ -472,8 +483,8 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     // needs: a prefetch past this wave's last tile reads only out-of-range
     // rows (zeros, no memory access), and its registers are never read.
     // First row of tile `it`; a tile past the wave's last one reads rows from
-    // L on, which are all out of range.
-    auto tile_row = [&](int it) -> int { return it < ntiles ? t_begin + it * TT : L; };
+    // Lr on, which are all out of range.
+    auto tile_row = [&](int it) -> int { return it < ntiles ? t_begin + it * TT : Lr; };
     // K row of subtile j read by this lane (tile-relative): rows of the A
     // operand are ordered so that the score layout gives lane row lq the rows
     // 8*lq .. 8*lq+7 of the tile.  Lane (ln, lq) needs k-slots 8*lq .. 8*lq+7
@@ -932,6 +943,17 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     uint32_t krs[NS][2][KR];
     uint32_t vrs[NS][C::V_DW];
     uint32_t srs[NS][C::S_DW];
+    // the new row's value of this thread (element tid & 31 of block tid >> 5:
+    // K blocks, then V blocks), loaded first so it arrives with the tiles
+    uint16_t xnew = 0;
+    if constexpr (NEWROW_OK) {
+        if (newrow) {
+            const int blk2 = tid >> 5;
+            const bool isv = blk2 >= C::NB_ROW;
+            xnew = ((isv ? a.v_new : a.k_new) + ((int64_t)b * a.Hkv + g) * D + 32 * (isv ? blk2 - C::NB_ROW : blk2))
+                [tid & 31];
+        }
+    }
     load_q();
     if (it < ntiles) {
 #pragma unroll
@@ -1005,7 +1027,44 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     //      code-offset correction of its block), so each output column is a
     //      four-term weighted sum with no second barrier.
     const float l_head = xsum4(l_part);
+    // the new row: quantised into row L-1 (the block quantiser of
+    // kvq_quantize_append, bit for bit), its decoded values (scale * code,
+    // exact) kept in lds_new: K in [0, D), V in [D, 2D); its scores in
+    // lds_new[2D + column], log2 units
+    if constexpr (NEWROW_OK) {
+        if (newrow) {
+            const int blk2 = tid >> 5, j = tid & 31;
+            const bool isv = blk2 >= C::NB_ROW;
+            const int blk = isv ? blk2 - C::NB_ROW : blk2;
+            const int64_t row = (isv ? vrow0 : krow0) + (L - 1);
+            lds_new[tid] = isv ? quantize_block_lanes_v<TV>(xnew, a.v.data + row * rb(TV, D) + blk * rb(TV, 32),
+                                                           a.v.scales + row * (D / 32) + blk, j)
+                               : quantize_block_lanes_v<TK>(xnew, a.k.data + row * rb(TK, D) + blk * rb(TK, 32),
+                                                           a.k.scales + row * (D / 32) + blk, j);
+        }
+    }
     __syncthreads();
+    if constexpr (NEWROW_OK) {
+        if (newrow && wave == 0) {
+            // score of column ln: Q (the MFMA operand, k-slot e of block kb
+            // holds element 32 kb + kel(e)) times the decoded K row
+            float acc = 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < C::NB; ++kb) {
+                const u32x4 qu = __builtin_bit_cast(u32x4, qop[kb]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t w2 = (uint32_t)qu[e >> 1];
+                    const half2v h2 = __builtin_bit_cast(half2v, w2);
+                    const int kel = C::KNIB ? 4 * lq + ((e & 1) ? 2 : 0) + ((e & 2) ? 16 : 0) + (e >> 2)
+                                            : 8 * lq + e;
+                    acc = fmaf((float)h2[e & 1], lds_new[32 * kb + kel], acc);
+                }
+            }
+            acc = xsum4(acc);
+            if (lq == 0) lds_new[2 * D + ln] = acc * a.scale_log2;
+        }
+    }
     uint8_t* marea = merge_lds_bytes<TK, TV, D>(NC) <= lds_cap ? lds_a : lds_merge_dyn;
     float* mw = reinterpret_cast<float*>(marea);          // [WAVES][16]   running max
     float* lw = mw + WAVES * 16;                          // [WAVES][16]   running sum
@@ -1043,12 +1102,17 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) M = fmaxf(M, mw[w * 16 + n]);
+        // the new row's term: max m_new, sum 1, row v (decoded)
+        const float m_new = NEWROW_OK && newrow ? lds_new[2 * D + n] : -INFINITY;
+        M = fmaxf(M, m_new);
         float f[WAVES], lsum = 0.0f;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
             f[w] = exp2f(mw[w * 16 + n] - M);     // 0 for waves that saw no row (m at the floor)
             lsum += f[w] * lw[w * 16 + n];
         }
+        const float f_new = NEWROW_OK && newrow ? exp2f(m_new - M) : 0.0f;
+        lsum += f_new;
         // quantised V: O = (acc - offset sum) * 2^24 (no row at all: o = 0,
         // lse = -inf)
         const float inv = lsum > 0.0f ? (C::V_SCALE ? TWO24 : 1.0f) / lsum : 0.0f;
@@ -1070,6 +1134,16 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
             o.z -= c;
             o.w -= c;
         }
+        if constexpr (NEWROW_OK) {
+            if (newrow) {
+                const float fn = f_new / lsum;
+                const float4 v = reinterpret_cast<const float4*>(lds_new + D)[c4];
+                o.x = fmaf(fn, v.x, o.x);
+                o.y = fmaf(fn, v.y, o.y);
+                o.z = fmaf(fn, v.z, o.z);
+                o.w = fmaf(fn, v.w, o.w);
+            }
+        }
         reinterpret_cast<float4*>(po + crow(n) * ho_stride)[c4] = o;
         if (c4 == 0) pl[crow(n) * a.max_splits] = (M + log2f(lsum)) * 0.69314718055994531f;
     }
@@ -1082,8 +1156,9 @@ decode_mfma_kernel(DecodeArgs a)
     using C = Cfg<TK, TV, D>;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[C::WV * C::BUF];
     __shared__ __attribute__((aligned(16))) float lds_sx[C::SX_FLOATS];
+    __shared__ __attribute__((aligned(16))) float lds_new[C::NEWROW && !MQ ? 2 * D + 16 : 1];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
-    decode_wg<TK, TV, D, MQ>(a, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn);
+    decode_wg<TK, TV, D, MQ>(a, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn, lds_new);
 }
 
 // The two regions of a mixed cache in one launch (HAL #582 section 5 P2): the
@@ -1108,12 +1183,14 @@ decode_mfma_dual_kernel(DecodeArgs t, DecodeArgs w)
     using DC = DualCfg<TK, TV, D>;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[DC::BUF];
     __shared__ __attribute__((aligned(16))) float lds_sx[DC::SX];
+    __shared__ __attribute__((aligned(16))) float lds_new[DC::F::NEWROW || DC::T::NEWROW ? 2 * D + 16 : 1];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
     const int ts = grid_splits(t);  // the first ts workgroups of each row take the tail
     if ((int)blockIdx.x < ts)
-        decode_wg<TK, TV, D, false>(t, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn);
+        decode_wg<TK, TV, D, false>(t, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn, lds_new);
     else
-        decode_wg<T_F16, T_F16, D, false>(w, blockIdx.x - ts, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn);
+        decode_wg<T_F16, T_F16, D, false>(w, blockIdx.x - ts, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn,
+                                          lds_new);
 }
 
 template <int TK, int TV, int D>
@@ -1133,7 +1210,8 @@ template <int TK, int TV, int D>
 size_t lds_bytes(int nc)
 {
     using C = Cfg<TK, TV, D>;
-    return (size_t)C::WV * C::BUF + sizeof(float) * C::SX_FLOATS + dyn_lds_bytes<TK, TV, D>(nc);
+    return (size_t)C::WV * C::BUF + sizeof(float) * (C::SX_FLOATS + (C::NEWROW ? 2 * D + 16 : 1)) +
+           dyn_lds_bytes<TK, TV, D>(nc);
 }
 
 template <int TK, int TV, int D, bool MQ>
@@ -1217,7 +1295,8 @@ bool dual_supports3(const DecodeArgs& t)
     if constexpr (!DC::VALID) {
         return false;
     } else {
-        return (size_t)DC::BUF + sizeof(float) * DC::SX + dual_dyn_bytes<TK, TV, D>(t.G) <= 160 * 1024;
+        return (size_t)DC::BUF + sizeof(float) * (DC::SX + 2 * D + 16) + dual_dyn_bytes<TK, TV, D>(t.G) <=
+               160 * 1024;
     }
 }
 
@@ -1229,7 +1308,7 @@ hipError_t launch_dual3(const DecodeArgs& t, const DecodeArgs& w, hipStream_t s)
         return hipErrorInvalidConfiguration;
     } else {
         const size_t dyn = dual_dyn_bytes<TK, TV, D>(t.G);
-        if ((size_t)DC::BUF + sizeof(float) * DC::SX + dyn > 64 * 1024) {
+        if ((size_t)DC::BUF + sizeof(float) * (DC::SX + 2 * D + 16) + dyn > 64 * 1024) {
             const hipError_t e = hipFuncSetAttribute(
                 reinterpret_cast<const void*>(&decode_mfma_dual_kernel<TK, TV, D>),
                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);

@@ -24,7 +24,7 @@ int check_plane(const kvq_plane_desc* p, int B, int Hkv, int64_t rows_needed)
     if (!known_type(p->type)) return KVQ_ERR_TYPE;
     if (!p->data) return KVQ_ERR_NULL;
     if (p->type != KVQ_F16 && !p->scales) return KVQ_ERR_NULL;
-    if (!aligned(p->data, 16) || (p->scales && !aligned(p->scales, 16))) return KVQ_ERR_ALIGN;
+    if (!aligned(p->data, 16) || (p->scales && !aligned(p->scales, 4))) return KVQ_ERR_ALIGN;
     if (p->capacity < 0 || p->seq_stride_rows < 0 || p->head_stride_rows < 0) return KVQ_ERR_SHAPE;
     if (B > 1 && p->seq_stride_rows == 0) return KVQ_ERR_SHAPE;
     if (Hkv > 1 && p->head_stride_rows == 0) return KVQ_ERR_SHAPE;
@@ -93,6 +93,26 @@ kvq::DecodeArgs decode_args(const kvq_plane_desc* k_cache, const kvq_plane_desc*
 }
 
 }  // namespace
+
+namespace kvq {
+
+int validate_step(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache, const void* k_new,
+                  const void* v_new, const void* q, const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                  float softmax_scale, int max_seq_len, int split_tokens, int max_splits, const float* part_o,
+                  const float* part_lse, int out_type, const void* out, const float* lse_out)
+{
+    const int rc = validate_decode(k_cache, v_cache, q, seq_lens, B, Hq, Hkv, D, softmax_scale, max_seq_len,
+                                   split_tokens, max_splits, part_o, part_lse);
+    if (rc != KVQ_OK) return rc;
+    if (!k_new || !v_new || !out) return KVQ_ERR_NULL;
+    if (out_type != KVQ_F16 && out_type != KVQ_OUT_F32) return KVQ_ERR_TYPE;
+    if (B > 65535 || Hq > 65535) return KVQ_ERR_SHAPE;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
+        return KVQ_ERR_ALIGN;
+    return KVQ_OK;
+}
+
+}  // namespace kvq
 
 extern "C" {
 
@@ -535,15 +555,10 @@ int kvq_decode_step(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache
                     float* part_o, float* part_lse, int out_type, void* out, float* lse_out,
                     void* stream)
 {
-    const int rc = validate_decode(k_cache, v_cache, q, seq_lens, B, Hq, Hkv, D, softmax_scale,
-                                   max_seq_len, split_tokens, max_splits, part_o, part_lse);
+    const int rc = kvq::validate_step(k_cache, v_cache, k_new, v_new, q, seq_lens, B, Hq, Hkv, D,
+                                      softmax_scale, max_seq_len, split_tokens, max_splits, part_o,
+                                      part_lse, out_type, out, lse_out);
     if (rc != KVQ_OK) return rc;
-    if (!k_new || !v_new || !out) return KVQ_ERR_NULL;
-    if (out_type != KVQ_F16 && out_type != KVQ_OUT_F32) return KVQ_ERR_TYPE;
-    if (B > 65535 || Hq > 65535) return KVQ_ERR_SHAPE;
-    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16) ||
-        (lse_out && !aligned(lse_out, 4)))
-        return KVQ_ERR_ALIGN;
 
     kvq::DecodeArgs a = decode_args(k_cache, v_cache, q, seq_lens, B, Hq, Hkv, D, softmax_scale,
                                     max_seq_len, split_tokens, max_splits, part_o, part_lse);

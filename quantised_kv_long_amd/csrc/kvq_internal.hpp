@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kvq.h"
 #include "kvq_device.hpp"
 
 namespace kvq {
@@ -79,6 +80,13 @@ struct CombineArgs {
     void* out;
     float* lse_out;
 };
+
+// Every host-side check of kvq_decode_step (no HIP call); KVQ_OK or the
+// status the call returns.
+int validate_step(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache, const void* k_new,
+                  const void* v_new, const void* q, const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                  float softmax_scale, int max_seq_len, int split_tokens, int max_splits, const float* part_o,
+                  const float* part_lse, int out_type, const void* out, const float* lse_out);
 
 hipError_t launch_quantize_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t s);

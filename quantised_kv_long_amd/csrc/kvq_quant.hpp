@@ -213,14 +213,15 @@ __device__ __forceinline__ void quantize_block_ext(const uint16_t* __restrict__ 
 // identical.  All 32 lanes of the half-wave must call it together.
 // quantize_block_lanes_v takes the lane's value xh (element j of the block,
 // fp16 bits) already loaded, so a caller can issue the loads of several
-// blocks before quantising any of them.
+// blocks before quantising any of them.  It returns the value the stored
+// bytes decode to for element j (scale * code, exact in fp32).
 template <int T>
-__device__ __forceinline__ void quantize_block_lanes_v(uint16_t xh, uint8_t* __restrict__ dst,
-                                                       uint16_t* __restrict__ sdst, int j)
+__device__ __forceinline__ float quantize_block_lanes_v(uint16_t xh, uint8_t* __restrict__ dst,
+                                                        uint16_t* __restrict__ sdst, int j)
 {
     if constexpr (T == T_F16) {
         reinterpret_cast<uint16_t*>(dst)[j] = xh;
-        return;
+        return h2f(xh);
     } else {
         const float x = h2f(xh);
         if constexpr (T == T_Q8) {
@@ -239,6 +240,7 @@ __device__ __forceinline__ void quantize_block_lanes_v(uint16_t xh, uint8_t* __r
                                (__shfl_down(c, 3, 32) << 24);
             if ((j & 3) == 0) *reinterpret_cast<uint32_t*>(dst + j) = w;
             if (j == 0) *sdst = d16;
+            return d * (float)(int8_t)c;
         } else {
             // first value of largest magnitude: a value is a candidate when
             // its magnitude exceeds 0 (NaN never is); larger magnitude wins,
@@ -273,6 +275,7 @@ __device__ __forceinline__ void quantize_block_lanes_v(uint16_t xh, uint8_t* __r
                                ((__shfl_down(byte, 3, 32) & 0xff) << 24);
             if (j < 16 && (j & 3) == 0) *reinterpret_cast<uint32_t*>(dst + j) = w;
             if (j == 0) *sdst = d16;
+            return d * (float)((int)n - 8);
         }
     }
 }

@@ -159,3 +159,79 @@ def assert_partials(po, pl, ro, rl, lens, split_tokens):
     assert np.all(np.isnan(pl[~live])) and np.all(np.isnan(po[~live])), "a split with no row was written"
     assert np.all(np.abs(pl[live] - rl[live]) <= 1e-4)
     assert np.all(np.abs(po[live] - ro[live]) <= 2e-3 + 1e-2 * np.abs(ro[live]))
+
+
+def gpu_row_scores(kc, vc, q_rows, g, n_rows, scale, chunk=32768):
+    """The attention kernel's own score of every row t < n_rows of KV head g
+    (sequence 0) for the query rows q_rows ((G, D) fp16 on the device).  Each
+    row is presented as a sequence of length 1 through a plane view whose
+    sequence stride is one row, so the log-sum-exp of that one-row split is
+    the kernel's score of the row.  Returns (G, n_rows) float64."""
+    from quantised_kv_long_amd import _lib
+    G, D = q_rows.shape
+    dev = q_rows.device
+    out = np.empty((G, n_rows))
+
+    def view(p, t0):
+        rb = _lib.kvq_data_row_bytes(p.type, D)
+        sb = _lib.kvq_scale_row_bytes(p.type, D)
+        row0 = g * p.capacity + t0
+        return _lib.kvq_plane_desc(p.type, 1, p.data.data_ptr() + row0 * rb,
+                                   p.scales.data_ptr() + row0 * sb if p.scales is not None else None, 1, 0)
+
+    for t0 in range(0, n_rows, chunk):
+        nb = min(chunk, n_rows - t0)
+        q = q_rows.unsqueeze(0).expand(nb, G, D).contiguous()
+        lens = torch.ones(nb, dtype=torch.int32, device=dev)
+        po = torch.empty((nb, G, 1, D), dtype=torch.float32, device=dev)
+        pl = torch.empty((nb, G, 1), dtype=torch.float32, device=dev)
+        _lib.kvq_decode_attn(view(kc, t0), view(vc, t0), q, lens, nb, G, 1, D, scale, 1, 64, 1, po, pl)
+        torch.cuda.synchronize()
+        out[:, t0:t0 + nb] = pl[:, :, 0].T.cpu().numpy()
+    return out
+
+
+def oracle_row_scores(kc, q_rows_u16, g, n_rows, scale):
+    """The oracle's fp64 scores scale * q . k_t of rows t < n_rows of KV head g
+    (sequence 0) for the query rows q_rows ((G, D) fp16 bits): the plain
+    definition over the oracle's dequantised rows."""
+    name, data, scales = planes_to_oracle(kc)
+    D = q_rows_u16.shape[-1]
+    k = O.dequantize(name, data[0, g, :n_rows], scales[0, g, :n_rows], D)     # (n, D) fp64
+    qf = q_rows_u16.view(np.float16).astype(np.float64)                          # (G, D)
+    return scale * (qf @ k.T)
+
+
+def assert_step_matches_three_calls(out_step, lse_step, out_three, lse_three, v_new_max, what=""):
+    """A decode step against the same step as three calls.  The step merges the
+    new row as one term: its score is the fp32 sum of q times the decoded
+    row, its weight w an fp32 value.  The attention launch reads the row back
+    inside a tile: the weight enters the matrix-core product rounded to fp16
+    (relative error up to 2^-11), and a quantised K row's score is summed on
+    the matrix cores as (code + offset) * q, the offset removed afterwards,
+    whose fp32 cancellation costs up to about 2^-24 * 32 * (15 + 8) * |q| *
+    |scale| per block (a few 1e-6 to 1e-5 here).  So the outputs of head h
+    differ by at most 2^-11 * w * max|v_new| (w <= 1) plus a relative 1e-4
+    from the weights' score errors; the LSEs by 5e-5.  v_new_max: (B, Hq) the
+    largest |value| of the new V row each head reads."""
+    a = np.asarray(out_step, np.float64)
+    c = np.asarray(out_three, np.float64)
+    assert np.array_equal(np.isfinite(a), np.isfinite(c)), what
+    bound = 2e-6 + 1e-4 * np.abs(c) + 2.0 ** -11 * np.asarray(v_new_max, np.float64)[..., None]
+    err = np.abs(a - c)
+    f = np.isfinite(c)
+    assert np.all(err[f] <= bound[f]), f"{what}: step and three calls differ by {err[f].max():.3g}"
+    la, lc = np.asarray(lse_step, np.float64), np.asarray(lse_three, np.float64)
+    assert np.array_equal(np.isneginf(la), np.isneginf(lc)), what
+    g = np.isfinite(lc)
+    d = np.abs(la[g] - lc[g])
+    assert np.all(d <= 5e-5 + 2e-6 * np.abs(lc[g])), f"{what}: LSE differs by {d.max():.3g}"
+
+
+def new_row_vmax(v_new, G):
+    """(B, Hq) the largest |value| of the new V row (B, Hkv, D) fp16 read by
+    each query head (head h reads KV head h // G), with room for the
+    quantised row's rounding (|v_hat| <= |v| * (1 + 1/14) for q4_0's
+    clamped codes)."""
+    m = v_new.float().abs().amax(dim=-1).cpu().numpy().astype(np.float64)   # (B, Hkv)
+    return np.repeat(m, G, axis=1) * 1.1

@@ -133,6 +133,9 @@ def test_append_validation(lib):
     assert append(lib, v=plane(t=-1)) == -3
     assert append(lib, k=plane(data=A + 8)) == -4
     assert append(lib, v=plane(scales=A + 2)) == -4
+    # 4-byte aligned scales pass the alignment check (which comes before the
+    # capacity check): the call fails on the capacity instead
+    assert append(lib, v=plane(scales=A + 4), max_end=101) == -5
     assert append(lib, kn=A + 2) == -4
     assert append(lib, pos=A + 2) == -4
     assert append(lib, max_end=101) == -5

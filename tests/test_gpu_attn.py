@@ -12,8 +12,8 @@ import pytest
 
 from oracle import oracle as O
 
-from .gpu_util import (assert_close, assert_partials, fill_pair, note, oracle_threads,
-                       planes_to_oracle, require_gpu, run_decode, to_host_u16)
+from .gpu_util import (assert_close, assert_partials, fill_pair, gpu_row_scores, note, oracle_row_scores,
+                       oracle_threads, planes_to_oracle, require_gpu, run_decode, to_host_u16)
 from .test_oracle_attention import identity_values
 
 torch = pytest.importorskip("torch")
@@ -253,13 +253,14 @@ def build_workload(wl, tk, tv, layer=0, needle_pos=None):
     return kc, vc, q, lens
 
 
-def workload_case(name, tk, tv, variant, heads=None, layer=0, needle_pos=None):
+def workload_case(name, tk, tv, variant, heads=None, layer=0, needle_pos=None, split_tokens=None):
     wl = synth.WORKLOADS[name]
     if not variant_ok(variant, wl.D, wl.G, tk, tv):
         pytest.skip("variant does not cover the shape")
-    note(f"workload {name} {tk}/{tv} {variant} layer={layer}")
+    st = split_tokens or wl.split_tokens
+    note(f"workload {name} {tk}/{tv} {variant} layer={layer} split={st}")
     kc, vc, q, lens = build_workload(wl, tk, tv, layer, needle_pos)
-    out, lse, _ = run_decode(kc, vc, q, lens, wl.split_tokens, variant)
+    out, lse, _ = run_decode(kc, vc, q, lens, st, variant)
     if heads is None:
         ref, ref_lse = oracle_ref(kc, vc, q, lens, wl.Hkv)
         assert_close(out, lse, ref, ref_lse, name)
@@ -295,19 +296,45 @@ def test_workload_stack48_layers_sampled(variant, tk, tv):
         workload_case("stack48_d128_ctx64k", tk, tv, variant, layer=layer)
 
 
+def assert_needle_argmax(kc, vc, q, g, h, p, n_rows, D):
+    """The needle pin: row p has the largest score of query head h (the head
+    its needle was built from) among all n_rows rows of KV head g, in the
+    oracle's fp64 scores and in the attention kernel's own scores, which also
+    agree row by row within fp32 rounding."""
+    scale = 1 / math.sqrt(D)
+    so = oracle_row_scores(kc, to_host_u16(q[0, h:h + 1]), g, n_rows, scale)[0]
+    sg = gpu_row_scores(kc, vc, q[0, h:h + 1], g, n_rows, scale)[0]
+    assert int(np.argmax(so)) == p, f"oracle: argmax {int(np.argmax(so))} != needle row {p} (KV head {g})"
+    assert int(np.argmax(sg)) == p, f"GPU: argmax {int(np.argmax(sg))} != needle row {p} (KV head {g})"
+    err = np.abs(sg - so)
+    assert np.all(err <= 1e-4 + 1e-5 * np.abs(so)), f"scores differ by {err.max():.3g}"
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0")])
 def test_workload_long_ctx256k_with_needle(variant, tk, tv):
-    """All 40 heads at 262144 rows; the planted needle carries a visible share
-    of each constructing head's attention in both the oracle and the GPU."""
+    """All 40 heads at 262144 rows against the oracle.  The planted needle: for
+    every KV head, row p is the argmax of the constructing head's scores in
+    both the oracle and the kernel, and carries a visible share of that head's
+    attention."""
     kc, vc, q, lens, out, lse = workload_case("long_d128_ctx256k", tk, tv, variant)
     wl = synth.WORKLOADS["long_d128_ctx256k"]
     p = lens[0] // 3
     vneedle = O.dequantize(tv, planes_to_oracle(vc)[1][0, :, p], planes_to_oracle(vc)[2][0, :, p], wl.D)
     for g in range(wl.Hkv):
+        if variant == "mfma":
+            assert_needle_argmax(kc, vc, q, g, g * wl.G, p, lens[0], wl.D)
         o = out[0, g * wl.G]
         cos = float(o @ vneedle[g] / (np.linalg.norm(o) * np.linalg.norm(vneedle[g])))
         assert cos > 0.5, f"needle of KV head {g} not visible (cos {cos:.3f})"
+
+
+@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0")])
+@pytest.mark.parametrize("split_tokens", [2048, 1024])
+def test_workload_long_ctx256k_128_and_256_splits(tk, tv, split_tokens):
+    """The 262144-row layer cut into 128 and 256 splits (the benchmark's 64 are
+    covered above), all 40 heads against the oracle."""
+    workload_case("long_d128_ctx256k", tk, tv, "mfma", split_tokens=split_tokens)
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -323,6 +350,9 @@ def test_needle_at_split_boundaries(variant):
         for p in (0, st - 1, st, st + 1, 5 * st, wl.ctx - 1):
             kc, vc, q, lens, out, lse = workload_case(wl.name, "q8_0", "q4_0", variant,
                                                       heads=[0, wl.G * 3], needle_pos=p)
+            if variant == "mfma":
+                for g in (0, 3):
+                    assert_needle_argmax(kc, vc, q, g, g * wl.G, p, lens[0], wl.D)
     finally:
         del synth.WORKLOADS[wl.name]
 
@@ -332,5 +362,6 @@ def test_needle_at_split_boundaries(variant):
 @pytest.mark.parametrize("tk,tv", [("q4_0", "q4_0"), ("q8_0", "q4_0")])
 def test_workload_batch16_ragged(variant, name, tk, tv):
     wl = synth.WORKLOADS[name]
-    heads = [0, wl.Hq - 1] if wl.D == 128 else [0, 9]
+    # one query head of every KV head, at a different place in each group
+    heads = [g * wl.G + g % wl.G for g in range(wl.Hkv)]
     workload_case(name, tk, tv, variant, heads=heads)

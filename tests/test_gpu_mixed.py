@@ -16,7 +16,7 @@ import pytest
 
 from oracle import oracle as O
 
-from .gpu_util import (assert_close, download_planes, fill_pair, note, oracle_planes,
+from .gpu_util import (assert_close, download_planes, fill_pair, new_row_vmax, note, oracle_planes,
                        oracle_threads, planes_to_oracle, require_gpu, to_host_u16,
                        upload_oracle_planes)
 
@@ -131,11 +131,12 @@ def test_mixed_call_is_the_two_calls_bit_for_bit(tk, tv, case):
 
 @pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0"), ("f16", "q4_0")])
 @pytest.mark.parametrize("case", range(len(CASES)))
-def test_step_mixed_is_append_attention_merge_bit_for_bit(tk, tv, case):
+def test_step_mixed_is_append_attention_merge(tk, tv, case):
     """kvq_decode_step_mixed equals kvq_quantize_append of the new row into the
     window at row win_lens[b] - 1, kvq_decode_attn_mixed and
-    kvq_combine_regions, bit for bit: window rows, partials, output and LSE (a
-    sequence whose window length is 0 gets no row)."""
+    kvq_combine_regions: window rows and tail partials bit for bit, window
+    partials, output and LSE up to fp32 rounding (a sequence whose window
+    length is 0 gets no row)."""
     B, Hkv, G, D, tl, tcap, wl, wcap, st_t, st_w = CASES[case]
     note(f"step_mixed vs three calls {tk}/{tv} case {case}")
     dev = "cuda"
@@ -168,17 +169,51 @@ def test_step_mixed_is_append_attention_merge_bit_for_bit(tk, tv, case):
                     parts[1].o.clone(), parts[1].lse.clone(), out, lse))
     names = ("window K", "window V", "tail part_o", "tail part_lse", "window part_o", "window part_lse",
              "out", "lse")
+    vmax = new_row_vmax(v_new, G)
+
+    def close(a, c, what):
+        # outputs (B, Hq, D) and LSEs (B, Hq): the step's new-row term (an
+        # fp32 weight) against the tile's fp16-rounded one
+        a, c = a.cpu().numpy().astype(np.float64), c.cpu().numpy().astype(np.float64)
+        assert np.array_equal(np.isneginf(a), np.isneginf(c)), what
+        f = np.isfinite(c)
+        if a.ndim == 2:
+            assert np.all(np.abs(a[f] - c[f]) <= 2e-6 * np.maximum(1.0, np.abs(c[f]))), what
+        else:
+            bound = 2e-6 + 2e-5 * np.abs(c) + 2.0 ** -11 * vmax[..., None]
+            assert np.all(np.abs(a[f] - c[f]) <= bound[f]), f"{what}: {np.abs(a[f] - c[f]).max():.3g}"
+
+    # the window bytes are identical; the tail partials too (the tail is not
+    # written); the step merges the new row's decoded values as a term of its
+    # window split with an fp32 weight, where the three calls read the row
+    # back inside a tile and round its weight to fp16 for the matrix cores:
+    # the window partials and the outputs agree within 2^-11 of that weight
+    # times the row's largest value, plus fp32 rounding
     for n, a, b in zip(names, *res):
         if n.endswith("part_o") or n.endswith("part_lse"):
             # splits past a sequence's last one are not written by either path
             continue
-        assert torch.equal(a, b), n
+        if n in ("out", "lse"):
+            close(a, b, n)
+        else:
+            assert torch.equal(a, b), n
     for b in range(B):
         for (n, a, c), L, st in zip(((2, res[0][2], res[1][2]), (4, res[0][4], res[1][4])), (tl, wl),
                                     (st_t, st_w)):
             S = -(-L[b] // st)
-            assert torch.equal(a[b, :, :S], c[b, :, :S]), f"{names[n]} b {b}"
-            assert torch.equal(res[0][n + 1][b, :, :S], res[1][n + 1][b, :, :S]), f"{names[n + 1]} b {b}"
+            if n == 2:
+                assert torch.equal(a[b, :, :S], c[b, :, :S]), f"{names[n]} b {b}"
+                assert torch.equal(res[0][n + 1][b, :, :S], res[1][n + 1][b, :, :S]), f"{names[n + 1]} b {b}"
+            else:
+                # window partials (Hq, S, D), and their LSEs (Hq, S)
+                pa, pc = a[b, :, :S], c[b, :, :S]
+                fa = pa.cpu().numpy().astype(np.float64)
+                fc = pc.cpu().numpy().astype(np.float64)
+                bound = 2e-6 + 2e-5 * np.abs(fc) + 2.0 ** -11 * vmax[b][:, None, None]
+                assert np.all(np.abs(fa - fc) <= bound), f"{names[n]} b {b}"
+                la = res[0][n + 1][b, :, :S].cpu().numpy().astype(np.float64)
+                lc = res[1][n + 1][b, :, :S].cpu().numpy().astype(np.float64)
+                assert np.all(np.abs(la - lc) <= 2e-6 * np.maximum(1.0, np.abs(lc))), f"{names[n + 1]} b {b}"
     # the new row is in the window where the lengths say
     kh = to_host_u16(k_new)
     wk = res[0][0].cpu().numpy().view(np.uint16)

@@ -75,15 +75,7 @@ def test_multi_matches_oracle(tk, tv, case):
     kc, vc = fill_pair(tk, tv, synth.normal_f16((B, Hkv, max(lens), D), seed, dev),
                        synth.normal_f16((B, Hkv, max(lens), D), seed + 1, dev))
     q = synth.normal_f16((B, nq, Hkv * G, D), seed + 2, dev)
-    try:
-        out, lse = run_multi(kc, vc, q, lens, st)
-    except _lib.KVQError as e:
-        # the matrix-core kernel does not cover every type pair at every
-        # head_dim (e.g. fp16 V rows at 256 exceed its LDS budget): documented
-        # as KVQ_ERR_SHAPE
-        if e.status == -2 and (D, tv) == (256, "f16"):
-            pytest.skip("type pair not built for the matrix-core kernel at this head_dim")
-        raise
+    out, lse = run_multi(kc, vc, q, lens, st)
     ref, ref_lse = oracle_multi(kc, vc, q, lens)
     assert_close(out.reshape(B, -1, D), lse.reshape(B, -1), ref.reshape(B, -1, D), ref_lse.reshape(B, -1),
                  f"multi {tk}/{tv} case {case}")
@@ -97,8 +89,6 @@ def test_step_multi_is_append_attention_merge_bit_for_bit(tk, tv, case):
     heads, bit for bit: cache rows, partials of every split that holds rows,
     output and LSE.  Cases include new rows that straddle a split boundary."""
     B, Hkv, G, D, lens, st, nq = CASES[case]
-    if D == 256 and tv == "f16":
-        pytest.skip("type pair not built for the matrix-core kernel at this head_dim")
     note(f"step_multi vs three calls {tk}/{tv} case {case}")
     dev = "cuda"
     seed = 4100 + case
@@ -148,7 +138,10 @@ def test_one_query_token_is_the_decode_call_bit_for_bit():
     C.decode_multi(kc, vc, q, lt, max(lens), p1, 1 / math.sqrt(D))
     C.decode(kc, vc, q[:, 0].contiguous(), lt, max(lens), p2, 1 / math.sqrt(D))
     torch.cuda.synchronize()
-    assert torch.equal(p1.o, p2.o) and torch.equal(p1.lse, p2.lse)
+    # every split that holds a row (the others are written by neither call)
+    for b, L in enumerate(lens):
+        S = -(-L // st)
+        assert torch.equal(p1.o[b, :, :S], p2.o[b, :, :S]) and torch.equal(p1.lse[b, :, :S], p2.lse[b, :, :S])
 
 
 def test_multi_rejects_what_it_does_not_cover():

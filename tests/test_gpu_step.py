@@ -14,8 +14,8 @@ import pytest
 
 from oracle import oracle as O
 
-from .gpu_util import (assert_close, download_planes, note, oracle_planes, oracle_threads,
-                       require_gpu, to_host_u16, upload_oracle_planes)
+from .gpu_util import (assert_close, assert_step_matches_three_calls, download_planes, new_row_vmax, note,
+                       oracle_planes, oracle_threads, require_gpu, to_host_u16, upload_oracle_planes)
 
 torch = pytest.importorskip("torch")
 from quantised_kv_long_amd import cache as C  # noqa: E402
@@ -97,6 +97,8 @@ STEP_CASES = [
     # (B, Hkv, G, D, lens, split_tokens): D 128 / 256 take the one-launch
     # matrix-core step where it covers the types, the others the three kernels
     (2, 2, 5, 128, [1000, 65], 256),
+    # the new row alone in its split (L - 1 at a split boundary; L = 1)
+    (3, 2, 5, 128, [257, 1, 64], 256),
     (1, 2, 8, 256, [777], 128),
     (2, 1, 4, 512, [300, 64], 64),
     (3, 2, 4, 64, [1, 129, 200], 64),
@@ -125,12 +127,15 @@ def test_step_matches_oracle_and_three_calls(tk, tv, case):
     assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
     # the three-call path on a fresh copy of the sentinel cache: the same
-    # kernels, so the same bits
+    # cache bytes, and the same results up to fp32 rounding (the step merges
+    # the new row's decoded values as a term of its split's merge, the
+    # attention launch reads the row back inside a tile)
     kc3, vc3, *_ = step_setup(tk, tv, B, Hkv, G, D, lens, cap, 500 + case)
     out3, lse3 = run_three_calls(kc3, vc3, k_new, v_new, q, lens, st)
     check_planes(kc3, k_exp, "K (three calls)")
-    assert torch.equal(out, out3), "decode step and three calls differ"
-    assert torch.equal(lse, lse3)
+    check_planes(vc3, v_exp, "V (three calls)")
+    assert_step_matches_three_calls(out.cpu().numpy(), lse.cpu().numpy(), out3.cpu().numpy(),
+                                    lse3.cpu().numpy(), new_row_vmax(v_new, G), f"step {tk}/{tv} case {case}")
 
 
 @pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0")])
@@ -223,6 +228,12 @@ def workload_step(name, tk, tv, heads, layer=0):
         assert np.array_equal(s[b, :, L - 1], v_exp[2][b, :, L - 1])
     got = out.cpu().numpy().astype(np.float64)
     got_lse = lse.cpu().numpy().astype(np.float64)
+    if heads is None:
+        # every head: the whole oracle
+        ref, ref_lse = O.attend(to_host_u16(q), k_exp, v_exp, lens, Hkv, 1 / math.sqrt(D),
+                                nthreads=oracle_threads())
+        assert_close(got, got_lse, ref, ref_lse, f"{name} step")
+        return
     for h in heads:
         g = h // wl.G
         sub = lambda p: (p[0], np.ascontiguousarray(p[1][:, g:g + 1]),
@@ -234,16 +245,28 @@ def workload_step(name, tk, tv, heads, layer=0):
 
 @pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0"), ("f16", "f16")])
 def test_step_stack48_layer_full_size(tk, tv):
-    workload_step("stack48_d128_ctx64k", tk, tv, heads=[0, 17, 39], layer=5)
+    """A layer of the 64k stack, every head."""
+    workload_step("stack48_d128_ctx64k", tk, tv, heads=None, layer=5)
 
 
 @pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0")])
 def test_step_long_ctx256k_full_size(tk, tv):
-    workload_step("long_d128_ctx256k", tk, tv, heads=[0, 39])
+    """The 262144-row layer, every head."""
+    workload_step("long_d128_ctx256k", tk, tv, heads=None)
 
 
-def test_step_batch16_ragged_full_size():
-    workload_step("batch16_ragged", "q8_0", "q4_0", heads=[0, 31])
+@pytest.mark.parametrize("tk,tv", [("f16", "f16"), ("q8_0", "q8_0")])
+def test_step_hybrid_d256_ctx32k_full_size(tk, tv):
+    """The hybrid model's full-attention layer (16 query / 2 KV heads, head_dim
+    256, 32768 rows, outlier K channels), every head."""
+    workload_step("hybrid_d256_ctx32k", tk, tv, heads=None)
+
+
+@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0")])
+@pytest.mark.parametrize("name", ["batch16_ragged", "batch16_ragged_d512"])
+def test_step_batch16_ragged_full_size(name, tk, tv):
+    """16 ragged sequences (16k-128k rows), head_dim 128 and 512, every head."""
+    workload_step(name, tk, tv, heads=None)
 
 
 # ------------------------------------------- the new row's quantisation

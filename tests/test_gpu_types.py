@@ -12,7 +12,7 @@ import pytest
 from oracle import oracle as O
 
 from .gpu_util import (assert_close, assert_partials, fill_pair, note, oracle_threads, planes_to_oracle,
-                       run_decode, to_host_u16)
+                       require_gpu, run_decode, to_host_u16)
 from .test_oracle_quant_n3 import WORKED as WORKED_N3
 
 torch = pytest.importorskip("torch")

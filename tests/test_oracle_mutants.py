@@ -21,6 +21,10 @@ MUTANTS = {
     6: "q4_1 / q5_1 divide by the unrounded binary32 scale",
     7: "q5 / q6 high bits of adjacent elements swapped",
     8: "q5_0 / q6_0 clamp one level too high",
+    9: "query head h reads KV head h mod Hkv",
+    10: "softmax scale dropped from the scores",
+    11: "V rows decoded from the K planes",
+    12: "q4_0 decoded with offset 7",
 }
 
 
@@ -91,7 +95,35 @@ def n3_brute_agrees(lib) -> bool:
     return True
 
 
-BATTERY = [worked_blocks_pass, brute_agrees, split_combine_matches, n3_worked_blocks_pass, n3_brute_agrees]
+def attention_brute_agrees(lib) -> bool:
+    """fp64 attention of the oracle against the stdlib brute force (its own
+    row decoding, math.fsum sums) on tiny contexts: 2 sequences, 2 distinct KV
+    heads, 3 query heads each, q8_0 K and q4_0 V."""
+    rng = np.random.default_rng(24)
+    B, Hkv, G, D, C = 2, 2, 3, 32, 6
+    lens = [6, 3]
+    q = rng.standard_normal((B, Hkv * G, D)).astype(np.float16)
+    k = rng.standard_normal((B, Hkv, C, D)).astype(np.float16)
+    v = rng.standard_normal((B, Hkv, C, D)).astype(np.float16)
+    kc = ("q8_0",) + O.quantize("q8_0", k, lib=lib)
+    vc = ("q4_0",) + O.quantize("q4_0", v, lib=lib)
+    out, lse = O.attend(q, kc, vc, lens, Hkv, 0.3, lib=lib)
+    for b in range(B):
+        for h in range(Hkv * G):
+            g = h // G
+            krows = [brute.dequant_row("q8_0", kc[1][b, g, t].tobytes(), [int(x) for x in kc[2][b, g, t]], D)
+                     for t in range(lens[b])]
+            vrows = [brute.dequant_row("q4_0", vc[1][b, g, t].tobytes(), [int(x) for x in vc[2][b, g, t]], D)
+                     for t in range(lens[b])]
+            qf = [float(x) for x in q[b, h].astype(np.float64)]
+            ref, ref_lse = brute.attend_rows(qf, krows, vrows, 0.3)
+            if not (np.allclose(out[b, h], ref, atol=1e-12) and abs(lse[b, h] - ref_lse) <= 1e-12):
+                return False
+    return True
+
+
+BATTERY = [worked_blocks_pass, brute_agrees, split_combine_matches, n3_worked_blocks_pass, n3_brute_agrees,
+           attention_brute_agrees]
 
 
 def test_unmutated_oracle_passes_battery():
