@@ -601,6 +601,58 @@ def cpu_baseline(arm, budget_s):
                            "us_per_step_scaled": round(s1 * wl.layers * 1e6, 1)}}
 
 
+def run_arms(wl, arms, headline, split_tokens, args, dev):
+    """Time every arm of a workload; returns (results per arm, the headline
+    arm's device state)."""
+    import torch
+
+    import quantised_kv_long_amd as kvq
+
+    results = {}
+    head_arm = None
+    for tk, tv in arms:
+        per_layer = sum(wl.lengths()) * wl.Hkv * (
+            kvq.kvq_data_row_bytes(tk, wl.D) + kvq.kvq_scale_row_bytes(tk, wl.D) +
+            kvq.kvq_data_row_bytes(tv, wl.D) + kvq.kvq_scale_row_bytes(tv, wl.D))
+        reps = args.replicas or max(1, math.ceil(1.0e9 / (per_layer * wl.layers)))
+        log(f"arm {tk}/{tv}: building {wl.layers} layer(s) x {reps} replica(s)")
+        arm = Arm(wl, tk, tv, split_tokens, reps, dev, args.queries, args.window)
+        log(f"arm {tk}/{tv}: timing {args.steps} steps")
+        ms, samples = time_arm(arm, args.steps, args.warmup, not args.no_graph, args.variant)
+        per_launch = {m: ms[m] / wl.layers for m in MODES}
+        evict_us = time_evictions(arm) if args.window else None
+        r = {
+            "us_per_step": round(ms["step"] * 1e3, 2),
+            "stored_bytes_per_step": arm.stored_bytes_step,
+            "GBps": round(arm.stored_bytes_step / (ms["step"] * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(arm.stored_bytes_step / (ms["step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "step_us_per_layer": round(per_launch["step"] * 1e3, 3),
+            "three_call_us_per_step": round(ms["three"] * 1e3, 2),
+            "decode_only_us_per_launch": round(per_launch["decode"] * 1e3, 3),
+            "split_tokens": arm.split_tokens,
+            **({"window_split_tokens": arm.win_split_tokens} if args.window else {}),
+            "decode_only_GBps": round(arm.stored_bytes_layer / (per_launch["decode"] * 1e-3) / 1e9, 1),
+            "replicas": reps,
+        }
+        if args.queries > 1:
+            r["tokens_per_step"] = args.queries
+            r["us_per_token_per_layer"] = round(per_launch["step"] * 1e3 / args.queries, 3)
+        if evict_us is not None:
+            # once every WINDOW steps per layer: quantise the window into the tail
+            r["eviction_us_per_layer"] = round(evict_us, 3)
+            r["eviction_us_per_step_layer_amortised"] = round(evict_us / args.window, 4)
+        if samples:
+            r["single_step_us_p10_p50_p90"] = [round(percentile(samples, q), 2) for q in (0.1, 0.5, 0.9)]
+        results[f"{tk}/{tv}"] = r
+        log(f"arm {tk}/{tv}: {r}")
+        if (tk, tv) == headline:
+            head_arm = arm
+        else:
+            del arm
+            torch.cuda.empty_cache()
+    return results, head_arm
+
+
 def arm_ratios(results):
     """Speed-ups between the arms of one workload (median single steps and
     their p10-p90 separation where sampled)."""
