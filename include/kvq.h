@@ -461,6 +461,33 @@ int kvq_decode_step(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache
                     int split_tokens, int max_splits, float* part_o, float* part_lse,
                     int out_type, void* out, float* lse_out, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * step as kvq_decode_step, with the split partials (max_splits =
+ * ceil(max_seq_len / split_tokens)) in a device array of
+ * KVQ_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * from load until the process ends, instead of caller memory.  The call
+ * allocates nothing.  Results are those of kvq_decode_step with partials of
+ * that shape.
+ *
+ *   Arguments as for kvq_decode_step, without part_o, part_lse and
+ *   max_splits.
+ *   KVQ_ERR_CAPACITY if the partials need more than the array
+ *   (kvq_decode_step_noalloc_bytes gives the bytes a call needs); the other
+ *   statuses as for kvq_decode_step, all checked before any HIP call.
+ *   Every call on one GPU uses that GPU's one array and leaves its partials
+ *   there: calls that overlap on one GPU (other streams, other host threads)
+ *   race and must be serialised by the caller.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t kvq_decode_step_noalloc_bytes(int B, int Hq, int D, int max_seq_len, int split_tokens);
+int kvq_decode_step_noalloc(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache,
+                            const void* k_new, const void* v_new, const void* q,
+                            const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
+                            float softmax_scale, int max_seq_len, int split_tokens, int out_type,
+                            void* out, float* lse_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -108,6 +108,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_decode_step.argtypes = [DP, DP, P, P, P, P, i32, i32, i32, i32, f32, i32, i32, i32, P, P,
                                     i32, P, P, P]
     lib.kvq_decode_step.restype = i32
+    lib.kvq_decode_step_noalloc_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.kvq_decode_step_noalloc_bytes.restype = ctypes.c_size_t
+    lib.kvq_decode_step_noalloc.argtypes = [DP, DP, P, P, P, P, i32, i32, i32, i32, f32, i32, i32, i32, P, P,
+                                            P]
+    lib.kvq_decode_step_noalloc.restype = i32
     _lib = lib
     return lib
 
@@ -312,3 +317,17 @@ def kvq_decode_step(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, k_new, v_n
                                 _ptr(lse_out), _stream(stream))
     return _check("kvq_decode_step", rc)
 
+
+def kvq_decode_step_noalloc_bytes(B: int, Hq: int, D: int, max_seq_len: int, split_tokens: int) -> int:
+    return int(load().kvq_decode_step_noalloc_bytes(B, Hq, D, max_seq_len, split_tokens))
+
+
+def kvq_decode_step_noalloc(k_cache: kvq_plane_desc, v_cache: kvq_plane_desc, k_new, v_new, q, seq_lens,
+                            B: int, Hq: int, Hkv: int, D: int, softmax_scale: float, max_seq_len: int,
+                            split_tokens: int, out_type, out, lse_out=None, stream=None) -> int:
+    ot = OUT_F32 if out_type in ("f32", OUT_F32) else _tcode(out_type)
+    rc = load().kvq_decode_step_noalloc(ctypes.byref(k_cache), ctypes.byref(v_cache), _ptr(k_new),
+                                        _ptr(v_new), _ptr(q), _ptr(seq_lens), B, Hq, Hkv, D,
+                                        float(softmax_scale), max_seq_len, split_tokens, ot, _ptr(out),
+                                        _ptr(lse_out), _stream(stream))
+    return _check("kvq_decode_step_noalloc", rc)

@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
               "kvq_decode_step", "kvq_quantize_rows", "kvq_combine_regions", "kvq_decode_attn_multi",
               "kvq_decode_attn_mixed", "kvq_decode_step_mixed", "kvq_decode_step_multi",
               "kvq_select_kv_tier", "kvq_tier_cache_bytes", "kvq_tier_types", "kvq_data_row_bytes",
-              "kvq_scale_row_bytes", "kvq_status_string"):
+              "kvq_scale_row_bytes", "kvq_status_string", "kvq_decode_step_noalloc",
+              "kvq_decode_step_noalloc_bytes"):
         assert n in names
 
 
@@ -237,6 +238,47 @@ def test_decode_step_validation(lib):
     assert step(lib, vn=A + 8) == -4
     assert step(lib, out=A + 8) == -4
     assert step(lib, lse=A + 2) == -4
+
+
+def step_noalloc(lib, k=None, v=None, kn=A, vn=A, q=A, lens=A, B=1, Hq=40, Hkv=8, D=128, scale=0.088,
+                 max_len=100, split=64, ot=0, out=A, lse=None):
+    k = k if k is not None else plane()
+    v = v if v is not None else plane()
+    return lib.kvq_decode_step_noalloc(ctypes.byref(k), ctypes.byref(v), kn, vn, q, lens, B, Hq, Hkv, D,
+                                       scale, max_len, split, ot, out, lse, None)
+
+
+def test_noalloc_scratch_bytes(lib):
+    """The partials a no-allocation step needs: B*Hq*S*D fp32 rows (rounded up
+    to 256 bytes) then B*Hq*S fp32 LSEs, S = ceil(max_seq_len / split_tokens)."""
+    assert _lib.kvq_decode_step_noalloc_bytes(1, 40, 128, 65536, 1024) == 40 * 64 * 128 * 4 + 40 * 64 * 4
+    assert _lib.kvq_decode_step_noalloc_bytes(2, 5, 32, 65, 64) == 2 * 5 * 2 * 32 * 4 + 2 * 5 * 2 * 4
+    assert _lib.kvq_decode_step_noalloc_bytes(1, 3, 32, 1, 64) == 512 + 12
+    assert _lib.kvq_decode_step_noalloc_bytes(0, 3, 32, 1, 64) == 0
+
+
+@nogpu
+def test_decode_step_noalloc_validation(lib):
+    """Every status of kvq_decode_step, and KVQ_ERR_CAPACITY for partials beyond
+    the library's array, all before any HIP call."""
+    assert step_noalloc(lib, q=None) == -1
+    assert step_noalloc(lib, kn=None) == -1
+    assert step_noalloc(lib, out=None) == -1
+    assert step_noalloc(lib, Hq=41) == -2
+    assert step_noalloc(lib, D=1024) == -2
+    assert step_noalloc(lib, B=0) == -2
+    assert step_noalloc(lib, k=plane(t=8)) == -3
+    assert step_noalloc(lib, ot=1) == -3
+    assert step_noalloc(lib, kn=A + 2) == -4
+    assert step_noalloc(lib, max_len=101) == -5
+    assert step_noalloc(lib, split=100) == -6
+    assert step_noalloc(lib, split=32) == -6
+    # 40 heads x 4097 splits x 129 floats is beyond 64 MiB
+    big = plane(cap=1 << 25, seq=8 << 25, head=1 << 25)
+    assert _lib.kvq_decode_step_noalloc_bytes(1, 40, 128, 4096 * 4097, 4096) > 64 << 20
+    assert step_noalloc(lib, k=big, v=big, max_len=4096 * 4097, split=4096) == -5
+    # more splits than the partials' index allows
+    assert step_noalloc(lib, k=big, v=big, max_len=64 * 65536, split=64) == -6
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
