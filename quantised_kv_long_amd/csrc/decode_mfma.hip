@@ -216,9 +216,10 @@ struct Cfg {
     // the V code offset as an fp16 subnormal pair (0: no offset, min types)
     static constexpr uint32_t VOFF_BITS = TV == T_Q4 ? 0x00080008u : TV == T_Q8 ? 0x00800080u
                                         : TV == T_Q5_0 ? 0x00100010u : TV == T_Q6_0 ? 0x00200020u : 0u;
-    // a decode step's new row merged from registers (whole 128-wide rows of
-    // the base types: one value per thread, 2 * NB_ROW blocks of 32)
-    static constexpr bool NEWROW = DS == 1 && !NEWT && NTH == 2 * NB_ROW * 32;
+    // a decode step's new row merged from registers (the base types: each
+    // aligned half-wave quantises NEW_IT of the row's 2 * NB_ROW blocks)
+    static constexpr bool NEWROW = !NEWT;
+    static constexpr int NEW_IT = (2 * NB_ROW * 32 + NTH - 1) / NTH;   // new-row blocks per half-wave
     static constexpr bool VALID = V_BYTES % 1024 == 0 && SK_BYTES % 256 == 0 && SV_BYTES % 256 == 0 &&
                                   (!VBYTES || (TT * NB) % 64 == 0) && V_DW <= (DW == 128 ? 32 : 64) &&
                                   WV * BUF <= 64 * 1024 && (!NEWT || (D == 128 && DS == 1));
@@ -232,7 +233,7 @@ __host__ __device__ constexpr size_t merge_lds_bytes(int nc)
 {
     return Cfg<TK, TV, D>::DS > 1 ? 0
                                   : sizeof(float) * ((size_t)WAVES * 16 * 2 + (size_t)WAVES * 16 * (D / 32) +
-                                                     (size_t)WAVES * nc * D);
+                                                     (size_t)WAVES * nc * D);   // (DS == 1: WV = WAVES)
 }
 
 // Every instance is built for two waves per SIMD (at most 256 registers):
@@ -277,10 +278,10 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     const int L = a.seq_lens[b];
     const int t_begin = s * a.split_tokens;
     const int t_end_all = min(t_begin + a.split_tokens, L);
-    // Decode step with one new token over whole 128-wide rows (NEWROW): the
-    // workgroup whose split holds row L-1 leaves that row out of its tiles,
-    // quantises the new row into it after its tile loop, and merges the row's
-    // decoded values as one more term, so no load waits for those stores.
+    // Decode step with one new token (NEWROW, the base types): the workgroup
+    // whose split holds row L-1 leaves that row out of its tiles, quantises
+    // the new row into it after its tile loop, and merges the row's decoded
+    // values as one more term, so no load waits for those stores.
     constexpr bool NEWROW_OK = C::NEWROW && !MQ;
     const bool newrow = NEWROW_OK && a.k_new != nullptr && t_end_all == L;
     const int Lr = newrow ? L - 1 : L;             // rows the tiles read
@@ -929,14 +930,16 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
         }
     };
 
-    // ---- main loop over this wave's tiles (it, it+W, ...), with a ring of
-    //      NS register sets so that loads run ahead: K of tile it+NS*W is
-    //      issued as soon as tile it's QK products are done (into the
-    //      registers they free); after tile it's PV the V rows and scales of
-    //      tile it+W go to LDS (a wave's LDS reads and writes are performed in
-    //      order, so one buffer suffices) and V of tile it+(NS+1)*W is issued
-    //      into the registers that frees.
-    // (a 512-wide head: all waves walk every tile, each over its slice)
+    // ---- main loop over this wave's tiles, with a ring of NS register sets
+    //      so that loads run ahead: K of the tile NS places ahead in the
+    //      wave's sequence is issued as soon as the current tile's QK products
+    //      are done (into the registers they free); after the current tile's
+    //      PV the V rows and scales of the next tile go to LDS (a wave's LDS
+    //      reads and writes are performed in order, so one buffer suffices)
+    //      and V of the tile NS + 1 places ahead is issued into the registers
+    //      that frees.
+    //    Wave w of a whole-row workgroup takes tiles w, w + W, ...; with a
+    //    head wider than 128 all waves walk every tile, each over its slice.
     constexpr int W = C::DS > 1 ? 1 : WAVES;
     constexpr int NS = C::NSET;
     int it = C::DS > 1 ? 0 : wave;
@@ -945,28 +948,71 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     uint32_t srs[NS][C::S_DW];
     // the new row's value of this thread (element tid & 31 of block tid >> 5:
     // K blocks, then V blocks), loaded first so it arrives with the tiles
-    uint16_t xnew = 0;
+    uint16_t xnew[C::NEW_IT];
     if constexpr (NEWROW_OK) {
         if (newrow) {
-            const int blk2 = tid >> 5;
-            const bool isv = blk2 >= C::NB_ROW;
-            xnew = ((isv ? a.v_new : a.k_new) + ((int64_t)b * a.Hkv + g) * D + 32 * (isv ? blk2 - C::NB_ROW : blk2))
-                [tid & 31];
-        }
-    }
-    load_q();
-    if (it < ntiles) {
 #pragma unroll
-        for (int x = 0; x < NS; ++x) {
-            issue_k(it + x * W, krs[x]);
-            issue_vs(it + x * W, vrs[x], srs[x]);
+            for (int k = 0; k < C::NEW_IT; ++k) {
+                // (half-waves past the row's blocks load its last block again:
+                // no branch, so the loads stay in flight through the tile loop)
+                const int blk2 = min((tid >> 5) + k * (C::NTH / 32), 2 * C::NB_ROW - 1);
+                const bool isv = blk2 >= C::NB_ROW;
+                xnew[k] = ((isv ? a.v_new : a.k_new) + ((int64_t)b * a.Hkv + g) * D +
+                           32 * (isv ? blk2 - C::NB_ROW : blk2))[tid & 31];
+            }
         }
     }
-    init_q();
-    if (it < ntiles) {
-        stage(vrs[0], srs[0]);
-        issue_vs(it + NS * W, vrs[0], srs[0]);
+    // The new row, after the tile loop: quantised into row L-1 (the block
+    // quantiser of kvq_quantize_append, bit for bit), its decoded values
+    // (scale * code, exact) kept in lds_new: K in [0, D), V in [D, 2D).
+    auto newrow_quantise = [&]() {
+#pragma unroll
+        for (int k = 0; k < C::NEW_IT; ++k) {
+            const int blk2 = (tid >> 5) + k * (C::NTH / 32), j = tid & 31;
+            if (blk2 >= 2 * C::NB_ROW) break;         // (uniform over the half-wave)
+            // the raw value is opaque to the compiler until here, so its load
+            // is waited for only now
+            uint16_t xk = xnew[k];
+            asm volatile("" : "+v"(xk));
+            const bool isv = blk2 >= C::NB_ROW;
+            const int blk = isv ? blk2 - C::NB_ROW : blk2;
+            const int64_t row = (isv ? vrow0 : krow0) + (L - 1);
+            lds_new[32 * blk2 + j] =
+                isv ? quantize_block_lanes_v<TV>(xk, a.v.data + row * rb(TV, D) + blk * rb(TV, 32),
+                                                 a.v.scales + row * (D / 32) + blk, j)
+                    : quantize_block_lanes_v<TK>(xk, a.k.data + row * rb(TK, D) + blk * rb(TK, 32),
+                                                 a.k.scales + row * (D / 32) + blk, j);
+        }
+    };
+    // The new row's score of column ln over this wave's slice of the head
+    // dimension (the same for the four lanes of the column): Q (the MFMA
+    // operand, k-slot e of block kb holds element 32 kb + kel(e)) times the
+    // decoded K row, in fp32.
+    auto newrow_score_part = [&]() -> float {
+        float acc = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < C::NB; ++kb) {
+            const u32x4 qu = __builtin_bit_cast(u32x4, qop[kb]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t w2 = (uint32_t)qu[e >> 1];
+                const half2v h2 = __builtin_bit_cast(half2v, w2);
+                const int kel = C::KNIB ? 4 * lq + ((e & 1) ? 2 : 0) + ((e & 2) ? 16 : 0) + (e >> 2) : 8 * lq + e;
+                acc = fmaf((float)h2[e & 1], lds_new[wsl * C::DW + 32 * kb + kel], acc);
+            }
+        }
+        return xsum4(acc);
+    };
+    load_q();
+    // (issued on every path: a wave with no tile reads only out-of-range rows)
+#pragma unroll
+    for (int x = 0; x < NS; ++x) {
+        issue_k(it + x * W, krs[x]);
+        issue_vs(it + x * W, vrs[x], srs[x]);
     }
+    // the tiles' loads go out before anything waits for Q
+    __builtin_amdgcn_sched_barrier(0);
+    init_q();
     // tile it uses K set x; V of tile it is in LDS, V of the next tile in set
     // (x + 1) % NS.  The loop runs whole rounds of the ring with no branch
     // around a load, so the compiler's wait before each use counts exactly
@@ -974,6 +1020,8 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     // NS - 1 per wave) runs on rows at or past L: its loads are out of range
     // (zeros, no memory access) and every row is masked out of the softmax.
     if (it < ntiles) {
+        stage(vrs[0], srs[0]);
+        issue_vs(it + NS * W, vrs[0], srs[0]);
         const int rounds = ((ntiles - it + W - 1) / W + NS - 1) / NS;
         for (int r = 0; r < rounds; ++r) {
 #pragma unroll
@@ -990,9 +1038,32 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     if constexpr (C::DS > 1) {
         // every wave holds the same (m, l) and its own slice of O: write it
         const float l_head = xsum4(l_part);
+        // the new row's term (max m_new, sum 1, row v): its score is the sum
+        // of the waves' slice scores, in a fixed order
+        float m_new = -INFINITY;
+        if constexpr (NEWROW_OK) {
+            if (newrow) {
+                newrow_quantise();
+                __syncthreads();
+                const float sc = newrow_score_part();
+                if (lq == 0) lds_new[2 * D + 16 * wave + ln] = sc;
+                __syncthreads();
+                float tot = 0.0f;
+#pragma unroll
+                for (int w = 0; w < C::WV; ++w) tot += lds_new[2 * D + 16 * w + ln];
+                m_new = tot * a.scale_log2;
+            }
+        }
         if (ln < NC) {
             // (a column that saw no row: l = 0, o = 0, lse = -inf)
-            const float inv = l_head > 0.0f ? (C::V_SCALE ? TWO24 : 1.0f) / l_head : 0.0f;
+            const bool nr = NEWROW_OK && newrow;
+            const float M = nr ? fmaxf(m_ref, m_new) : m_ref;
+            const float al = nr ? exp2f(m_ref - M) : 1.0f;
+            const float be = nr ? exp2f(m_new - M) : 0.0f;
+            const float lt = al * l_head + be;
+            const float inv = lt > 0.0f ? al * (C::V_SCALE ? TWO24 : 1.0f) / lt : 0.0f;
+            const float fn = nr ? be / lt : 0.0f;
+            const float* vnew = lds_new + D + wsl * C::DW;
             float* prow = po + crow(ln) * ho_stride + wsl * C::DW;
 #pragma unroll
             for (int t = 0; t < C::NDT; ++t) {
@@ -1002,6 +1073,12 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
                     o[i] = oacc[t][i];
                     if constexpr (C::V_SCALE) o[i] -= bacc[t >> 1][i];
                     o[i] *= inv;
+                    if (nr) {
+                        // the column register i of tile t holds (see the stores below)
+                        const int col = TV == T_Q4 ? 32 * (t >> 1) + 8 * (t & 1) + 2 * lq + (i >> 1) + 16 * (i & 1)
+                                                   : 16 * t + 4 * lq + i;
+                        o[i] = fmaf(fn, vnew[col], o[i]);
+                    }
                 }
                 // register i holds output row m = 4*lq + i of the tile: for
                 // q4_0 V column 32*(t/2) + 8*(t%2) + m/2 + 16*(m%2), i.e. two
@@ -1015,8 +1092,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
                     *reinterpret_cast<float4*>(prow + 16 * t + 4 * lq) = make_float4(o[0], o[1], o[2], o[3]);
                 }
             }
-            if (wave == 0 && lq == 0)
-                pl[crow(ln) * a.max_splits] = (m_ref + log2f(l_head)) * 0.69314718055994531f;
+            if (wave == 0 && lq == 0) pl[crow(ln) * a.max_splits] = (M + log2f(lt)) * 0.69314718055994531f;
         }
         return;
     }
@@ -1027,42 +1103,15 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     //      code-offset correction of its block), so each output column is a
     //      four-term weighted sum with no second barrier.
     const float l_head = xsum4(l_part);
-    // the new row: quantised into row L-1 (the block quantiser of
-    // kvq_quantize_append, bit for bit), its decoded values (scale * code,
-    // exact) kept in lds_new: K in [0, D), V in [D, 2D); its scores in
-    // lds_new[2D + column], log2 units
     if constexpr (NEWROW_OK) {
-        if (newrow) {
-            const int blk2 = tid >> 5, j = tid & 31;
-            const bool isv = blk2 >= C::NB_ROW;
-            const int blk = isv ? blk2 - C::NB_ROW : blk2;
-            const int64_t row = (isv ? vrow0 : krow0) + (L - 1);
-            lds_new[tid] = isv ? quantize_block_lanes_v<TV>(xnew, a.v.data + row * rb(TV, D) + blk * rb(TV, 32),
-                                                           a.v.scales + row * (D / 32) + blk, j)
-                               : quantize_block_lanes_v<TK>(xnew, a.k.data + row * rb(TK, D) + blk * rb(TK, 32),
-                                                           a.k.scales + row * (D / 32) + blk, j);
-        }
+        if (newrow) newrow_quantise();
     }
     __syncthreads();
     if constexpr (NEWROW_OK) {
+        // its scores in lds_new[2D + column], log2 units
         if (newrow && wave == 0) {
-            // score of column ln: Q (the MFMA operand, k-slot e of block kb
-            // holds element 32 kb + kel(e)) times the decoded K row
-            float acc = 0.0f;
-#pragma unroll
-            for (int kb = 0; kb < C::NB; ++kb) {
-                const u32x4 qu = __builtin_bit_cast(u32x4, qop[kb]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t w2 = (uint32_t)qu[e >> 1];
-                    const half2v h2 = __builtin_bit_cast(half2v, w2);
-                    const int kel = C::KNIB ? 4 * lq + ((e & 1) ? 2 : 0) + ((e & 2) ? 16 : 0) + (e >> 2)
-                                            : 8 * lq + e;
-                    acc = fmaf((float)h2[e & 1], lds_new[32 * kb + kel], acc);
-                }
-            }
-            acc = xsum4(acc);
-            if (lq == 0) lds_new[2 * D + ln] = acc * a.scale_log2;
+            const float sc = newrow_score_part();
+            if (lq == 0) lds_new[2 * D + ln] = sc * a.scale_log2;
         }
     }
     uint8_t* marea = merge_lds_bytes<TK, TV, D>(NC) <= lds_cap ? lds_a : lds_merge_dyn;
@@ -1156,7 +1205,7 @@ decode_mfma_kernel(DecodeArgs a)
     using C = Cfg<TK, TV, D>;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[C::WV * C::BUF];
     __shared__ __attribute__((aligned(16))) float lds_sx[C::SX_FLOATS];
-    __shared__ __attribute__((aligned(16))) float lds_new[C::NEWROW && !MQ ? 2 * D + 16 : 1];
+    __shared__ __attribute__((aligned(16))) float lds_new[C::NEWROW && !MQ ? 2 * D + 64 : 1];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
     decode_wg<TK, TV, D, MQ>(a, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn, lds_new);
 }
@@ -1183,7 +1232,7 @@ decode_mfma_dual_kernel(DecodeArgs t, DecodeArgs w)
     using DC = DualCfg<TK, TV, D>;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[DC::BUF];
     __shared__ __attribute__((aligned(16))) float lds_sx[DC::SX];
-    __shared__ __attribute__((aligned(16))) float lds_new[DC::F::NEWROW || DC::T::NEWROW ? 2 * D + 16 : 1];
+    __shared__ __attribute__((aligned(16))) float lds_new[DC::F::NEWROW || DC::T::NEWROW ? 2 * D + 64 : 1];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
     const int ts = grid_splits(t);  // the first ts workgroups of each row take the tail
     if ((int)blockIdx.x < ts)
@@ -1210,7 +1259,7 @@ template <int TK, int TV, int D>
 size_t lds_bytes(int nc)
 {
     using C = Cfg<TK, TV, D>;
-    return (size_t)C::WV * C::BUF + sizeof(float) * (C::SX_FLOATS + (C::NEWROW ? 2 * D + 16 : 1)) +
+    return (size_t)C::WV * C::BUF + sizeof(float) * (C::SX_FLOATS + (C::NEWROW ? 2 * D + 64 : 1)) +
            dyn_lds_bytes<TK, TV, D>(nc);
 }
 
@@ -1295,7 +1344,7 @@ bool dual_supports3(const DecodeArgs& t)
     if constexpr (!DC::VALID) {
         return false;
     } else {
-        return (size_t)DC::BUF + sizeof(float) * (DC::SX + 2 * D + 16) + dual_dyn_bytes<TK, TV, D>(t.G) <=
+        return (size_t)DC::BUF + sizeof(float) * (DC::SX + 2 * D + 64) + dual_dyn_bytes<TK, TV, D>(t.G) <=
                160 * 1024;
     }
 }
@@ -1308,7 +1357,7 @@ hipError_t launch_dual3(const DecodeArgs& t, const DecodeArgs& w, hipStream_t s)
         return hipErrorInvalidConfiguration;
     } else {
         const size_t dyn = dual_dyn_bytes<TK, TV, D>(t.G);
-        if ((size_t)DC::BUF + sizeof(float) * (DC::SX + 2 * D + 16) + dyn > 64 * 1024) {
+        if ((size_t)DC::BUF + sizeof(float) * (DC::SX + 2 * D + 64) + dyn > 64 * 1024) {
             const hipError_t e = hipFuncSetAttribute(
                 reinterpret_cast<const void*>(&decode_mfma_dual_kernel<TK, TV, D>),
                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
