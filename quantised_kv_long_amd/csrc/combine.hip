@@ -5,131 +5,199 @@
 // One workgroup (256 threads) per (sequence, query head, chunk of at most
 // 128 columns, chosen by chunk_cols); the merge itself is combine_fold_src() /
 // combine_finish() in kvq_combine.hpp.  A chunk of W columns gives its 256
-// threads 256 / (W / 4) residue classes of the splits (8 for 128 columns),
-// each folding its splits in batches of 8 or 16 loads; every chunk reads all
+// threads cmb_classes(W / 4) residue classes of the splits (8 for 128
+// columns), each folding its splits in batches of 2 to 16 loads; every chunk reads all
 // the lse values and writes its own columns (the first chunk also writes the
-// LSE).
+// LSE).  The splits loaded are those that can hold rows given the launch
+// arguments (live_splits), so the loads do not wait for the sequence lengths.
 #include "kvq_combine.hpp"
 #include "kvq_internal.hpp"
 
 namespace kvq {
 namespace {
 
+#ifndef KVQ_CMB_TARGET_U
+#define KVQ_CMB_TARGET_U 4
+#endif
+
 // Columns of one merge workgroup for rows of D columns (a multiple of 32) and
-// up to S splits: the whole row up to 128 columns, else the largest multiple
-// of 32 up to 128 that divides it; then narrower divisors while a thread
-// would fold more than 16 splits (one batch of loads), since a chunk of w
-// columns has 256 / (w / 4) residue classes.
-inline int chunk_cols(int D, int S)
+// n splits to load: 128, 64 or 32, the widest that divides D, then halved
+// while a thread would load more than KVQ_CMB_TARGET_U splits (a chunk of w
+// columns has cmb_classes(w / 4) residue classes): narrower chunks mean more
+// workgroups and fewer loads per thread.  Every chunk width gives all 256
+// threads a column.
+inline int chunk_cols(int D, int n)
 {
-    auto next_down = [D](int w) {
-        for (int v = w - 32; v >= 32; v -= 32)
-            if (D % v == 0) return v;
-        return 32;
-    };
-    int w = D <= 128 ? D : next_down(160);
-    while (w > 32 && (S + CMB_NT / (w / 4) - 1) / (CMB_NT / (w / 4)) > 16) w = next_down(w);
+    int w = D % 128 == 0 ? 128 : D % 64 == 0 ? 64 : 32;
+    while (w > 32 && (n + cmb_classes(w / 4) - 1) / cmb_classes(w / 4) > KVQ_CMB_TARGET_U) w /= 2;
     return w;
 }
 
-__global__ void __launch_bounds__(CMB_NT) combine_kernel(CombineArgs a)
+// Splits one thread loads per batch: the fewest of 2, 4, 8, 16 that cover n
+// splits in one batch (16 beyond).
+inline int batch_splits(int n, int W)
 {
-    __shared__ CombineLds sm;
-    const int h = blockIdx.x, b = blockIdx.y;
-    const int W = a.D / (int)gridDim.z, c0 = blockIdx.z * W;
-    const int L = a.seq_lens[b];
-    const int S = L > 0 ? min((L + a.split_tokens - 1) / a.split_tokens, a.max_splits) : 0;
-    const int64_t bh = (int64_t)b * a.Hq + h;
-    void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh * a.D + c0)
-                          : (void*)(reinterpret_cast<float*>(a.out) + bh * a.D + c0);
-    const float* pl = a.part_lse + bh * a.max_splits;
-    const CombineSrc1 src{pl, reinterpret_cast<const float4*>(a.part_o + bh * a.max_splits * a.D + c0),
-                          a.D >> 2};
-    float* lse = a.lse_out && blockIdx.z == 0 ? a.lse_out + bh : nullptr;
-    // one batch of loads covers S <= 8 * (256 / (W / 4)) splits with U = 8
-    CombineState st = combine_init();
-    if (S <= 8 * (CMB_NT / (W / 4)))
-        combine_fold_src<8>(src, S, W, st);
-    else
-        combine_fold_src<16>(src, S, W, st);
-    combine_finish(st, W, a.out_f16, out, lse, sm);
+    const int R = cmb_classes(W / 4);
+    return n <= 2 * R ? 2 : n <= 4 * R ? 4 : n <= 8 * R ? 8 : 16;
 }
 
-// The splits of all regions of one (sequence, query head) as one list:
-// region 0's splits, then region 1's, ... so that one batch of loads spans
-// the regions.
+template <int U>
+__global__ void __launch_bounds__(CMB_NT) combine_kernel(CombineArgs a)
+{
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int W = a.D / (int)gridDim.z, c0 = blockIdx.z * W;
+    const int64_t bh = (int64_t)b * a.Hq + h;
+    // the loads are issued before the sequence length arrives
+    CombineSrc1 src;
+    src.rl = cmb_rsrc(a.part_lse + bh * a.max_splits, (int64_t)a.max_splits * 4);
+    src.ro = cmb_rsrc(a.part_o + bh * a.max_splits * a.D + c0, ((int64_t)a.max_splits * a.D - c0) * 4);
+    src.len = a.seq_lens + b;
+    src.split_tokens = a.split_tokens;
+    src.D = a.D;
+    src.n = a.live_splits;
+    src.S = 0;
+    void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh * a.D + c0)
+                          : (void*)(reinterpret_cast<float*>(a.out) + bh * a.D + c0);
+    float* lse = a.lse_out && blockIdx.z == 0 ? a.lse_out + bh : nullptr;
+    // (the output pointers are read with the other arguments, not after the merge)
+    asm volatile("" ::"s"(out), "s"(lse));
+    CombineState st = combine_init();
+    combine_fold_src<U>(src, W, st);
+    combine_finish(st, W, a.out_f16, out, lse);
+}
+
+// The splits of all regions of one (sequence, query head) as one list of
+// slots: region 0's live_splits slots, then region 1's, ... (slot offsets from
+// the launch arguments), so that one batch of loads spans the regions and
+// needs no sequence length; slots past a region's own split count are masked.
 struct CombineSrcN {
-    const float* pl[MAX_REGIONS];
-    const float4* po4[MAX_REGIONS];
-    int first[MAX_REGIONS];   // index of each region's split 0 in the list
-    int n, D4;
-    __device__ __forceinline__ void load(int sp, int c, float& ls, float4& v) const
+    const float* pl[MAX_REGIONS];   // lse values of the (sequence, head)
+    const float* po[MAX_REGIONS];   // its rows, from the chunk's first column
+    int first[MAX_REGIONS];         // slot of each region's split 0
+    int last[MAX_REGIONS];          // max_splits - 1: loads clamp to it
+    int S[MAX_REGIONS];             // splits holding rows, per region
+    int live_n[MAX_REGIONS];        // each region's slots
+    int split_tokens[MAX_REGIONS];
+    const int32_t* len[MAX_REGIONS];   // the sequence's length in each region
+    int nreg, D, n, e;
+    // (global loads with per-lane addresses: the lanes of one load may fall
+    // in different regions; every address stays inside the region's partials)
+    __device__ __forceinline__ void load(int su, int r, int c, uint32_t& ls, cmb_u32x4& v) const
     {
-        // the last region whose first split is at or before sp (static
-        // indices only: the arrays stay in registers)
-        const float* p = pl[0];
-        const float4* o = po4[0];
-        int f = 0;
+        const int sp = su + r;
+        const float* l = pl[0];
+        const float* o = po[0];
+        int f = 0, z = last[0];
 #pragma unroll
-        for (int k = 1; k < MAX_REGIONS; ++k) {
-            if (k < n && sp >= first[k]) {
-                p = pl[k];
-                o = po4[k];
-                f = first[k];
+        for (int i = 1; i < MAX_REGIONS; ++i) {
+            if (i < nreg && sp >= first[i]) {
+                l = pl[i];
+                o = po[i];
+                f = first[i];
+                z = last[i];
             }
         }
-        ls = p[sp - f];
-        v = o[(int64_t)(sp - f) * D4 + c];
+        const int j = min(sp - f, z);
+        ls = *reinterpret_cast<const uint32_t*>(l + j);
+        v = *reinterpret_cast<const cmb_u32x4*>(o + (int64_t)j * D + 4 * c);
     }
+    __device__ __forceinline__ void settle()
+    {
+        e = 0;
+#pragma unroll
+        for (int i = 0; i < MAX_REGIONS; ++i) {
+            // (an unused region has live_n = 0, so S = 0)
+            const int L = max(*len[i], 0);
+            S[i] = min((L + split_tokens[i] - 1) / split_tokens[i], live_n[i]);
+            e = S[i] > 0 ? first[i] + S[i] : e;
+        }
+    }
+    __device__ __forceinline__ bool live(int sp) const
+    {
+        bool ok = false;
+#pragma unroll
+        for (int i = 0; i < MAX_REGIONS; ++i)
+            if (i < nreg && sp >= first[i] && sp < first[i] + S[i]) ok = true;
+        return ok;
+    }
+    __device__ __forceinline__ int end() const { return e; }
 };
 
 // The same merge over the partials of several regions (HAL #582 section 5
 // P2: each region of a mixed cache, the fp16 window and the quantised tail,
 // has its own typed attention; their partials are merged exactly).
+template <int U>
 __global__ void __launch_bounds__(CMB_NT) combine_regions_kernel(CombineRegionsArgs a)
 {
-    __shared__ CombineLds sm;
     const int h = blockIdx.x, b = blockIdx.y;
     const int W = a.D / (int)gridDim.z, c0 = blockIdx.z * W;
     const int64_t bh = (int64_t)b * a.Hq + h;
-    void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh * a.D + c0)
-                          : (void*)(reinterpret_cast<float*>(a.out) + bh * a.D + c0);
     CombineSrcN src;
-    src.n = a.n;
-    src.D4 = a.D >> 2;                 // row stride in float4 (each row starts at column c0)
-    int S = 0;
+    src.nreg = a.n;
+    src.D = a.D;
+    // every field of every region is read without a branch: the launcher
+    // fills an unused region with region 0's pointers and no splits
+    int n = 0;
 #pragma unroll
     for (int i = 0; i < MAX_REGIONS; ++i) {
-        src.first[i] = S;
-        if (i >= a.n) continue;
-        const int L = a.seq_lens[i][b];
-        S += L > 0 ? min((L + a.split_tokens[i] - 1) / a.split_tokens[i], a.max_splits[i]) : 0;
+        src.first[i] = n;
+        src.S[i] = 0;
+        src.live_n[i] = a.live_splits[i];
+        src.split_tokens[i] = a.split_tokens[i];
+        src.last[i] = a.max_splits[i] - 1;
         src.pl[i] = a.part_lse[i] + bh * a.max_splits[i];
-        src.po4[i] = reinterpret_cast<const float4*>(a.part_o[i] + bh * a.max_splits[i] * a.D + c0);
+        src.po[i] = a.part_o[i] + bh * a.max_splits[i] * a.D + c0;
+        src.len[i] = a.seq_lens[i] + b;
+        n += src.live_n[i];
     }
+    src.n = n;
+    src.e = 0;
+    void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh * a.D + c0)
+                          : (void*)(reinterpret_cast<float*>(a.out) + bh * a.D + c0);
+    float* lse = a.lse_out && blockIdx.z == 0 ? a.lse_out + bh : nullptr;
+    asm volatile("" ::"s"(out), "s"(lse));
     CombineState st = combine_init();
-    if (S <= 8 * (CMB_NT / (W / 4)))
-        combine_fold_src<8>(src, S, W, st);
-    else
-        combine_fold_src<16>(src, S, W, st);
-    combine_finish(st, W, a.out_f16, out, a.lse_out && blockIdx.z == 0 ? a.lse_out + bh : nullptr, sm);
+    combine_fold_src<U>(src, W, st);
+    combine_finish(st, W, a.out_f16, out, lse);
 }
 
 }  // namespace
 
-hipError_t launch_combine_regions(const CombineRegionsArgs& a, hipStream_t s)
+hipError_t launch_combine_regions(const CombineRegionsArgs& args, hipStream_t s)
 {
-    int S = 0;
-    for (int i = 0; i < a.n; ++i) S += a.max_splits[i];
-    dim3 grid(a.Hq, a.B, a.D / chunk_cols(a.D, S));
-    hipLaunchKernelGGL(combine_regions_kernel, grid, dim3(CMB_NT), 0, s, a);
+    CombineRegionsArgs a = args;
+    for (int i = a.n; i < MAX_REGIONS; ++i) {
+        // an unused region: valid pointers, no splits
+        a.part_o[i] = a.part_o[0];
+        a.part_lse[i] = a.part_lse[0];
+        a.seq_lens[i] = a.seq_lens[0];
+        a.split_tokens[i] = a.split_tokens[0];
+        a.max_splits[i] = a.max_splits[0];
+        a.live_splits[i] = 0;
+    }
+    int n = 0;
+    for (int i = 0; i < a.n; ++i) n += a.live_splits[i];
+    const int W = chunk_cols(a.D, n);
+    const dim3 grid(a.Hq, a.B, a.D / W);
+    switch (batch_splits(n, W)) {
+    case 2: hipLaunchKernelGGL(combine_regions_kernel<2>, grid, dim3(CMB_NT), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(combine_regions_kernel<4>, grid, dim3(CMB_NT), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(combine_regions_kernel<8>, grid, dim3(CMB_NT), 0, s, a); break;
+    default: hipLaunchKernelGGL(combine_regions_kernel<16>, grid, dim3(CMB_NT), 0, s, a); break;
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s)
 {
-    dim3 grid(a.Hq, a.B, a.D / chunk_cols(a.D, a.max_splits));
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(CMB_NT), 0, s, a);
+    const int W = chunk_cols(a.D, a.live_splits);
+    const dim3 grid(a.Hq, a.B, a.D / W);
+    switch (batch_splits(a.live_splits, W)) {
+    case 2: hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(CMB_NT), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(CMB_NT), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(CMB_NT), 0, s, a); break;
+    default: hipLaunchKernelGGL(combine_kernel<16>, grid, dim3(CMB_NT), 0, s, a); break;
+    }
     return hipGetLastError();
 }
 

@@ -64,6 +64,15 @@ constexpr float TAU = 8.0f;            // lazy rescale threshold, log2 units
 constexpr float TWO24 = 16777216.0f;   // 2^24
 constexpr float TWOM24 = 1.0f / 16777216.0f;
 constexpr int VMCNT0 = 0x0F70;         // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
+#ifndef KVQ_RING_WIDE
+#define KVQ_RING_WIDE 2
+#endif
+#ifndef KVQ_RING_WIDE_F16
+#define KVQ_RING_WIDE_F16 1
+#endif
+#ifndef KVQ_WPE_WIDE
+#define KVQ_WPE_WIDE 2
+#endif
 #ifndef KVQ_RING
 #define KVQ_RING 2                     // register sets of the quantised head_dim-128 load ring
 #endif
@@ -209,7 +218,9 @@ struct Cfg {
     // registers, measured slower), one where a slice shared by several waves
     // has f16 rows (their registers do not fit twice)
     static constexpr int NSET = DW == 128 && (DS == 1 || (TK != T_F16 && TV != T_F16))
-                                    ? (DS == 1 && TK != T_F16 && TV != T_F16 ? KVQ_RING : 2) : 1;
+                                    ? (DS == 1 && TK != T_F16 && TV != T_F16 ? KVQ_RING : (DS > 1 ? KVQ_RING_WIDE : 2))
+                                    : (DS > 1 ? KVQ_RING_WIDE_F16 : 1);
+    static constexpr int WPE = DS > 1 ? KVQ_WPE_WIDE : 2;              // waves per SIMD the build targets
     static constexpr int SX_FLOATS = DS > 1 ? 2 * WV * 64 * 8 : 1;     // partial-score exchange
     static constexpr float KOFF = TK == T_Q4 ? 8.0f : TK == T_Q8 ? 128.0f : TK == T_Q5_0 ? 16.0f
                                 : TK == T_Q6_0 ? 32.0f : 0.0f;
@@ -280,8 +291,8 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     const int t_end_all = min(t_begin + a.split_tokens, L);
     // Decode step with one new token (NEWROW, the base types): the workgroup
     // whose split holds row L-1 leaves that row out of its tiles, quantises
-    // the new row into it after its tile loop, and merges the row's decoded
-    // values as one more term, so no load waits for those stores.
+    // the new row into it while its first tiles are loading, and merges the
+    // row's decoded values as one more term: no load reads the stored row.
     constexpr bool NEWROW_OK = C::NEWROW && !MQ;
     const bool newrow = NEWROW_OK && a.k_new != nullptr && t_end_all == L;
     const int Lr = newrow ? L - 1 : L;             // rows the tiles read
@@ -962,22 +973,61 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
             }
         }
     }
-    // The new row, after the tile loop: quantised into row L-1 (the block
-    // quantiser of kvq_quantize_append, bit for bit), its decoded values
-    // (scale * code, exact) kept in lds_new: K in [0, D), V in [D, 2D).
+    // The new row: quantised into row L-1 (the block quantiser of
+    // kvq_quantize_append, bit for bit), its decoded values (scale * code,
+    // exact) kept in lds_new: K in [0, D), V in [D, 2D).
     auto newrow_quantise = [&]() {
+        const int j = tid & 31, h = tid >> 5;
+        if constexpr (C::NEW_IT >= 2) {
+            // (head_dim 256 / 512) each half-wave h holds NK K blocks, h + k
+            // HW, then as many V blocks: the 2 NK blocks are quantised in
+            // lockstep and stored after all of them are computed
+            constexpr int HW = C::NTH / 32, NK = C::NEW_IT / 2;
+            static_assert(C::NEW_IT * C::NTH == 2 * C::NB_ROW * 32 && NK * HW == C::NB_ROW, "new-row blocks");
+            uint16_t xk[NK], xv[NK];
 #pragma unroll
-        for (int k = 0; k < C::NEW_IT; ++k) {
-            const int blk2 = (tid >> 5) + k * (C::NTH / 32), j = tid & 31;
-            if (blk2 >= 2 * C::NB_ROW) break;         // (uniform over the half-wave)
-            // the raw value is opaque to the compiler until here, so its load
-            // is waited for only now
-            uint16_t xk = xnew[k];
-            asm volatile("" : "+v"(xk));
-            const bool isv = blk2 >= C::NB_ROW;
-            const int blk = isv ? blk2 - C::NB_ROW : blk2;
+            for (int k = 0; k < NK; ++k) {
+                // the raw values are opaque to the compiler until here, so
+                // their loads are waited for only now
+                uint32_t tk = xnew[k], tv = xnew[NK + k];
+                asm volatile("" : "+v"(tk), "+v"(tv));
+                xk[k] = (uint16_t)tk;
+                xv[k] = (uint16_t)tv;
+            }
+            uint32_t wk[NK], wv[NK];
+            uint16_t dk[NK], dv[NK];
+            float ek[NK], ev[NK];
+            quantize_blocks_lanes_compute<TK, NK>(xk, j, wk, dk, ek);
+            quantize_blocks_lanes_compute<TV, NK>(xv, j, wv, dv, ev);
+            uint8_t* pk[NK];
+            uint8_t* pv[NK];
+            uint16_t* sk[NK];
+            uint16_t* sv[NK];
+            const int64_t rk = krow0 + (L - 1), rv = vrow0 + (L - 1);
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
+                const int blk = h + k * HW;
+                pk[k] = a.k.data + rk * rb(TK, D) + blk * rb(TK, 32);
+                sk[k] = a.k.scales + rk * (D / 32) + blk;
+                pv[k] = a.v.data + rv * rb(TV, D) + blk * rb(TV, 32);
+                sv[k] = a.v.scales + rv * (D / 32) + blk;
+            }
+            quantize_blocks_lanes_store<TK, NK>(pk, sk, j, wk, dk);
+            quantize_blocks_lanes_store<TV, NK>(pv, sv, j, wv, dv);
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
+                lds_new[32 * (h + k * HW) + j] = ek[k];
+                lds_new[32 * (C::NB_ROW + h + k * HW) + j] = ev[k];
+            }
+        } else {
+            // (head_dim 128) one block per half-wave: K for h < NB_ROW, else V
+            uint32_t t = xnew[0];
+            asm volatile("" : "+v"(t));
+            const uint16_t xk = (uint16_t)t;
+            const bool isv = h >= C::NB_ROW;
+            const int blk = isv ? h - C::NB_ROW : h;
             const int64_t row = (isv ? vrow0 : krow0) + (L - 1);
-            lds_new[32 * blk2 + j] =
+            lds_new[32 * h + j] =
                 isv ? quantize_block_lanes_v<TV>(xk, a.v.data + row * rb(TV, D) + blk * rb(TV, 32),
                                                  a.v.scales + row * (D / 32) + blk, j)
                     : quantize_block_lanes_v<TK>(xk, a.k.data + row * rb(TK, D) + blk * rb(TK, 32),
@@ -1013,6 +1063,32 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     // the tiles' loads go out before anything waits for Q
     __builtin_amdgcn_sched_barrier(0);
     init_q();
+    // The new row is quantised and scored while the first tiles are in
+    // flight: its score (log2 units) in m_new (head_dim 256 / 512: the sum of
+    // the waves' slice scores, in a fixed order) or, over whole rows, in
+    // lds_new[2D + column] (written by wave 0).  Its stores precede the
+    // loop's later loads; no load of this launch reads row L-1.
+    float m_new = -INFINITY;
+    if constexpr (NEWROW_OK) {
+        if (newrow) {
+            newrow_quantise();
+            __syncthreads();
+            if constexpr (C::DS > 1) {
+                const float sc = newrow_score_part();
+                if (lq == 0) lds_new[2 * D + 16 * wave + ln] = sc;
+                __syncthreads();
+                float tot = 0.0f;
+#pragma unroll
+                for (int w = 0; w < C::WV; ++w) tot += lds_new[2 * D + 16 * w + ln];
+                m_new = tot * a.scale_log2;
+            } else {
+                if (wave == 0) {
+                    const float sc = newrow_score_part();
+                    if (lq == 0) lds_new[2 * D + ln] = sc * a.scale_log2;
+                }
+            }
+        }
+    }
     // tile it uses K set x; V of tile it is in LDS, V of the next tile in set
     // (x + 1) % NS.  The loop runs whole rounds of the ring with no branch
     // around a load, so the compiler's wait before each use counts exactly
@@ -1038,22 +1114,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     if constexpr (C::DS > 1) {
         // every wave holds the same (m, l) and its own slice of O: write it
         const float l_head = xsum4(l_part);
-        // the new row's term (max m_new, sum 1, row v): its score is the sum
-        // of the waves' slice scores, in a fixed order
-        float m_new = -INFINITY;
-        if constexpr (NEWROW_OK) {
-            if (newrow) {
-                newrow_quantise();
-                __syncthreads();
-                const float sc = newrow_score_part();
-                if (lq == 0) lds_new[2 * D + 16 * wave + ln] = sc;
-                __syncthreads();
-                float tot = 0.0f;
-#pragma unroll
-                for (int w = 0; w < C::WV; ++w) tot += lds_new[2 * D + 16 * w + ln];
-                m_new = tot * a.scale_log2;
-            }
-        }
+        // (the new row's term: max m_new, sum 1, row v)
         if (ln < NC) {
             // (a column that saw no row: l = 0, o = 0, lse = -inf)
             const bool nr = NEWROW_OK && newrow;
@@ -1103,17 +1164,8 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     //      code-offset correction of its block), so each output column is a
     //      four-term weighted sum with no second barrier.
     const float l_head = xsum4(l_part);
-    if constexpr (NEWROW_OK) {
-        if (newrow) newrow_quantise();
-    }
+    (void)m_new;
     __syncthreads();
-    if constexpr (NEWROW_OK) {
-        // its scores in lds_new[2D + column], log2 units
-        if (newrow && wave == 0) {
-            const float sc = newrow_score_part();
-            if (lq == 0) lds_new[2 * D + ln] = sc * a.scale_log2;
-        }
-    }
     uint8_t* marea = merge_lds_bytes<TK, TV, D>(NC) <= lds_cap ? lds_a : lds_merge_dyn;
     float* mw = reinterpret_cast<float*>(marea);          // [WAVES][16]   running max
     float* lw = mw + WAVES * 16;                          // [WAVES][16]   running sum
@@ -1199,7 +1251,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
 }
 
 template <int TK, int TV, int D, bool MQ>
-__global__ void __launch_bounds__((Cfg<TK, TV, D>::NTH)) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__((Cfg<TK, TV, D>::NTH)) __attribute__((amdgpu_waves_per_eu(Cfg<TK, TV, D>::WPE)))
 decode_mfma_kernel(DecodeArgs a)
 {
     using C = Cfg<TK, TV, D>;

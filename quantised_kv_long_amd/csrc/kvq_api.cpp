@@ -363,6 +363,7 @@ int kvq_decode_step_multi(const kvq_plane_desc* k_cache, const kvq_plane_desc* v
     c.D = D;
     c.split_tokens = split_tokens;
     c.max_splits = max_splits;
+    c.live_splits = kvq::grid_splits(a);
     c.out_f16 = out_type == KVQ_F16;
     c.out = out;
     c.lse_out = lse_out;
@@ -391,6 +392,7 @@ int kvq_combine(const float* part_o, const float* part_lse, const int32_t* seq_l
     a.D = D;
     a.split_tokens = split_tokens;
     a.max_splits = max_splits;
+    a.live_splits = max_splits;
     a.out_f16 = out_type == KVQ_F16;
     a.out = out;
     a.lse_out = lse_out;
@@ -495,7 +497,7 @@ int kvq_decode_step_mixed(const kvq_plane_desc* k_tail, const kvq_plane_desc* v_
     }
     if (e != hipSuccess) return KVQ_ERR_LAUNCH;
 
-    kvq::CombineRegionsArgs c;
+    kvq::CombineRegionsArgs c{};
     c.n = 2;
     const kvq::DecodeArgs* r[2] = {&t, &w};
     for (int i = 0; i < 2; ++i) {
@@ -504,6 +506,7 @@ int kvq_decode_step_mixed(const kvq_plane_desc* k_tail, const kvq_plane_desc* v_
         c.seq_lens[i] = r[i]->seq_lens;
         c.split_tokens[i] = r[i]->split_tokens;
         c.max_splits[i] = r[i]->max_splits;
+        c.live_splits[i] = kvq::grid_splits(*r[i]);
     }
     c.B = B;
     c.Hq = Hq;
@@ -524,7 +527,7 @@ int kvq_combine_regions(int n_regions, const float* const* part_o, const float* 
     if (B < 1 || Hq < 1 || !valid_head_dim(D)) return KVQ_ERR_SHAPE;
     if (B > 65535 || Hq > 65535) return KVQ_ERR_SHAPE;
     if (!aligned(out, 16) || (lse_out && !aligned(lse_out, 4))) return KVQ_ERR_ALIGN;
-    kvq::CombineRegionsArgs a;
+    kvq::CombineRegionsArgs a{};
     a.n = n_regions;
     for (int i = 0; i < n_regions; ++i) {
         if (!part_o[i] || !part_lse[i] || !seq_lens[i]) return KVQ_ERR_NULL;
@@ -538,6 +541,7 @@ int kvq_combine_regions(int n_regions, const float* const* part_o, const float* 
         a.seq_lens[i] = seq_lens[i];
         a.split_tokens[i] = split_tokens[i];
         a.max_splits[i] = max_splits[i];
+        a.live_splits[i] = max_splits[i];
     }
     a.B = B;
     a.Hq = Hq;
@@ -604,6 +608,7 @@ int kvq_decode_step(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache
     c.D = D;
     c.split_tokens = split_tokens;
     c.max_splits = max_splits;
+    c.live_splits = kvq::grid_splits(a);
     c.out_f16 = out_type == KVQ_F16;
     c.out = out;
     c.lse_out = lse_out;

@@ -65,6 +65,10 @@ struct CombineRegionsArgs {
     const int32_t* seq_lens[MAX_REGIONS];
     int split_tokens[MAX_REGIONS];
     int max_splits[MAX_REGIONS];
+    // splits of each region that can hold rows: min(max_splits,
+    // ceil(max_seq_len / split_tokens)) where max_seq_len is known, else
+    // max_splits
+    int live_splits[MAX_REGIONS];
     int B, Hq, D;
     bool out_f16;
     void* out;
@@ -76,6 +80,7 @@ struct CombineArgs {
     const float* part_lse;
     const int32_t* seq_lens;
     int B, Hq, D, split_tokens, max_splits;
+    int live_splits;   // as in CombineRegionsArgs
     bool out_f16;
     void* out;
     float* lse_out;

@@ -211,73 +211,127 @@ __device__ __forceinline__ void quantize_block_ext(const uint16_t* __restrict__ 
 // the block maximum found by cross-lane exchanges.  Every lane performs the
 // same float operations on its value as quantize_block does, so the bytes are
 // identical.  All 32 lanes of the half-wave must call it together.
-// quantize_block_lanes_v takes the lane's value xh (element j of the block,
-// fp16 bits) already loaded, so a caller can issue the loads of several
-// blocks before quantising any of them.  It returns the value the stored
-// bytes decode to for element j (scale * code, exact in fp32).
+// quantize_blocks_lanes_compute takes the lanes' values xh[k] (element j of
+// block k, fp16 bits) already loaded, so a caller can issue the loads of
+// several blocks before quantising any of them, and quantises N blocks in
+// lockstep (their cross-lane exchanges overlap; no branch, no store).  Per
+// block and lane it gives the word w that quantize_blocks_lanes_store writes
+// (the lane's fp16 value; for q8_0 and q4_0 the data word the lane stores,
+// when it stores one), the fp16 scale d16 and the value the stored bytes
+// decode to for element j (scale * code, exact in fp32).
+template <int T, int N>
+__device__ __forceinline__ void quantize_blocks_lanes_compute(const uint16_t (&xh)[N], int j, uint32_t (&w)[N],
+                                                              uint16_t (&d16)[N], float (&dec)[N])
+{
+    if constexpr (T == T_F16) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            w[k] = xh[k];
+            d16[k] = 0;
+            dec[k] = h2f(xh[k]);
+        }
+    } else if constexpr (T == T_Q8) {
+        float x[N], amax[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            x[k] = h2f(xh[k]);
+            amax[k] = fmaxf(0.0f, fabsf(x[k]));   // as the sequential fold from 0 (NaN drops out)
+        }
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1)
+#pragma unroll
+            for (int k = 0; k < N; ++k) amax[k] = fmaxf(amax[k], __shfl_xor(amax[k], off, 32));
+        uint32_t c[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            d16[k] = f2h_rne(amax[k] / 127.0f);
+            const float d = h2f(d16[k]);
+            // (a zero scale stores code 0; the quotient is then not used)
+            const float r = fminf(fmaxf(roundf(x[k] / d), -127.0f), 127.0f);
+            c[k] = d != 0.0f ? (uint32_t)(uint8_t)(int8_t)(int)r : 0u;
+            dec[k] = d * (float)(int8_t)c[k];
+        }
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            w[k] = c[k] | (__shfl_down(c[k], 1, 32) << 8) | (__shfl_down(c[k], 2, 32) << 16) |
+                   (__shfl_down(c[k], 3, 32) << 24);
+    } else {
+        // first value of largest magnitude: a value is a candidate when its
+        // magnitude exceeds 0 (NaN never is); larger magnitude wins, then the
+        // lower index.  No candidate: s = +0.
+        float x[N], a[N];
+        int idx[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            x[k] = h2f(xh[k]);
+            const float ax = fabsf(x[k]);
+            a[k] = ax > 0.0f ? ax : 0.0f;
+            idx[k] = a[k] > 0.0f ? j : 32;
+        }
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) {
+#pragma unroll
+            for (int k = 0; k < N; ++k) {
+                const float a2 = __shfl_xor(a[k], off, 32);
+                const int i2 = __shfl_xor(idx[k], off, 32);
+                const bool take = a2 > a[k] || (a2 == a[k] && i2 < idx[k]);
+                a[k] = take ? a2 : a[k];
+                idx[k] = take ? i2 : idx[k];
+            }
+        }
+        uint32_t n[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            const float xs = __shfl(x[k], idx[k] & 31, 32);
+            const float smax = idx[k] < 32 ? xs : 0.0f;
+            const uint16_t mag16 = f2h_rne(fabsf(smax) * 0.125f);
+            d16[k] = (uint16_t)(mag16 | (smax < 0.0f ? 0 : 0x8000));
+            const float d = h2f(d16[k]);
+            const float r = fminf(fmaxf(roundf(x[k] / d), -8.0f), 7.0f);
+            n[k] = d != 0.0f ? (uint32_t)((int)r + 8) : 8u;
+            dec[k] = d * (float)((int)n[k] - 8);
+        }
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            // byte j (< 16) holds element j (low nibble) and element j+16
+            const uint32_t byte = n[k] | (__shfl_down(n[k], 16, 32) << 4);
+            w[k] = (byte & 0xff) | ((__shfl_down(byte, 1, 32) & 0xff) << 8) |
+                   ((__shfl_down(byte, 2, 32) & 0xff) << 16) | ((__shfl_down(byte, 3, 32) & 0xff) << 24);
+        }
+    }
+}
+
+// The stores of N blocks quantised by quantize_blocks_lanes_compute: block k
+// at dst[k] (data) and sdst[k] (its scale).
+template <int T, int N>
+__device__ __forceinline__ void quantize_blocks_lanes_store(uint8_t* const (&dst)[N], uint16_t* const (&sdst)[N],
+                                                            int j, const uint32_t (&w)[N], const uint16_t (&d16)[N])
+{
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        if constexpr (T == T_F16) {
+            reinterpret_cast<uint16_t*>(dst[k])[j] = (uint16_t)w[k];
+        } else {
+            if ((T == T_Q8 || j < 16) && (j & 3) == 0) *reinterpret_cast<uint32_t*>(dst[k] + j) = w[k];
+            if (j == 0) *sdst[k] = d16[k];
+        }
+    }
+}
+
+// One block: quantised, stored, and the lane's decoded value returned.
 template <int T>
 __device__ __forceinline__ float quantize_block_lanes_v(uint16_t xh, uint8_t* __restrict__ dst,
                                                         uint16_t* __restrict__ sdst, int j)
 {
-    if constexpr (T == T_F16) {
-        reinterpret_cast<uint16_t*>(dst)[j] = xh;
-        return h2f(xh);
-    } else {
-        const float x = h2f(xh);
-        if constexpr (T == T_Q8) {
-            float amax = fmaxf(0.0f, fabsf(x));   // as the sequential fold from 0 (NaN drops out)
-#pragma unroll
-            for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
-            const uint16_t d16 = f2h_rne(amax / 127.0f);
-            const float d = h2f(d16);
-            uint32_t c = 0;
-            if (d != 0.0f) {
-                float r = roundf(x / d);
-                r = fminf(fmaxf(r, -127.0f), 127.0f);
-                c = (uint32_t)(uint8_t)(int8_t)(int)r;
-            }
-            const uint32_t w = c | (__shfl_down(c, 1, 32) << 8) | (__shfl_down(c, 2, 32) << 16) |
-                               (__shfl_down(c, 3, 32) << 24);
-            if ((j & 3) == 0) *reinterpret_cast<uint32_t*>(dst + j) = w;
-            if (j == 0) *sdst = d16;
-            return d * (float)(int8_t)c;
-        } else {
-            // first value of largest magnitude: a value is a candidate when
-            // its magnitude exceeds 0 (NaN never is); larger magnitude wins,
-            // then the lower index.  No candidate: s = +0.
-            const float ax = fabsf(x);
-            float a = ax > 0.0f ? ax : 0.0f;
-            int idx = a > 0.0f ? j : 32;
-#pragma unroll
-            for (int off = 16; off >= 1; off >>= 1) {
-                const float a2 = __shfl_xor(a, off, 32);
-                const int i2 = __shfl_xor(idx, off, 32);
-                if (a2 > a || (a2 == a && i2 < idx)) {
-                    a = a2;
-                    idx = i2;
-                }
-            }
-            const float xs = __shfl(x, idx & 31, 32);
-            const float smax = idx < 32 ? xs : 0.0f;
-            const uint16_t mag16 = f2h_rne(fabsf(smax) * 0.125f);
-            const uint16_t d16 = (uint16_t)(mag16 | (smax < 0.0f ? 0 : 0x8000));
-            const float d = h2f(d16);
-            uint32_t n = 8;
-            if (d != 0.0f) {
-                float r = roundf(x / d);
-                r = fminf(fmaxf(r, -8.0f), 7.0f);
-                n = (uint32_t)((int)r + 8);
-            }
-            // byte j (< 16) holds element j (low nibble) and element j+16
-            const uint32_t byte = n | (__shfl_down(n, 16, 32) << 4);
-            const uint32_t w = (byte & 0xff) | ((__shfl_down(byte, 1, 32) & 0xff) << 8) |
-                               ((__shfl_down(byte, 2, 32) & 0xff) << 16) |
-                               ((__shfl_down(byte, 3, 32) & 0xff) << 24);
-            if (j < 16 && (j & 3) == 0) *reinterpret_cast<uint32_t*>(dst + j) = w;
-            if (j == 0) *sdst = d16;
-            return d * (float)((int)n - 8);
-        }
-    }
+    const uint16_t x1[1] = {xh};
+    uint8_t* const d1[1] = {dst};
+    uint16_t* const s1[1] = {sdst};
+    uint32_t w[1];
+    uint16_t d16[1];
+    float dec[1];
+    quantize_blocks_lanes_compute<T, 1>(x1, j, w, d16, dec);
+    quantize_blocks_lanes_store<T, 1>(d1, s1, j, w, d16);
+    return dec[0];
 }
 
 template <int T>
