@@ -304,9 +304,9 @@ int kvq_decode_step_multi(const kvq_plane_desc* k_cache, const kvq_plane_desc* v
                           void* stream);
 
 /* Kernel family for kvq_decode_attn_variant.  The matrix-core kernel covers
- * every pair of f16, q8_0 and q4_0 at D = 128, 256 and 512, and
- * at D = 128 the pairs q8_0/q6_0, q8_0/q5_0, q6_0/q6_0, q6_0/q4_0,
- * q5_0/q5_0, q5_1/q5_1, q4_1/q4_1 and q5_1/q4_0.  The vector-ALU kernel
+ * D = 128, 256 and 512 with every pair of f16, q8_0 and q4_0 and the pairs
+ * q8_0/q6_0, q8_0/q5_0, q6_0/q6_0, q6_0/q4_0, q5_0/q5_0, q5_1/q5_1,
+ * q4_1/q4_1 and q5_1/q4_0.  The vector-ALU kernel
  * covers every pair of types at every valid D; AUTO picks the matrix cores
  * where they cover the call. */
 enum {

@@ -195,7 +195,13 @@ struct Cfg {
     static constexpr int RBV_LDS = VBYTES ? DW : RBV;                  // LDS bytes of a V row (slice)
     static constexpr int KU = KNIB ? 1 : (TK == T_Q8 ? 2 : 4);         // dwords per lane per block
     static constexpr int KDW = 4 * KU * NBG;                           // K code dwords per lane per subtile
-    static constexpr int KHW = KHB * NB;                               // K high-bit dwords of a row
+    static constexpr int KHW = KHB * NB;                               // K high-bit dwords of a row (slice)
+    // a row of the 4-bit-code types holds the D/2 nibble bytes of all its
+    // blocks, then (q5, q6) the high-bit words of all its blocks: slice w's
+    // codes start w * DW/2 bytes in, its high bits D/2 + w * NB * 4 * KHB
+    // bytes in; the other types' slices are contiguous (w * RBK)
+    static constexpr int KSL = KNIB ? DW / 2 : RBK;                   // code bytes before slice 1 (K)
+    static constexpr int VSL = VBYTES ? DW / 2 : RBV;                 // the same for V
     static constexpr int BBK = KNIB ? 16 : RBK / NB;                   // code bytes of a block (K row)
     static constexpr int V_BYTES = TT * RBV_LDS;                       // V tile bytes in LDS (slice)
     static constexpr int V_LOADS = VBYTES ? 0 : V_BYTES / 1024;        // 16-byte loads per lane
@@ -233,7 +239,7 @@ struct Cfg {
     static constexpr int NEW_IT = (2 * NB_ROW * 32 + NTH - 1) / NTH;   // new-row blocks per half-wave
     static constexpr bool VALID = V_BYTES % 1024 == 0 && SK_BYTES % 256 == 0 && SV_BYTES % 256 == 0 &&
                                   (!VBYTES || (TT * NB) % 64 == 0) && V_DW <= (DW == 128 ? 32 : 64) &&
-                                  WV * BUF <= 64 * 1024 && (!NEWT || (D == 128 && DS == 1));
+                                  WV * BUF <= 64 * 1024;
 };
 
 // Bytes of the four-wave merge area: per wave and score column the running
@@ -358,9 +364,10 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
             __builtin_amdgcn_s_waitcnt(VMCNT0);
             __syncthreads();
         }
-    } else if (!NEWROW_OK && a.k_new != nullptr && t_end == L) {
-        // 2*NB_ROW blocks (K then V), one aligned half-wave of 32 lanes per block
-        if constexpr (C::NEWT) {
+    } else if constexpr (C::NEWT) {
+        if (a.k_new != nullptr && t_end == L) {
+            // 2*NB_ROW blocks (K then V), one aligned half-wave of 32 lanes
+            // per block
             for (int blk2 = tid >> 5; blk2 < 2 * C::NB_ROW; blk2 += C::NTH / 32) {
                 const bool isv = blk2 >= C::NB_ROW;
                 const int blk = isv ? blk2 - C::NB_ROW : blk2;
@@ -369,41 +376,12 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
                 if (isv) write_block_lanes_d<TV, D>(src, a.v, row, blk, tid & 31);
                 else write_block_lanes_d<TK, D>(src, a.k, row, blk, tid & 31);
             }
-        } else {
-            // each half-wave loads its value of every block it handles first,
-            // so the loads are in flight together, then quantises them
-            constexpr int HW = C::NTH / 32, NIT = (2 * C::NB_ROW + HW - 1) / HW;
-            uint16_t xh[NIT];
-#pragma unroll
-            for (int k = 0; k < NIT; ++k) {
-                const int blk2 = (tid >> 5) + k * HW;
-                if (blk2 < 2 * C::NB_ROW) {
-                    const bool isv = blk2 >= C::NB_ROW;
-                    const int blk = isv ? blk2 - C::NB_ROW : blk2;
-                    xh[k] = ((isv ? a.v_new : a.k_new) + ((int64_t)b * a.Hkv + g) * D + 32 * blk)[tid & 31];
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < NIT; ++k) {
-                const int blk2 = (tid >> 5) + k * HW;
-                if (blk2 < 2 * C::NB_ROW) {
-                    const bool isv = blk2 >= C::NB_ROW;
-                    const int blk = isv ? blk2 - C::NB_ROW : blk2;
-                    const int64_t row = (isv ? vrow0 : krow0) + (L - 1);
-                    if (isv)
-                        quantize_block_lanes_v<TV>(xh[k], a.v.data + row * rb(TV, D) + blk * rb(TV, 32),
-                                                   a.v.scales + row * (D / 32) + blk, tid & 31);
-                    else
-                        quantize_block_lanes_v<TK>(xh[k], a.k.data + row * rb(TK, D) + blk * rb(TK, 32),
-                                                   a.k.scales + row * (D / 32) + blk, tid & 31);
-                }
-            }
+            // the row is read back only by this workgroup, whose loads of that
+            // tile are issued after the barrier: the stores must be complete
+            // (acknowledged by L2) first; no other workgroup reads these lines
+            __builtin_amdgcn_s_waitcnt(VMCNT0);
+            __syncthreads();
         }
-        // the row is read back only by this workgroup, whose loads of that
-        // tile are issued after the barrier: the stores must be complete
-        // (acknowledged by L2) first; no other workgroup reads these lines
-        __builtin_amdgcn_s_waitcnt(VMCNT0);
-        __syncthreads();
     }
 
     // ---- Q as the B operand of S^T = K Q^T: column ln = head, lane row lq
@@ -529,16 +507,18 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
         if constexpr (C::DS == 1) return (uint32_t)(4 * c4);
         else return (uint32_t)((c4 / wpr) * srow + wsl * C::NB * spb * 2 + 4 * (c4 % wpr));
     };
-    const uint32_t krow_off[2] = {(uint32_t)(krow_rel0 * C::RBK_ROW + wsl * C::RBK),
-                                  (uint32_t)((krow_rel0 + 4) * C::RBK_ROW + wsl * C::RBK)};
+    const uint32_t krow_off[2] = {(uint32_t)(krow_rel0 * C::RBK_ROW + wsl * C::KSL),
+                                  (uint32_t)((krow_rel0 + 4) * C::RBK_ROW + wsl * C::KSL)};
+    // the slice's K high-bit words, relative to its codes
+    const uint32_t khoff = (uint32_t)(D / 2 + wsl * (C::KHB * 4 * C::NB - C::KSL));
 
     // one K row's share of this lane (ro: the row's byte offset in the plane)
     auto load_k_row = [&](uint32_t ro, uint32_t (&x)[KR]) {
         if constexpr (C::KHB > 0) {
-            // the row's high-bit words, after its D/2 nibble bytes
+            // the slice's high-bit words, after the row's D/2 nibble bytes
 #pragma unroll
             for (int u = 0; u < C::KHW / 4; ++u) {
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rk, ro + C::DW / 2 + 16 * u, 0, 0);
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rk, ro + khoff + 16 * u, 0, 0);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) x[C::KDW + 4 * u + c] = v[c];
             }
@@ -595,14 +575,17 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
 #pragma unroll
             for (int k = 0; k < C::V_UNITS; ++k) {
                 const int u = k * 64 + lane;
-                const uint32_t ro = (uint32_t)(t0 + u / C::NB) * C::RBV_ROW;
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rv, ro + 16 * (u % C::NB), 0, 0);
+                const uint32_t ro = (uint32_t)(t0 + u / C::NB) * C::RBV_ROW;   // the row's start
+                const u32x4 v =
+                    __builtin_amdgcn_raw_buffer_load_b128(rv, ro + wsl * C::VSL + 16 * (u % C::NB), 0, 0);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) vr[k * (4 + C::VHB) + c] = v[c];
+                // the slice's high-bit words: D/2 + (slice block) * 4 * VHB
+                const uint32_t vho = ro + D / 2 + 4 * C::VHB * (wsl * C::NB + u % C::NB);
                 if constexpr (C::VHB == 1) {
-                    vr[k * 5 + 4] = __builtin_amdgcn_raw_buffer_load_b32(rv, ro + C::DW / 2 + 4 * (u % C::NB), 0, 0);
+                    vr[k * 5 + 4] = __builtin_amdgcn_raw_buffer_load_b32(rv, vho, 0, 0);
                 } else if constexpr (C::VHB == 2) {
-                    const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(rv, ro + C::DW / 2 + 8 * (u % C::NB), 0, 0);
+                    const u32x2 h = __builtin_amdgcn_raw_buffer_load_b64(rv, vho, 0, 0);
                     vr[k * 6 + 4] = h[0];
                     vr[k * 6 + 5] = h[1];
                 }
@@ -1114,6 +1097,18 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     if constexpr (C::DS > 1) {
         // every wave holds the same (m, l) and its own slice of O: write it
         const float l_head = xsum4(l_part);
+        // V with block minima (q4_1, q5_1): block kb's sum of p * m for head
+        // ln, held by lane ln (lane row 0) in bacc[0][kb], enters in the
+        // accumulators' units (2^-24)
+        float vmin[C::VMIN ? C::NB : 1];
+        if constexpr (C::VMIN) {
+            static_assert(C::NB <= 4, "block minima of one lane row");
+#pragma unroll
+            for (int kb = 0; kb < C::NB; ++kb) {
+                const float x = bacc[0][kb];
+                vmin[kb] = __shfl(x, ln) * TWOM24;
+            }
+        }
         // (the new row's term: max m_new, sum 1, row v)
         if (ln < NC) {
             // (a column that saw no row: l = 0, o = 0, lse = -inf)
@@ -1132,7 +1127,8 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     o[i] = oacc[t][i];
-                    if constexpr (C::V_SCALE) o[i] -= bacc[t >> 1][i];
+                    if constexpr (C::VMIN) o[i] += vmin[t >> 1];
+                    else if constexpr (C::V_SCALE) o[i] -= bacc[t >> 1][i];
                     o[i] *= inv;
                     if (nr) {
                         // the column register i of tile t holds (see the stores below)
@@ -1362,21 +1358,38 @@ bool new_pair(int tk, int tv)
     return false;
 }
 
-bool new_supports(const DecodeArgs& a)
+template <int D>
+bool new_supports_d(const DecodeArgs& a)
 {
-    if (a.D != 128) return false;
 #define KVQ_X(K, V) \
-    if (a.tk == K && a.tv == V) return cfg_valid<K, V, 128>() && lds_bytes<K, V, 128>(a.nq * a.G) <= 160 * 1024;
+    if (a.tk == K && a.tv == V) return cfg_valid<K, V, D>() && lds_bytes<K, V, D>(a.nq * a.G) <= 160 * 1024;
     KVQ_NEW_PAIRS(KVQ_X)
 #undef KVQ_X
     return false;
 }
 
-hipError_t new_launch(const DecodeArgs& a, hipStream_t s)
+bool new_supports(const DecodeArgs& a)
 {
-#define KVQ_X(K, V) if (a.tk == K && a.tv == V) return launch3<K, V, 128>(a, s);
+    if (a.D == 128) return new_supports_d<128>(a);
+    if (a.D == 256) return new_supports_d<256>(a);
+    if (a.D == 512) return new_supports_d<512>(a);
+    return false;
+}
+
+template <int D>
+hipError_t new_launch_d(const DecodeArgs& a, hipStream_t s)
+{
+#define KVQ_X(K, V) if (a.tk == K && a.tv == V) return launch3<K, V, D>(a, s);
     KVQ_NEW_PAIRS(KVQ_X)
 #undef KVQ_X
+    return hipErrorInvalidConfiguration;
+}
+
+hipError_t new_launch(const DecodeArgs& a, hipStream_t s)
+{
+    if (a.D == 128) return new_launch_d<128>(a, s);
+    if (a.D == 256) return new_launch_d<256>(a, s);
+    if (a.D == 512) return new_launch_d<512>(a, s);
     return hipErrorInvalidConfiguration;
 }
 

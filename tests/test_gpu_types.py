@@ -123,7 +123,7 @@ CASES = [
 
 
 # pairs with the further types that the matrix-core kernel is built for
-# (head_dim 128, one query token)
+# (head_dim 128, 256 and 512; one or several query tokens)
 MFMA_PAIRS = {("q8_0", "q6_0"), ("q8_0", "q5_0"), ("q6_0", "q6_0"), ("q6_0", "q4_0"), ("q5_0", "q5_0"),
               ("q5_1", "q5_1"), ("q4_1", "q4_1"), ("q5_1", "q4_0")}
 
@@ -133,7 +133,7 @@ MFMA_PAIRS = {("q8_0", "q6_0"), ("q8_0", "q5_0"), ("q6_0", "q6_0"), ("q6_0", "q4
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_decode_matches_oracle(tk, tv, case, variant):
     B, Hkv, G, D, lens, st = CASES[case]
-    covered = (tk, tv) in MFMA_PAIRS and D == 128
+    covered = (tk, tv) in MFMA_PAIRS and D in (128, 256, 512)
     note(f"decode {variant} {tk}/{tv} B={B} Hkv={Hkv} G={G} D={D} lens={lens} split={st}")
     dev = "cuda"
     seed = 3300 + case
@@ -161,12 +161,13 @@ def test_decode_matches_oracle(tk, tv, case, variant):
 
 
 def test_matrix_core_kernel_reports_what_it_does_not_cover():
-    """The further types on the matrix cores: head_dim 128 only (KVQ_ERR_SHAPE
-    otherwise, also for multi-query decode; kvq_decode_attn falls back to the
-    vector ALUs for single-token decode)."""
+    """The further types on the matrix cores: the listed pairs at head_dim 128,
+    256 and 512 only (KVQ_ERR_SHAPE otherwise, also for multi-query decode;
+    kvq_decode_attn falls back to the vector ALUs for single-token decode)."""
     dev = "cuda"
-    for D, nq in ((256, 1), (256, 2)):
-        kc, vc = fill_pair("q5_1", "q4_0", synth.normal_f16((1, 1, 64, D), 1, dev),
+    for (tk, tv), D, nq in ((("q5_1", "q4_0"), 64, 1), (("q5_1", "q4_0"), 64, 2),
+                            (("q4_1", "q8_0"), 256, 1), (("q4_1", "q8_0"), 256, 2)):
+        kc, vc = fill_pair(tk, tv, synth.normal_f16((1, 1, 64, D), 1, dev),
                            synth.normal_f16((1, 1, 64, D), 2, dev))
         with pytest.raises(_lib.KVQError) as e:
             if nq == 1:
@@ -178,16 +179,17 @@ def test_matrix_core_kernel_reports_what_it_does_not_cover():
         assert e.value.status == -2
 
 
-@pytest.mark.parametrize("tk,tv", [("q5_1", "q4_0"), ("q6_0", "q6_0")])
-def test_decode_step_is_append_attention_merge(tk, tv):
-    """kvq_decode_step on these types (append, vector-ALU attention, merge) equals
-    the three calls bit for bit, and the oracle over the oracle-quantised rows
-    within the tolerance."""
+@pytest.mark.parametrize("D", [128, 256, 512])
+@pytest.mark.parametrize("tk,tv", [("q5_1", "q4_0"), ("q6_0", "q6_0"), ("q4_1", "q4_1")])
+def test_decode_step_is_append_attention_merge(tk, tv, D):
+    """kvq_decode_step on these types (the attention kernel writes the new row,
+    then the merge) equals the three calls bit for bit, and the oracle over
+    the oracle-quantised rows within the tolerance."""
     dev = "cuda"
-    B, Hkv, G, D, st = 2, 2, 5, 128, 128
+    B, Hkv, G, st = 2, 2, 5, 128
     lens = [300, 77]
     cap = max(lens)
-    note(f"decode step {tk}/{tv}")
+    note(f"decode step {tk}/{tv} D={D}")
     k = synth.normal_f16((B, Hkv, cap, D), 71, dev)
     v = synth.normal_f16((B, Hkv, cap, D), 72, dev)
     q = synth.normal_f16((B, Hkv * G, D), 73, dev)
@@ -312,16 +314,17 @@ def test_fused_step_rows_bit_exact(t):
     assert np.all(np.isfinite(out.cpu().numpy()))
 
 
+@pytest.mark.parametrize("D", [128, 256, 512])
 @pytest.mark.parametrize("tk,tv", sorted(MFMA_PAIRS))
-def test_multi_query_decode_matches_oracle(tk, tv):
+def test_multi_query_decode_matches_oracle(tk, tv, D):
     """Multi-query decode (n_q tokens, causal among them) of the further types on
     the matrix cores against the oracle, token by token; and the fused
     multi-query step equals append + attention + merge bit for bit."""
     from .test_gpu_multi import oracle_multi, run_multi
     dev = "cuda"
-    B, Hkv, G, D, nq, st = 2, 2, 5, 128, 3, 64
+    B, Hkv, G, nq, st = 2, 2, 5, 3, 64
     lens = [300, 130]                      # the second: query tokens across a split boundary
-    note(f"multi {tk}/{tv}")
+    note(f"multi {tk}/{tv} D={D}")
     cap = max(lens)
     kc, vc = fill_pair(tk, tv, synth.normal_f16((B, Hkv, cap, D), 61, dev),
                        synth.normal_f16((B, Hkv, cap, D), 62, dev))
