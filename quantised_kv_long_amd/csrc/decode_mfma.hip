@@ -64,6 +64,13 @@ constexpr float TAU = 8.0f;            // lazy rescale threshold, log2 units
 constexpr float TWO24 = 16777216.0f;   // 2^24
 constexpr float TWOM24 = 1.0f / 16777216.0f;
 constexpr int VMCNT0 = 0x0F70;         // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
+// Build-time knobs of the load ring (the defaults are the measured best):
+// register sets of the quantised head_dim-128 ring, of the head_dim 256/512
+// ring (quantised rows; fp16 rows), and the waves per SIMD a head_dim 256/512
+// instance is built for (1 lets it use up to 512 registers).
+#ifndef KVQ_RING
+#define KVQ_RING 2
+#endif
 #ifndef KVQ_RING_WIDE
 #define KVQ_RING_WIDE 2
 #endif
@@ -72,9 +79,6 @@ constexpr int VMCNT0 = 0x0F70;         // s_waitcnt vmcnt(0) (expcnt, lgkmcnt un
 #endif
 #ifndef KVQ_WPE_WIDE
 #define KVQ_WPE_WIDE 2
-#endif
-#ifndef KVQ_RING
-#define KVQ_RING 2                     // register sets of the quantised head_dim-128 load ring
 #endif
 
 __host__ __device__ constexpr int rb(int t, int D) { return data_row_bytes(t, D); }
