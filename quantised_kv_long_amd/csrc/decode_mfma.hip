@@ -279,7 +279,7 @@ __device__ __forceinline__ void write_block_lanes_d(const uint16_t* src, const P
                                     blk, D, j);
 }
 
-template <int TK, int TV, int D, bool MQ>
+template <int TK, int TV, int D, bool MQ, bool SHORT = false>
 __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint8_t* const lds_a,
                                           const size_t lds_cap, float* const lds_sx,
                                           uint8_t* const lds_merge_dyn, float* const lds_new)
@@ -1082,17 +1082,33 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     // the loads issued after it.  A slot past the wave's last tile (at most
     // NS - 1 per wave) runs on rows at or past L: its loads are out of range
     // (zeros, no memory access) and every row is masked out of the softmax.
+    //   SHORT (splits of fewer tiles per wave than a round holds, chosen
+    //   on the host): the last round runs only the slots whose tile exists (a
+    //   branch per slot, after the loop), so a wave with one tile computes one
+    //   tile, not a whole round.  Otherwise every round is whole.
     if (it < ntiles) {
         stage(vrs[0], srs[0]);
         issue_vs(it + NS * W, vrs[0], srs[0]);
         const int rounds = ((ntiles - it + W - 1) / W + NS - 1) / NS;
-        for (int r = 0; r < rounds; ++r) {
+        for (int r = 0; r < (SHORT ? rounds - 1 : rounds); ++r) {
 #pragma unroll
             for (int x = 0; x < NS; ++x) {
                 compute(it, krs[x], it + NS * W);
                 const int y = (x + 1) % NS;
                 stage(vrs[y], srs[y]);
                 issue_vs(it + (NS + 1) * W, vrs[y], srs[y]);
+                it += W;
+            }
+        }
+        if constexpr (SHORT) {
+#pragma unroll
+            for (int x = 0; x < NS; ++x) {
+                if (it < ntiles) {
+                    compute(it, krs[x], it + NS * W);
+                    const int y = (x + 1) % NS;
+                    stage(vrs[y], srs[y]);
+                    issue_vs(it + (NS + 1) * W, vrs[y], srs[y]);
+                }
                 it += W;
             }
         }
@@ -1250,7 +1266,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     }
 }
 
-template <int TK, int TV, int D, bool MQ>
+template <int TK, int TV, int D, bool MQ, bool SHORT>
 __global__ void __launch_bounds__((Cfg<TK, TV, D>::NTH)) __attribute__((amdgpu_waves_per_eu(Cfg<TK, TV, D>::WPE)))
 decode_mfma_kernel(DecodeArgs a)
 {
@@ -1259,7 +1275,7 @@ decode_mfma_kernel(DecodeArgs a)
     __shared__ __attribute__((aligned(16))) float lds_sx[C::SX_FLOATS];
     __shared__ __attribute__((aligned(16))) float lds_new[C::NEWROW && !MQ ? 2 * D + 64 : 1];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
-    decode_wg<TK, TV, D, MQ>(a, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn, lds_new);
+    decode_wg<TK, TV, D, MQ, SHORT>(a, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn, lds_new);
 }
 
 // The two regions of a mixed cache in one launch (HAL #582 section 5 P2): the
@@ -1315,20 +1331,33 @@ size_t lds_bytes(int nc)
            dyn_lds_bytes<TK, TV, D>(nc);
 }
 
-template <int TK, int TV, int D, bool MQ>
-hipError_t launch4(const DecodeArgs& a, hipStream_t s)
+template <int TK, int TV, int D, bool MQ, bool SHORT>
+hipError_t launch5(const DecodeArgs& a, hipStream_t s)
 {
     dim3 grid(grid_splits(a), a.Hkv, a.B);
     const int nc = a.nq * a.G;
     const size_t dyn = dyn_lds_bytes<TK, TV, D>(nc);
     if (lds_bytes<TK, TV, D>(nc) > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&decode_mfma_kernel<TK, TV, D, MQ>),
+            reinterpret_cast<const void*>(&decode_mfma_kernel<TK, TV, D, MQ, SHORT>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((decode_mfma_kernel<TK, TV, D, MQ>), grid, dim3(Cfg<TK, TV, D>::NTH), dyn, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<TK, TV, D, MQ, SHORT>), grid, dim3(Cfg<TK, TV, D>::NTH), dyn, s, a);
     return hipGetLastError();
+}
+
+template <int TK, int TV, int D, bool MQ>
+hipError_t launch4(const DecodeArgs& a, hipStream_t s)
+{
+    using C = Cfg<TK, TV, D>;
+    if constexpr (!MQ && C::DS == 1) {
+        // a full split's tiles per wave that are not a whole number of rounds
+        // (e.g. 128-row splits: one tile per wave, two slots per round)
+        const int tpw = ((a.split_tokens + TT - 1) / TT + WAVES - 1) / WAVES;
+        if (tpw % C::NSET != 0) return launch5<TK, TV, D, MQ, true>(a, s);
+    }
+    return launch5<TK, TV, D, MQ, false>(a, s);
 }
 
 template <int TK, int TV, int D>
