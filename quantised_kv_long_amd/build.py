@@ -39,6 +39,12 @@ HIP_FLAGS = [
     # v_mfma): no accumulator-register copies around every use, and the
     # head_dim-128 decode kernels fit in 256 registers (two waves per SIMD)
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # the first kernel-argument dwords (up to the 14 free user SGPRs) arrive in
+    # scalar registers instead of being loaded from the argument buffer: the
+    # merge kernel takes scalar arguments so that it reads no argument from
+    # memory (struct arguments are not preloaded; a launch on a part without
+    # preloading runs the compiler's load-and-branch preamble instead)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -41,29 +41,34 @@ inline int batch_splits(int n, int W)
     return n <= 2 * R ? 2 : n <= 4 * R ? 4 : n <= 8 * R ? 8 : 16;
 }
 
-template <int U>
-__global__ void __launch_bounds__(CMB_NT) combine_kernel(CombineArgs a)
+// Scalar arguments, 14 dwords: the build preloads the first 14 argument
+// dwords into scalar registers (a struct argument gets none), so no
+// argument is read from memory.  hdw packs Hq (bits 0-15), D / 32 (bits
+// 16-20) and the chunk width W / 32 (bits 26-28).
+template <int U, bool F16>
+__global__ void __launch_bounds__(CMB_NT)
+combine_kernel(const float* part_o, const float* part_lse, int hdw, int max_splits, int live_splits,
+               int split_tokens, const int32_t* seq_lens, void* out_p, float* lse_out)
 {
+    const int Hq = hdw & 0xFFFF, D = ((hdw >> 16) & 31) * 32, W = ((hdw >> 26) & 7) * 32;
     const int h = blockIdx.x, b = blockIdx.y;
-    const int W = a.D / (int)gridDim.z, c0 = blockIdx.z * W;
-    const int64_t bh = (int64_t)b * a.Hq + h;
+    const int c0 = blockIdx.z * W;
+    const int64_t bh = (int64_t)b * Hq + h;
     // the loads are issued before the sequence length arrives
     CombineSrc1 src;
-    src.rl = cmb_rsrc(a.part_lse + bh * a.max_splits, (int64_t)a.max_splits * 4);
-    src.ro = cmb_rsrc(a.part_o + bh * a.max_splits * a.D + c0, ((int64_t)a.max_splits * a.D - c0) * 4);
-    src.len = a.seq_lens + b;
-    src.split_tokens = a.split_tokens;
-    src.D = a.D;
-    src.n = a.live_splits;
+    src.rl = cmb_rsrc(part_lse + bh * max_splits, (int64_t)max_splits * 4);
+    src.ro = cmb_rsrc(part_o + bh * max_splits * D + c0, ((int64_t)max_splits * D - c0) * 4);
+    src.len = seq_lens + b;
+    src.split_tokens = split_tokens;
+    src.D = D;
+    src.n = live_splits;
     src.S = 0;
-    void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh * a.D + c0)
-                          : (void*)(reinterpret_cast<float*>(a.out) + bh * a.D + c0);
-    float* lse = a.lse_out && blockIdx.z == 0 ? a.lse_out + bh : nullptr;
-    // (the output pointers are read with the other arguments, not after the merge)
-    asm volatile("" ::"s"(out), "s"(lse));
+    void* out = F16 ? (void*)(reinterpret_cast<uint16_t*>(out_p) + bh * D + c0)
+                    : (void*)(reinterpret_cast<float*>(out_p) + bh * D + c0);
+    float* lse = lse_out && blockIdx.z == 0 ? lse_out + bh : nullptr;
     CombineState st = combine_init();
     combine_fold_src<U>(src, W, st);
-    combine_finish(st, W, a.out_f16, out, lse);
+    combine_finish(st, W, F16, out, lse);
 }
 
 // The splits of all regions of one (sequence, query head) as one list of
@@ -192,12 +197,24 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s)
 {
     const int W = chunk_cols(a.D, a.live_splits);
     const dim3 grid(a.Hq, a.B, a.D / W);
+    // (Hq <= 65535 and D <= 512, a multiple of 32, are validated by the caller)
+    const int hdw = a.Hq | ((a.D / 32) << 16) | ((W / 32) << 26);
+#define KVQ_CMB(UU, FF)                                                                                     \
+    hipLaunchKernelGGL((combine_kernel<UU, FF>), grid, dim3(CMB_NT), 0, s, a.part_o, a.part_lse, hdw,          \
+                       a.max_splits, a.live_splits, a.split_tokens, a.seq_lens, a.out, a.lse_out)
+#define KVQ_CMB2(UU)           \
+    if (a.out_f16)             \
+        KVQ_CMB(UU, true);     \
+    else                       \
+        KVQ_CMB(UU, false);
     switch (batch_splits(a.live_splits, W)) {
-    case 2: hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(CMB_NT), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(CMB_NT), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(CMB_NT), 0, s, a); break;
-    default: hipLaunchKernelGGL(combine_kernel<16>, grid, dim3(CMB_NT), 0, s, a); break;
+    case 2: KVQ_CMB2(2) break;
+    case 4: KVQ_CMB2(4) break;
+    case 8: KVQ_CMB2(8) break;
+    default: KVQ_CMB2(16) break;
     }
+#undef KVQ_CMB2
+#undef KVQ_CMB
     return hipGetLastError();
 }
 

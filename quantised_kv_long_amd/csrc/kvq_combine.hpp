@@ -173,17 +173,19 @@ __device__ __forceinline__ void combine_finish(const CombineState& st, int W, bo
     float4 a = st.a;
 #pragma unroll
     for (int k = 1; k < 32; k <<= 1) {
-        if (k >= R) break;                 // (uniform)
-        const float m2 = __shfl_xor(m, k);
-        const float l2 = __shfl_xor(l, k);
-        const float4 a2 = make_float4(__shfl_xor(a.x, k), __shfl_xor(a.y, k), __shfl_xor(a.z, k),
-                                      __shfl_xor(a.w, k));
-        const float M = fmaxf(m, m2);
-        const float f1 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m - M) * CMB_LOG2E);
-        const float f2 = m2 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m2 - M) * CMB_LOG2E);
-        l = f1 * l + f2 * l2;
-        a = make_float4(f1 * a.x + f2 * a2.x, f1 * a.y + f2 * a2.y, f1 * a.z + f2 * a2.z, f1 * a.w + f2 * a2.w);
-        m = M;
+        if (k < R) {                       // (uniform)
+            const float m2 = __shfl_xor(m, k);
+            const float l2 = __shfl_xor(l, k);
+            const float4 a2 = make_float4(__shfl_xor(a.x, k), __shfl_xor(a.y, k), __shfl_xor(a.z, k),
+                                          __shfl_xor(a.w, k));
+            const float M = fmaxf(m, m2);
+            const float f1 = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m - M) * CMB_LOG2E);
+            const float f2 = m2 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m2 - M) * CMB_LOG2E);
+            l = f1 * l + f2 * l2;
+            a = make_float4(f1 * a.x + f2 * a2.x, f1 * a.y + f2 * a2.y, f1 * a.z + f2 * a2.z,
+                            f1 * a.w + f2 * a2.w);
+            m = M;
+        }
     }
     if (r != 0) return;
     float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
