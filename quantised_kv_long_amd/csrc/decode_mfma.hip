@@ -280,8 +280,8 @@ __device__ __forceinline__ void write_block_lanes_d(const uint16_t* src, const P
 }
 
 template <int TK, int TV, int D, bool MQ, bool SHORT = false>
-__device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint8_t* const lds_a,
-                                          const size_t lds_cap, float* const lds_sx,
+__device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* const seq_lens, const int s,
+                                          uint8_t* const lds_a, const size_t lds_cap, float* const lds_sx,
                                           uint8_t* const lds_merge_dyn, float* const lds_new)
 {
     using C = Cfg<TK, TV, D>;
@@ -296,7 +296,13 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     // last NQ rows of the sequence are the query tokens: token i sees rows
     // [0, L - NQ + 1 + i)) and head h0 + c % G
     const int NQ = MQ ? a.nq : 1, NC = NQ * G;
-    const int L = a.seq_lens[b];
+    const int L = seq_lens[b];                      // (seq_lens == a.seq_lens)
+    // the plane arguments are read together with the length (pinned here, or
+    // the compiler loads them only after the test for an empty split below)
+    asm volatile("" ::"s"(a.k.data), "s"(a.v.data), "s"(a.k.scales), "s"(a.v.scales));
+    asm volatile("" ::"s"(a.k.seq_stride), "s"(a.k.head_stride), "s"(a.v.seq_stride), "s"(a.v.head_stride));
+    asm volatile("" ::"s"(a.q), "s"(a.k_new), "s"(a.part_o), "s"(a.part_lse));
+    asm volatile("" ::"s"(a.G), "s"(a.Hq), "s"(a.Hkv), "s"(a.max_splits));
     const int t_begin = s * a.split_tokens;
     const int t_end_all = min(t_begin + a.split_tokens, L);
     // Decode step with one new token (NEWROW, the base types): the workgroup
@@ -314,10 +320,6 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     float* pl = a.part_lse + ((int64_t)b * HQT + h0) * a.max_splits + s;
     // partial row of column c, relative to (b, h0)
     auto crow = [&](int c) -> int64_t { return MQ ? (int64_t)(c / G) * a.Hq + c % G : (int64_t)c; };
-
-    // a split at or past ceil(L / split_tokens) holds no row: the merge never
-    // reads its partials, so nothing is written
-    if (t_begin >= t_end_all) return;
 
     const int64_t krow0 = (int64_t)b * a.k.seq_stride + (int64_t)g * a.k.head_stride;
     const int64_t vrow0 = (int64_t)b * a.v.seq_stride + (int64_t)g * a.v.head_stride;
@@ -341,6 +343,10 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     const __amdgpu_buffer_rsrc_t rvs =
         make_rsrc(C::V_SCALE ? (const void*)(a.v.scales + vrow0 * C::NB_ROW * C::SPBV) : (const void*)a.v.data,
                   C::V_SCALE ? (int64_t)Lr * SRV : 0);
+    // a split at or past ceil(L / split_tokens) holds no row: the merge never
+    // reads its partials, so nothing is written.  (Tested after the resource
+    // set-up, so that the argument loads it needs go out with the length's.)
+    if (t_begin >= t_end_all) return;
 
     // ---- decode step with the new tokens: the workgroup whose split holds
     //      row L-1 (multi-query: each workgroup whose split holds some of the
@@ -1008,6 +1014,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
             }
         } else {
             // (head_dim 128) one block per half-wave: K for h < NB_ROW, else V
+            if (h >= 2 * C::NB_ROW) return;           // (uniform over the half-wave)
             uint32_t t = xnew[0];
             asm volatile("" : "+v"(t));
             const uint16_t xk = (uint16_t)t;
@@ -1266,16 +1273,19 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int s, uint
     }
 }
 
+// seq_lens is a.seq_lens passed again as the first argument: the build
+// preloads leading scalar arguments into registers (not struct ones), so
+// the sequence length's load does not wait for the argument buffer.
 template <int TK, int TV, int D, bool MQ, bool SHORT>
 __global__ void __launch_bounds__((Cfg<TK, TV, D>::NTH)) __attribute__((amdgpu_waves_per_eu(Cfg<TK, TV, D>::WPE)))
-decode_mfma_kernel(DecodeArgs a)
+decode_mfma_kernel(const int32_t* seq_lens, DecodeArgs a)
 {
     using C = Cfg<TK, TV, D>;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[C::WV * C::BUF];
     __shared__ __attribute__((aligned(16))) float lds_sx[C::SX_FLOATS];
     __shared__ __attribute__((aligned(16))) float lds_new[C::NEWROW && !MQ ? 2 * D + 64 : 1];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
-    decode_wg<TK, TV, D, MQ, SHORT>(a, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn, lds_new);
+    decode_wg<TK, TV, D, MQ, SHORT>(a, seq_lens, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn, lds_new);
 }
 
 // The two regions of a mixed cache in one launch (HAL #582 section 5 P2): the
@@ -1304,9 +1314,10 @@ decode_mfma_dual_kernel(DecodeArgs t, DecodeArgs w)
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
     const int ts = grid_splits(t);  // the first ts workgroups of each row take the tail
     if ((int)blockIdx.x < ts)
-        decode_wg<TK, TV, D, false>(t, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn, lds_new);
+        decode_wg<TK, TV, D, false>(t, t.seq_lens, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn,
+                                    lds_new);
     else
-        decode_wg<T_F16, T_F16, D, false>(w, blockIdx.x - ts, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn,
+        decode_wg<T_F16, T_F16, D, false>(w, w.seq_lens, blockIdx.x - ts, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn,
                                           lds_new);
 }
 
@@ -1343,7 +1354,8 @@ hipError_t launch5(const DecodeArgs& a, hipStream_t s)
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((decode_mfma_kernel<TK, TV, D, MQ, SHORT>), grid, dim3(Cfg<TK, TV, D>::NTH), dyn, s, a);
+    hipLaunchKernelGGL((decode_mfma_kernel<TK, TV, D, MQ, SHORT>), grid, dim3(Cfg<TK, TV, D>::NTH), dyn, s,
+                       a.seq_lens, a);
     return hipGetLastError();
 }
 
