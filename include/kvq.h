@@ -437,13 +437,13 @@ int kvq_combine_regions(int n_regions, const float* const* part_o, const float* 
  * out / lse_out agree within floating-point rounding.  Where the matrix-core
  * kernel covers the call (see KVQ_VARIANT_MFMA) the step is two kernel
  * launches: attention, then the merge.  The attention kernel's workgroup whose
- * split holds row seq_lens[b] - 1 writes that row; at head_dim 128 (types
- * f16, q8_0, q4_0) it takes the row's decoded values straight from its
- * quantiser as one more term of its split, with an fp32 weight where the
- * three calls round that row's weight to fp16 for the matrix cores (the two
- * differ by at most 2^-11 of the weight times the row's largest value); at
- * other head dims it reads the row back after writing it.  Other calls run
- * the three kernels in order.
+ * split holds row seq_lens[b] - 1 writes that row; for types f16, q8_0 and
+ * q4_0 it takes the row's decoded values straight from its quantiser as one
+ * more term of its split, with an fp32 weight where the three calls round
+ * that row's weight to fp16 for the matrix cores (the two differ by at most
+ * 2^-11 of the weight times the row's largest value); for the further types
+ * it reads the row back after writing it.  Other calls run the three kernels
+ * in order.
  *
  *   k_new, v_new : device, [B][Hkv][D] binary16: the new token's K and V rows.
  *   seq_lens     : device, [B] int32: lengths *including* the new token,
