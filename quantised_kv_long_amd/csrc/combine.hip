@@ -134,8 +134,18 @@ struct CombineSrcN {
 template <int U>
 __global__ void __launch_bounds__(CMB_NT) combine_regions_kernel(CombineRegionsArgs a)
 {
+    // every argument is read in one round (pinned here, or the compiler
+    // spreads the loads over several)
+    asm volatile("" ::"s"(a.part_o[0]), "s"(a.part_o[1]), "s"(a.part_o[2]), "s"(a.part_o[3]));
+    asm volatile("" ::"s"(a.part_lse[0]), "s"(a.part_lse[1]), "s"(a.part_lse[2]), "s"(a.part_lse[3]));
+    asm volatile("" ::"s"(a.seq_lens[0]), "s"(a.seq_lens[1]), "s"(a.seq_lens[2]), "s"(a.seq_lens[3]));
+    asm volatile("" ::"s"(a.live_splits[0]), "s"(a.live_splits[1]), "s"(a.live_splits[2]), "s"(a.live_splits[3]));
+    asm volatile("" ::"s"(a.max_splits[0]), "s"(a.max_splits[1]), "s"(a.max_splits[2]), "s"(a.max_splits[3]));
+    asm volatile("" ::"s"(a.split_tokens[0]), "s"(a.split_tokens[1]), "s"(a.split_tokens[2]),
+                 "s"(a.split_tokens[3]));
+    asm volatile("" ::"s"(a.Hq), "s"(a.D), "s"(a.W), "s"(a.n), "s"(a.out), "s"(a.lse_out));
     const int h = blockIdx.x, b = blockIdx.y;
-    const int W = a.D / (int)gridDim.z, c0 = blockIdx.z * W;
+    const int W = a.W, c0 = blockIdx.z * W;
     const int64_t bh = (int64_t)b * a.Hq + h;
     CombineSrcN src;
     src.nreg = a.n;
@@ -160,7 +170,6 @@ __global__ void __launch_bounds__(CMB_NT) combine_regions_kernel(CombineRegionsA
     void* out = a.out_f16 ? (void*)(reinterpret_cast<uint16_t*>(a.out) + bh * a.D + c0)
                           : (void*)(reinterpret_cast<float*>(a.out) + bh * a.D + c0);
     float* lse = a.lse_out && blockIdx.z == 0 ? a.lse_out + bh : nullptr;
-    asm volatile("" ::"s"(out), "s"(lse));
     CombineState st = combine_init();
     combine_fold_src<U>(src, W, st);
     combine_finish(st, W, a.out_f16, out, lse);
@@ -183,6 +192,7 @@ hipError_t launch_combine_regions(const CombineRegionsArgs& args, hipStream_t s)
     int n = 0;
     for (int i = 0; i < a.n; ++i) n += a.live_splits[i];
     const int W = chunk_cols(a.D, n);
+    a.W = W;
     const dim3 grid(a.Hq, a.B, a.D / W);
     switch (batch_splits(n, W)) {
     case 2: hipLaunchKernelGGL(combine_regions_kernel<2>, grid, dim3(CMB_NT), 0, s, a); break;

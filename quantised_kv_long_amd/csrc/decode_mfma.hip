@@ -1303,21 +1303,23 @@ struct DualCfg {
     static constexpr bool VALID = T::VALID && F::VALID;
 };
 
+// The leading scalar arguments (the regions' length pointers and the tail's
+// split count ts = grid_splits(t)) are preloaded into registers, so neither
+// the region test nor a length load waits for the argument structs.
 template <int TK, int TV, int D>
 __global__ void __launch_bounds__((Cfg<TK, TV, D>::NTH)) __attribute__((amdgpu_waves_per_eu(2)))
-decode_mfma_dual_kernel(DecodeArgs t, DecodeArgs w)
+decode_mfma_dual_kernel(const int32_t* t_lens, const int32_t* w_lens, int ts, DecodeArgs t, DecodeArgs w)
 {
     using DC = DualCfg<TK, TV, D>;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[DC::BUF];
     __shared__ __attribute__((aligned(16))) float lds_sx[DC::SX];
     __shared__ __attribute__((aligned(16))) float lds_new[DC::F::NEWROW || DC::T::NEWROW ? 2 * D + 64 : 1];
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
-    const int ts = grid_splits(t);  // the first ts workgroups of each row take the tail
+    // the first ts workgroups of each row take the tail
     if ((int)blockIdx.x < ts)
-        decode_wg<TK, TV, D, false>(t, t.seq_lens, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn,
-                                    lds_new);
+        decode_wg<TK, TV, D, false>(t, t_lens, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn, lds_new);
     else
-        decode_wg<T_F16, T_F16, D, false>(w, w.seq_lens, blockIdx.x - ts, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn,
+        decode_wg<T_F16, T_F16, D, false>(w, w_lens, blockIdx.x - ts, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn,
                                           lds_new);
 }
 
@@ -1474,7 +1476,8 @@ hipError_t launch_dual3(const DecodeArgs& t, const DecodeArgs& w, hipStream_t s)
             if (e != hipSuccess) return e;
         }
         dim3 grid(grid_splits(t) + grid_splits(w), t.Hkv, t.B);
-        hipLaunchKernelGGL((decode_mfma_dual_kernel<TK, TV, D>), grid, dim3(Cfg<TK, TV, D>::NTH), dyn, s, t, w);
+        hipLaunchKernelGGL((decode_mfma_dual_kernel<TK, TV, D>), grid, dim3(Cfg<TK, TV, D>::NTH), dyn, s,
+                           t.seq_lens, w.seq_lens, grid_splits(t), t, w);
         return hipGetLastError();
     }
 }

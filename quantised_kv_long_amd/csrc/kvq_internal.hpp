@@ -70,6 +70,7 @@ struct CombineRegionsArgs {
     // max_splits
     int live_splits[MAX_REGIONS];
     int B, Hq, D;
+    int W;             // merge chunk width (set by the launcher)
     bool out_f16;
     void* out;
     float* lse_out;
