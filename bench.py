@@ -711,9 +711,9 @@ def run_long_context(args, dev):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the decode path would shard by sequence or KV head with no exchange, or by "
-              "context with one all-gather of split partials; see the design notes).",
+              "context with one all-gather of split partials).",
               file=sys.stderr)
         sys.exit(2)
 

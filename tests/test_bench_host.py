@@ -1,5 +1,5 @@
 """bench.py's host logic on the CPU: every name it loads is bound somewhere
-(a call to a function that no longer exists would only show on the GPU machine),
+(a call to a function that no longer exists would otherwise only show on a GPU),
 its arguments parse, and a request for more than one GPU exits with status 2."""
 import ast
 import builtins
