@@ -103,12 +103,16 @@ __device__ __forceinline__ uint32_t cvt_pk_h(float lo, float hi)
     return __builtin_bit_cast(uint32_t, r);
 }
 
-// 8 nibbles of one dword as fp16 subnormals (value = nibble * 2^-24), element
-// order [nib0, nib4, nib1, nib5, nib2, nib6, nib3, nib7].
-__device__ __forceinline__ half8 q4_sub8(uint32_t w)
+// 8 nibbles of one dword as fp16 subnormals, element order [nib0, nib4, nib1,
+// nib5, nib2, nib6, nib3, nib7] (one AND per pair, one shift for all): the
+// even pairs as nibble * 2^-24, the odd pairs ([nib1, nib5], [nib3, nib7])
+// left in bits 4-7 of their halves, i.e. 16 * nibble * 2^-24 (still exact);
+// the other operand of the product holds those slots divided by 16.
+__device__ __forceinline__ half8 q4_sub8x(uint32_t w)
 {
-    const uint32_t M = 0x000F000Fu;
-    return make_half8(w & M, (w >> 4) & M, (w >> 8) & M, (w >> 12) & M);
+    const uint32_t M = 0x000F000Fu, M4 = 0x00F000F0u;
+    const uint32_t w8 = w >> 8;
+    return make_half8(w & M, w & M4, w8 & M, w8 & M4);
 }
 
 // 8 signed bytes (two dwords) as fp16 subnormals of (byte + 128) * 2^-24, in
@@ -445,6 +449,11 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
                 if (ln >= NC) w[c] = 0;
                 part = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, w[c]), one2, part, false);
             }
+            if constexpr (C::KNIB && C::KHB == 0) {
+                // (q4_sub8x codes: slots 2, 3, 6, 7 hold 16 * code)
+                w[1] = pk_mul_h(w[1], 0x2C002C00u);
+                w[3] = pk_mul_h(w[3], 0x2C002C00u);
+            }
             qop[kb] = make_half8(w[0], w[1], w[2], w[3]);
             // the accumulator's start removes the code offset exactly once
             const float qsum = xsum4(part);
@@ -740,7 +749,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
                         }
                         av = make_half8(d[0], d[1], d[2], d[3]);
                     } else if constexpr (C::KNIB) {
-                        av = q4_sub8(q[0]);
+                        av = q4_sub8x(q[0]);
                     } else if constexpr (TK == T_Q8) {
                         av = q8_sub8(q[0], q[1]);
                     } else {
@@ -849,15 +858,20 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
 #pragma unroll
         for (int k = 0; k < 4; ++k) pp[k] = cvt_pk_h(p[2 * k], p[2 * k + 1]);
 
+        // (q4_0 V with q4_sub8x codes: slots 2, 3, 6, 7 of P' divided by 16,
+        // and their code offset 16 times as large)
+        constexpr bool VN16 = TV == T_Q4;
+        const uint32_t pq1 = VN16 ? pk_mul_h(pp[1], 0x2C002C00u) : pp[1];
+        const uint32_t pq3 = VN16 ? pk_mul_h(pp[3], 0x2C002C00u) : pp[3];
         // P' for block kb: p times the V scale of each of this lane row's
         // rows 8*lq + e (eight contiguous fp16 values of the transposed tile)
         auto pscaled = [&](int kb) -> half8 {
             const u32x4 sv4 = *reinterpret_cast<const u32x4*>(vst + (kb * C::SPBV) * TT + 8 * lq);
-            return make_half8(pk_mul_h(pp[0], sv4[0]), pk_mul_h(pp[1], sv4[1]),
-                              pk_mul_h(pp[2], sv4[2]), pk_mul_h(pp[3], sv4[3]));
+            return make_half8(pk_mul_h(pp[0], sv4[0]), pk_mul_h(pq1, sv4[1]),
+                              pk_mul_h(pp[2], sv4[2]), pk_mul_h(pq3, sv4[3]));
         };
-        const half8 voff = __builtin_bit_cast(half8, u32x4{C::VOFF_BITS, C::VOFF_BITS, C::VOFF_BITS,
-                                                           C::VOFF_BITS});
+        constexpr uint32_t VOFF_ODD = VN16 ? 0x00800080u : C::VOFF_BITS;
+        const half8 voff = __builtin_bit_cast(half8, u32x4{C::VOFF_BITS, VOFF_ODD, C::VOFF_BITS, VOFF_ODD});
 
         // -- PV: O^T tile t (16 value columns) += V^T(16 x 32 rows) * P'^T
         const LDS_AS uint8_t* vl = (const LDS_AS uint8_t*)vb;
@@ -874,10 +888,10 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
             for (int c2 = 0; c2 < C::NB; ++c2) {
                 const int2v w = __builtin_amdgcn_ds_read_tr4_b64_v2i32((LDS_AS int2v*)(tbase + 16 * c2));
                 const half8 bv = pscaled(c2);
-                oacc[2 * c2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(q4_sub8((uint32_t)w[0]), bv,
-                                                                     oacc[2 * c2], 0, 0, 0);
-                oacc[2 * c2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(q4_sub8((uint32_t)w[1]), bv,
-                                                                         oacc[2 * c2 + 1], 0, 0, 0);
+                const half8 a0 = q4_sub8x((uint32_t)w[0]);
+                const half8 a1 = q4_sub8x((uint32_t)w[1]);
+                oacc[2 * c2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bv, oacc[2 * c2], 0, 0, 0);
+                oacc[2 * c2 + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bv, oacc[2 * c2 + 1], 0, 0, 0);
                 bacc[c2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(voff, bv, bacc[c2], 0, 0, 0);
             }
         } else if constexpr (TV == T_Q8 || C::VBYTES) {
@@ -1042,7 +1056,9 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
                 const uint32_t w2 = (uint32_t)qu[e >> 1];
                 const half2v h2 = __builtin_bit_cast(half2v, w2);
                 const int kel = C::KNIB ? 4 * lq + ((e & 1) ? 2 : 0) + ((e & 2) ? 16 : 0) + (e >> 2) : 8 * lq + e;
-                acc = fmaf((float)h2[e & 1], lds_new[wsl * C::DW + 32 * kb + kel], acc);
+                // (slots 2, 3, 6, 7 of a q4_sub8x operand hold q / 16)
+                const float qe = (float)h2[e & 1] * (C::KNIB && C::KHB == 0 && (e & 2) ? 16.0f : 1.0f);
+                acc = fmaf(qe, lds_new[wsl * C::DW + 32 * kb + kel], acc);
             }
         }
         return xsum4(acc);
