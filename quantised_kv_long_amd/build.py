@@ -54,6 +54,8 @@ def sources() -> list[str]:
 
 PROBE_SRC = os.path.join(PKG, "probe", "stream_read.hip")
 PROBE_LIB = os.path.join(PKG, "libkvq_probe.so")
+TIMELINE_SRC = os.path.join(PKG, "probe", "timeline.hip")
+TIMELINE_LIB = os.path.join(PKG, "libkvq_timeline.so")
 
 
 def _hipcc(srcs: list[str], out: str, extra: list[str] | None, verbose: bool) -> str:
@@ -81,6 +83,15 @@ def build_probe(out: str = PROBE_LIB, verbose: bool = False) -> str:
     return _hipcc([PROBE_SRC], out, None, verbose)
 
 
+def build_timeline(out: str = TIMELINE_LIB, verbose: bool = False) -> str:
+    """The library again, with the attention kernel's per-workgroup timeline
+    (probe/timeline.hip compiles csrc/decode_mfma.hip with the timeline points
+    defined; not part of the decode path)."""
+    srcs = [TIMELINE_SRC if os.path.basename(f) == "decode_mfma.hip" else f for f in sources()]
+    return _hipcc(srcs, out, None, verbose)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_probe(verbose=True))
+    print(build_timeline(verbose=True))

@@ -68,6 +68,13 @@ constexpr int VMCNT0 = 0x0F70;         // s_waitcnt vmcnt(0) (expcnt, lgkmcnt un
 // register sets of the quantised head_dim-128 ring, of the head_dim 256/512
 // ring (quantised rows; fp16 rows), and the waves per SIMD a head_dim 256/512
 // instance is built for (1 lets it use up to 512 registers).
+// Per-workgroup timeline points: empty in the library.  The timeline probe
+// build defines KVQ_TL to record the workgroup's clock at its start (0), after
+// wave 0's last tile (1), at its end (2) and, in the four-wave merge, once
+// every wave's loop is done (3) and once the merge area is written (4).
+#ifndef KVQ_TL
+#define KVQ_TL(point)
+#endif
 #ifndef KVQ_RING
 #define KVQ_RING 2
 #endif
@@ -264,11 +271,11 @@ __host__ __device__ constexpr size_t merge_lds_bytes(int nc)
 // Every instance is built for two waves per SIMD (at most 256 registers):
 // each wave holds a 128-column slice of the head dimension.
 // The work of one workgroup: split s of (sequence blockIdx.z, KV head
-// blockIdx.y).  LDS: lds_a, lds_cap bytes (at least WAVES * BUF: one buffer
-// per wave, the V rows of the current tile, then the K and V scale tiles
-// transposed to [block][row]; also the merge area when that fits), lds_sx
-// (the partial-score exchange of a 512-wide head) and lds_merge_dyn (the
-// merge area otherwise).
+// blockIdx.y).  LDS: lds_a (WAVES * BUF bytes: one buffer per wave, the V
+// rows of the current tile, then the K and V scale tiles transposed to
+// [block][row]), lds_sx (the partial-score exchange of a 512-wide head) and
+// lds_merge (the four-wave merge area of whole rows, merge_lds_bytes: its
+// own memory, so a wave writes its part as soon as its last tile is done).
 // MQ: several query tokens per sequence (a.nq > 1); a separate instance, so
 // that the single-token kernels carry none of its per-column index arithmetic
 // One 32-value block of a new row, quantised by the 32 lanes of an aligned
@@ -285,8 +292,8 @@ __device__ __forceinline__ void write_block_lanes_d(const uint16_t* src, const P
 
 template <int TK, int TV, int D, bool MQ, bool SHORT = false>
 __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* const seq_lens, const int s,
-                                          uint8_t* const lds_a, const size_t lds_cap, float* const lds_sx,
-                                          uint8_t* const lds_merge_dyn, float* const lds_new)
+                                          uint8_t* const lds_a, float* const lds_sx, uint8_t* const lds_merge,
+                                          float* const lds_new)
 {
     using C = Cfg<TK, TV, D>;
     const int g = blockIdx.y, b = blockIdx.z;
@@ -1137,6 +1144,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
         }
     }
 
+    KVQ_TL(1);
     if constexpr (C::DS > 1) {
         // every wave holds the same (m, l) and its own slice of O: write it
         const float l_head = xsum4(l_part);
@@ -1198,14 +1206,15 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
     }
 
     // ---- merge the four waves: (m, l, O) per head through LDS.  Each lane
-    //      stores its raw accumulators; after one barrier every thread of the
-    //      output loop forms its head's four wave weights itself (and the V
-    //      code-offset correction of its block), so each output column is a
-    //      four-term weighted sum with no second barrier.
+    //      stores its raw accumulators in the merge area (no other wave reads
+    //      or writes it before the barrier); after the one barrier every
+    //      thread of the output loop forms its head's four wave weights
+    //      itself (and the V code-offset correction of its block), so each
+    //      output column is a four-term weighted sum.
     const float l_head = xsum4(l_part);
     (void)m_new;
-    __syncthreads();
-    uint8_t* marea = merge_lds_bytes<TK, TV, D>(NC) <= lds_cap ? lds_a : lds_merge_dyn;
+    KVQ_TL(3);
+    uint8_t* marea = lds_merge;
     float* mw = reinterpret_cast<float*>(marea);          // [WAVES][16]   running max
     float* lw = mw + WAVES * 16;                          // [WAVES][16]   running sum
     float* bw = lw + WAVES * 16;                          // [WAVES][16][NB] V offset sums
@@ -1237,6 +1246,11 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
             }
     }
     __syncthreads();
+    KVQ_TL(4);
+    // (the weights, their sum's reciprocal and the log use the hardware
+    // exp2 / rcp / log2, about 1 ulp each: this is the tail of every
+    // workgroup, where the library's exact sequences cost more than the
+    // rounding they save)
     for (int idx = tid; idx < NC * (D / 4); idx += C::NTH) {
         const int n = idx / (D / 4), c4 = idx % (D / 4);
         float M = -INFINITY;
@@ -1248,14 +1262,16 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
         float f[WAVES], lsum = 0.0f;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
-            f[w] = exp2f(mw[w * 16 + n] - M);     // 0 for waves that saw no row (m at the floor)
+            // 0 for waves that saw no row (m at -inf or at the floor)
+            f[w] = __builtin_amdgcn_exp2f(mw[w * 16 + n] - M);
             lsum += f[w] * lw[w * 16 + n];
         }
-        const float f_new = NEWROW_OK && newrow ? exp2f(m_new - M) : 0.0f;
+        const float f_new = NEWROW_OK && newrow ? __builtin_amdgcn_exp2f(m_new - M) : 0.0f;
         lsum += f_new;
-        // quantised V: O = (acc - offset sum) * 2^24 (no row at all: o = 0,
-        // lse = -inf)
-        const float inv = lsum > 0.0f ? (C::V_SCALE ? TWO24 : 1.0f) / lsum : 0.0f;
+        // quantised V: O = (acc - offset sum) * 2^24 (a column that sees no
+        // row of the split: o = 0, lse = -inf)
+        const float rl = lsum > 0.0f ? __builtin_amdgcn_rcpf(lsum) : 0.0f;
+        const float inv = (C::V_SCALE ? TWO24 : 1.0f) * rl;
         float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         float c = 0.0f;
 #pragma unroll
@@ -1276,7 +1292,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
         }
         if constexpr (NEWROW_OK) {
             if (newrow) {
-                const float fn = f_new / lsum;
+                const float fn = f_new * rl;
                 const float4 v = reinterpret_cast<const float4*>(lds_new + D)[c4];
                 o.x = fmaf(fn, v.x, o.x);
                 o.y = fmaf(fn, v.y, o.y);
@@ -1285,7 +1301,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
             }
         }
         reinterpret_cast<float4*>(po + crow(n) * ho_stride)[c4] = o;
-        if (c4 == 0) pl[crow(n) * a.max_splits] = (M + log2f(lsum)) * 0.69314718055994531f;
+        if (c4 == 0) pl[crow(n) * a.max_splits] = (M + __builtin_amdgcn_logf(lsum)) * 0.69314718055994531f;
     }
 }
 
@@ -1300,8 +1316,10 @@ decode_mfma_kernel(const int32_t* seq_lens, DecodeArgs a)
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[C::WV * C::BUF];
     __shared__ __attribute__((aligned(16))) float lds_sx[C::SX_FLOATS];
     __shared__ __attribute__((aligned(16))) float lds_new[C::NEWROW && !MQ ? 2 * D + 64 : 1];
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
-    decode_wg<TK, TV, D, MQ, SHORT>(a, seq_lens, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn, lds_new);
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge[];   // merge_lds_bytes(nc)
+    KVQ_TL(0);
+    decode_wg<TK, TV, D, MQ, SHORT>(a, seq_lens, blockIdx.x, lds_a, lds_sx, lds_merge, lds_new);
+    KVQ_TL(2);
 }
 
 // The two regions of a mixed cache in one launch (HAL #582 section 5 P2): the
@@ -1330,26 +1348,22 @@ decode_mfma_dual_kernel(const int32_t* t_lens, const int32_t* w_lens, int ts, De
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[DC::BUF];
     __shared__ __attribute__((aligned(16))) float lds_sx[DC::SX];
     __shared__ __attribute__((aligned(16))) float lds_new[DC::F::NEWROW || DC::T::NEWROW ? 2 * D + 64 : 1];
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge_dyn[];
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_merge[];   // dual_dyn_bytes(G)
     // the first ts workgroups of each row take the tail
     if ((int)blockIdx.x < ts)
-        decode_wg<TK, TV, D, false>(t, t_lens, blockIdx.x, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn, lds_new);
+        decode_wg<TK, TV, D, false>(t, t_lens, blockIdx.x, lds_a, lds_sx, lds_merge, lds_new);
     else
-        decode_wg<T_F16, T_F16, D, false>(w, w_lens, blockIdx.x - ts, lds_a, sizeof(lds_a), lds_sx, lds_merge_dyn,
-                                          lds_new);
+        decode_wg<T_F16, T_F16, D, false>(w, w_lens, blockIdx.x - ts, lds_a, lds_sx, lds_merge, lds_new);
 }
 
 template <int TK, int TV, int D>
 constexpr bool cfg_valid() { return Cfg<TK, TV, D>::VALID; }
 
-// Dynamic LDS of a launch: the merge area, when it does not fit in the
-// static stage array.
+// Dynamic LDS of a launch: the merge area (none for heads wider than 128).
 template <int TK, int TV, int D>
 size_t dyn_lds_bytes(int nc)
 {
-    using C = Cfg<TK, TV, D>;
-    const size_t merge = merge_lds_bytes<TK, TV, D>(nc);
-    return merge <= (size_t)C::WV * C::BUF ? 0 : merge;
+    return merge_lds_bytes<TK, TV, D>(nc);
 }
 
 template <int TK, int TV, int D>
@@ -1459,10 +1473,8 @@ hipError_t new_launch(const DecodeArgs& a, hipStream_t s)
 template <int TK, int TV, int D>
 size_t dual_dyn_bytes(int G)
 {
-    using DC = DualCfg<TK, TV, D>;
     const size_t mt = merge_lds_bytes<TK, TV, D>(G), mf = merge_lds_bytes<T_F16, T_F16, D>(G);
-    const size_t m = mt > mf ? mt : mf;
-    return m <= (size_t)DC::BUF ? 0 : m;
+    return mt > mf ? mt : mf;
 }
 
 template <int TK, int TV, int D>
