@@ -1160,16 +1160,18 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
                 vmin[kb] = __shfl(x, ln) * TWOM24;
             }
         }
-        // (the new row's term: max m_new, sum 1, row v)
+        // (the new row's term: max m_new, sum 1, row v; hardware exp2, rcp
+        // and log2, about 1 ulp each, as in the four-wave merge below)
         if (ln < NC) {
             // (a column that saw no row: l = 0, o = 0, lse = -inf)
             const bool nr = NEWROW_OK && newrow;
             const float M = nr ? fmaxf(m_ref, m_new) : m_ref;
-            const float al = nr ? exp2f(m_ref - M) : 1.0f;
-            const float be = nr ? exp2f(m_new - M) : 0.0f;
+            const float al = nr ? __builtin_amdgcn_exp2f(m_ref - M) : 1.0f;
+            const float be = nr ? __builtin_amdgcn_exp2f(m_new - M) : 0.0f;
             const float lt = al * l_head + be;
-            const float inv = lt > 0.0f ? al * (C::V_SCALE ? TWO24 : 1.0f) / lt : 0.0f;
-            const float fn = nr ? be / lt : 0.0f;
+            const float rl = lt > 0.0f ? __builtin_amdgcn_rcpf(lt) : 0.0f;
+            const float inv = al * (C::V_SCALE ? TWO24 : 1.0f) * rl;
+            const float fn = be * rl;
             const float* vnew = lds_new + D + wsl * C::DW;
             float* prow = po + crow(ln) * ho_stride + wsl * C::DW;
 #pragma unroll
@@ -1200,7 +1202,8 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
                     *reinterpret_cast<float4*>(prow + 16 * t + 4 * lq) = make_float4(o[0], o[1], o[2], o[3]);
                 }
             }
-            if (wave == 0 && lq == 0) pl[crow(ln) * a.max_splits] = (M + log2f(lt)) * 0.69314718055994531f;
+            if (wave == 0 && lq == 0)
+                pl[crow(ln) * a.max_splits] = (M + __builtin_amdgcn_logf(lt)) * 0.69314718055994531f;
         }
         return;
     }
