@@ -81,7 +81,7 @@ def traffic_record(workload: str, tk: str, tv: str):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="stack48_d128_ctx64k")
     p.add_argument("--arms", default=None, help="comma list like q8_0/q4_0,f16/f16 (default: all)")
