@@ -207,7 +207,12 @@ struct Cfg {
     // as one unsigned code byte per value and take the byte route of PV
     static constexpr bool VBYTES = TV == T_Q4_1 || TV == T_Q5_0 || TV == T_Q5_1 || TV == T_Q6_0;
     static constexpr bool NEWT = VBYTES || TK == T_Q4_1 || TK == T_Q5_0 || TK == T_Q5_1 || TK == T_Q6_0;
-    static constexpr int RBV_LDS = VBYTES ? DW : RBV;                  // LDS bytes of a V row (slice)
+    // LDS row stride of a staged V row (slice): its bytes plus 16, so that
+    // the rows one transposed read gathers (16 rows, 16 bytes each for the
+    // 4- and 8-bit codes) fall in different banks; unpadded, rows 64, 128 or
+    // 256 bytes apart share banks and the reads conflict 4- to 8-fold
+    static constexpr int RBV_LDS = (VBYTES ? DW : RBV) + 16;
+    static constexpr int VCH = RBV / 16;                               // 16-byte chunks of a V row (slice)
     static constexpr int KU = KNIB ? 1 : (TK == T_Q8 ? 2 : 4);         // dwords per lane per block
     static constexpr int KDW = 4 * KU * NBG;                           // K code dwords per lane per subtile
     static constexpr int KHW = KHB * NB;                               // K high-bit dwords of a row (slice)
@@ -219,7 +224,7 @@ struct Cfg {
     static constexpr int VSL = VBYTES ? DW / 2 : RBV;                 // the same for V
     static constexpr int BBK = KNIB ? 16 : RBK / NB;                   // code bytes of a block (K row)
     static constexpr int V_BYTES = TT * RBV_LDS;                       // V tile bytes in LDS (slice)
-    static constexpr int V_LOADS = VBYTES ? 0 : V_BYTES / 1024;        // 16-byte loads per lane
+    static constexpr int V_LOADS = VBYTES ? 0 : TT * RBV / 1024;       // 16-byte loads per lane
     // byte route: one (row, block) unit per lane and load: 16 nibble bytes
     // plus the block's high-bit words
     static constexpr int V_UNITS = VBYTES ? TT * NB / 64 : 0;
@@ -252,7 +257,8 @@ struct Cfg {
     // aligned half-wave quantises NEW_IT of the row's 2 * NB_ROW blocks)
     static constexpr bool NEWROW = !NEWT;
     static constexpr int NEW_IT = (2 * NB_ROW * 32 + NTH - 1) / NTH;   // new-row blocks per half-wave
-    static constexpr bool VALID = V_BYTES % 1024 == 0 && SK_BYTES % 256 == 0 && SV_BYTES % 256 == 0 &&
+    static constexpr bool VALID = (VBYTES || ((TT * RBV) % 1024 == 0 && 64 % VCH == 0)) && SK_BYTES % 256 == 0 &&
+                                  SV_BYTES % 256 == 0 &&
                                   (!VBYTES || (TT * NB) % 64 == 0) && V_DW <= (DW == 128 ? 32 : 64) &&
                                   WV * BUF <= 64 * 1024;
 };
@@ -685,10 +691,13 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
                 *reinterpret_cast<u32x4*>(dst + 16) = u32x4{o[4], o[5], o[6], o[7]};
             }
         } else {
+            // chunk k*64 + lane of the tile is row (k*64 + lane) / VCH, chunk
+            // (k*64 + lane) % VCH (VCH divides 64)
+            uint8_t* const vrow = vb + (lane / C::VCH) * C::RBV_LDS + 16 * (lane % C::VCH);
 #pragma unroll
             for (int k = 0; k < C::V_LOADS; ++k) {
                 const u32x4 v = {vr[4 * k], vr[4 * k + 1], vr[4 * k + 2], vr[4 * k + 3]};
-                *reinterpret_cast<u32x4*>(vb + 1024 * k + 16 * lane) = v;
+                *reinterpret_cast<u32x4*>(vrow + k * (64 / C::VCH) * C::RBV_LDS) = v;
             }
         }
         if constexpr (C::K_SCALE)
@@ -890,7 +899,7 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
             const int r = ln;
             const int rr = r & 7;
             const int trow = 8 * lq + ((rr < 4) ? 2 * rr : 2 * (rr - 4) + 1);
-            const LDS_AS uint8_t* tbase = vl + trow * C::RBV + 8 * (r >> 3);
+            const LDS_AS uint8_t* tbase = vl + trow * C::RBV_LDS + 8 * (r >> 3);
 #pragma unroll
             for (int c2 = 0; c2 < C::NB; ++c2) {
                 const int2v w = __builtin_amdgcn_ds_read_tr4_b64_v2i32((LDS_AS int2v*)(tbase + 16 * c2));
@@ -937,14 +946,14 @@ __device__ __forceinline__ void decode_wg(const DecodeArgs& a, const int32_t* co
             // rows; lane r addresses row 8*lq + 4*R + r/4, chunk 4t + (r&3)
             const int r = ln;
             const half8 bv = make_half8(pp[0], pp[1], pp[2], pp[3]);
-            const LDS_AS uint8_t* tbase = vl + (8 * lq + (r >> 2)) * C::RBV + 8 * (r & 3);
+            const LDS_AS uint8_t* tbase = vl + (8 * lq + (r >> 2)) * C::RBV_LDS + 8 * (r & 3);
 #pragma unroll
             for (int t = 0; t < C::NDT; ++t) {
                 uint32_t d[4];
 #pragma unroll
                 for (int R = 0; R < 2; ++R) {
                     const short4v w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (LDS_AS short4v*)(tbase + 4 * R * C::RBV + 32 * t));
+                        (LDS_AS short4v*)(tbase + 4 * R * C::RBV_LDS + 32 * t));
                     const u32x2 u = __builtin_bit_cast(u32x2, w);
                     d[2 * R] = u[0];
                     d[2 * R + 1] = u[1];
