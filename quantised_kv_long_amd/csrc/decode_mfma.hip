@@ -64,10 +64,6 @@ constexpr float TAU = 8.0f;            // lazy rescale threshold, log2 units
 constexpr float TWO24 = 16777216.0f;   // 2^24
 constexpr float TWOM24 = 1.0f / 16777216.0f;
 constexpr int VMCNT0 = 0x0F70;         // s_waitcnt vmcnt(0) (expcnt, lgkmcnt unconstrained)
-// Build-time knobs of the load ring (the defaults are the measured best):
-// register sets of the quantised head_dim-128 ring, of the head_dim 256/512
-// ring (quantised rows; fp16 rows), and the waves per SIMD a head_dim 256/512
-// instance is built for (1 lets it use up to 512 registers).
 // Per-workgroup timeline points: empty in the library.  The timeline probe
 // build defines KVQ_TL to record the workgroup's clock at its start (0), after
 // wave 0's last tile (1), at its end (2) and, in the four-wave merge, once
@@ -75,6 +71,10 @@ constexpr int VMCNT0 = 0x0F70;         // s_waitcnt vmcnt(0) (expcnt, lgkmcnt un
 #ifndef KVQ_TL
 #define KVQ_TL(point)
 #endif
+// Build-time knobs of the load ring (the defaults are the measured best):
+// register sets of the quantised head_dim-128 ring, of the head_dim 256/512
+// ring (quantised rows; fp16 rows), and the waves per SIMD a head_dim 256/512
+// instance is built for (1 lets it use up to 512 registers).
 #ifndef KVQ_RING
 #define KVQ_RING 2
 #endif
