@@ -140,7 +140,7 @@ WORKLOADS = {
         "16 sequences, ctx uniform in [16384, 131072], 40 query / 8 KV heads, head_dim 128; "
         "N(0,1)",
         layers=1, B=16, Hq=40, Hkv=8, D=128, ctx=131072, arms=[("q4_0", "q4_0"), ("q8_0", "q4_0")],
-        seed=1005, split_tokens=1024, ragged=(16384, 131072)),
+        seed=1005, split_tokens=2048, ragged=(16384, 131072)),
     "batch16_ragged_d512": Workload(
         "batch16_ragged_d512",
         "16 sequences, ctx uniform in [16384, 131072], 16 query / 2 KV heads, head_dim 512; N(0,1)",
