@@ -9,7 +9,10 @@
 // columns), each folding its splits in batches of 2 to 16 loads; every chunk reads all
 // the lse values and writes its own columns (the first chunk also writes the
 // LSE).  The splits loaded are those that can hold rows given the launch
-// arguments (live_splits), so the loads do not wait for the sequence lengths.
+// arguments (live_splits), so the loads do not wait for the sequence lengths;
+// with several sequences (LEN_FIRST) the length is read first instead and
+// the loads are range-checked to the sequence's own splits, so a short
+// sequence's dead splits cost no memory traffic.
 #include "kvq_combine.hpp"
 #include "kvq_internal.hpp"
 
@@ -45,7 +48,7 @@ inline int batch_splits(int n, int W)
 // dwords into scalar registers (a struct argument gets none), so no
 // argument is read from memory.  hdw packs Hq (bits 0-15), D / 32 (bits
 // 16-20) and the chunk width W / 32 (bits 26-28).
-template <int U, bool F16>
+template <int U, bool F16, bool LEN_FIRST>
 __global__ void __launch_bounds__(CMB_NT)
 combine_kernel(const float* part_o, const float* part_lse, int hdw, int max_splits, int live_splits,
                int split_tokens, const int32_t* seq_lens, void* out_p, float* lse_out)
@@ -54,15 +57,23 @@ combine_kernel(const float* part_o, const float* part_lse, int hdw, int max_spli
     const int h = blockIdx.x, b = blockIdx.y;
     const int c0 = blockIdx.z * W;
     const int64_t bh = (int64_t)b * Hq + h;
-    // the loads are issued before the sequence length arrives
     CombineSrc1 src;
-    src.rl = cmb_rsrc(part_lse + bh * max_splits, (int64_t)max_splits * 4);
-    src.ro = cmb_rsrc(part_o + bh * max_splits * D + c0, ((int64_t)max_splits * D - c0) * 4);
     src.len = seq_lens + b;
     src.split_tokens = split_tokens;
     src.D = D;
     src.n = live_splits;
     src.S = 0;
+    // the splits a load may touch: all that can hold rows (the loads are
+    // issued before the sequence length arrives), or with LEN_FIRST those of
+    // this sequence (past them a load reads zero and touches no memory)
+    int nr = max_splits;
+    if constexpr (LEN_FIRST) {
+        src.settle();
+        nr = src.S;
+    }
+    src.rl = cmb_rsrc(part_lse + bh * max_splits, (int64_t)nr * 4);
+    const int64_t ro_floats = (int64_t)nr * D - c0;
+    src.ro = cmb_rsrc(part_o + bh * max_splits * D + c0, (ro_floats > 0 ? ro_floats : 0) * 4);
     void* out = F16 ? (void*)(reinterpret_cast<uint16_t*>(out_p) + bh * D + c0)
                     : (void*)(reinterpret_cast<float*>(out_p) + bh * D + c0);
     float* lse = lse_out && blockIdx.z == 0 ? lse_out + bh : nullptr;
@@ -209,14 +220,24 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s)
     const dim3 grid(a.Hq, a.B, a.D / W);
     // (Hq <= 65535 and D <= 512, a multiple of 32, are validated by the caller)
     const int hdw = a.Hq | ((a.D / 32) << 16) | ((W / 32) << 26);
-#define KVQ_CMB(UU, FF)                                                                                     \
-    hipLaunchKernelGGL((combine_kernel<UU, FF>), grid, dim3(CMB_NT), 0, s, a.part_o, a.part_lse, hdw,          \
+    // one sequence: its length is the largest, every split up to live_splits
+    // holds rows and the loads need not wait for it; several: the length
+    // first, so that the dead splits of the shorter ones are not read
+#define KVQ_CMB(UU, FF, LL)                                                                                 \
+    hipLaunchKernelGGL((combine_kernel<UU, FF, LL>), grid, dim3(CMB_NT), 0, s, a.part_o, a.part_lse, hdw,      \
                        a.max_splits, a.live_splits, a.split_tokens, a.seq_lens, a.out, a.lse_out)
-#define KVQ_CMB2(UU)           \
-    if (a.out_f16)             \
-        KVQ_CMB(UU, true);     \
-    else                       \
-        KVQ_CMB(UU, false);
+#define KVQ_CMB2(UU)                  \
+    if (a.out_f16) {                  \
+        if (a.B > 1)                  \
+            KVQ_CMB(UU, true, true);  \
+        else                          \
+            KVQ_CMB(UU, true, false); \
+    } else {                          \
+        if (a.B > 1)                  \
+            KVQ_CMB(UU, false, true); \
+        else                          \
+            KVQ_CMB(UU, false, false);\
+    }
     switch (batch_splits(a.live_splits, W)) {
     case 2: KVQ_CMB2(2) break;
     case 4: KVQ_CMB2(4) break;
