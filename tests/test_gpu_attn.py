@@ -163,6 +163,42 @@ def test_combine_alone_on_oracle_partials(D, S):
         assert np.allclose(lse.cpu().numpy(), ref_lse, atol=1e-5)
 
 
+@pytest.mark.parametrize("B", [1, 3])
+def test_combine_ignores_dead_splits(B):
+    """Splits at or past a sequence's ceil(L / split_tokens) carry no weight
+    whatever their memory holds: they are filled with NaN rows and an lse
+    that would dominate every live one (one sequence: the merge loads them
+    and masks them; several: it reads the lengths first and does not load
+    them)."""
+    note(f"combine dead splits B={B}")
+    rng = np.random.default_rng(11 + B)
+    Hq, D, S, st = 5, 128, 40, 64
+    lens = [1000] if B == 1 else [1, 1000, 64 * 17 + 5]
+    po = rng.standard_normal((B, Hq, S, D))
+    pl = rng.standard_normal((B, Hq, S)) * 5
+    live = po.copy(), pl.copy()
+    for b in range(B):
+        nb = -(-lens[b] // st)
+        live[1][b, :, nb:] = -np.inf
+        live[0][b, :, nb:] = 0
+        po[b, :, nb:] = np.nan
+        pl[b, :, nb:] = 50.0
+    ref, ref_lse = O.combine(*live)
+    # max_seq_len of the partials: every split of the buffer may be loaded
+    part = C.Partials(B, Hq, D, S * st, st)
+    part.o.copy_(torch.from_numpy(po.astype(np.float32)))
+    part.lse.copy_(torch.from_numpy(pl.astype(np.float32)))
+    lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    C.combine(part, lt, out, lse)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    assert np.allclose(got, ref, atol=1e-5, rtol=1e-5)
+    assert np.allclose(lse.cpu().numpy(), ref_lse, atol=1e-5)
+
+
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_split_count_invariance_and_determinism(variant):
     dev = "cuda"
