@@ -182,3 +182,40 @@ def test_multi_full_size_64k_three_tokens(tk, tv):
                                     sub(planes_to_oracle(vc)), [L - nq + 1 + i], 1, 1 / math.sqrt(D),
                                     nthreads=oracle_threads())
             assert_close(out[:, i, h:h + 1], lse[:, i, h:h + 1], ref, ref_lse, f"token {i} head {h}")
+
+
+@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0")])
+def test_step_multi_full_size_64k_three_tokens(tk, tv):
+    """A layer of the 64k workload with three query tokens, in the launch
+    configuration of the benchmark (kvq_decode_step_multi, 1024-row splits):
+    the step writes the three new rows and attends; sampled query heads of
+    every token against the oracle over the same rows (its own bytes)."""
+    wl = synth.WORKLOADS["stack48_d128_ctx64k"]
+    B, Hkv, D, G, L, st, nq = wl.B, wl.Hkv, wl.D, wl.G, wl.ctx, wl.split_tokens, 3
+    dev = "cuda"
+    note(f"step_multi full size {tk}/{tv}")
+    # rows L - 3 .. L - 1 are the new tokens: the oracle's planes hold its own
+    # quantisation of them, the step writes them from k_new / v_new
+    k = synth.normal_f16((B, Hkv, L, D), 4201, dev)
+    v = synth.normal_f16((B, Hkv, L, D), 4202, dev)
+    kc, vc = fill_pair(tk, tv, k, v)
+    q = synth.normal_f16((B, nq, wl.Hq, D), 4203, dev)
+    k_new = k[:, :, L - nq:].transpose(1, 2).contiguous()
+    v_new = v[:, :, L - nq:].transpose(1, 2).contiguous()
+    del k, v
+    lt = torch.tensor([L] * B, dtype=torch.int32, device=dev)
+    part = C.Partials(B, nq * wl.Hq, D, L, st)
+    out = torch.empty((B, nq * wl.Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, nq * wl.Hq), dtype=torch.float32, device=dev)
+    C.decode_step_multi(kc, vc, k_new, v_new, q, lt, L, part, 1.0 / math.sqrt(D), out, lse)
+    torch.cuda.synchronize()
+    out = out.view(B, nq, wl.Hq, D).cpu().numpy().astype(np.float64)
+    lse = lse.view(B, nq, wl.Hq).cpu().numpy().astype(np.float64)
+    kp, vp = planes_to_oracle(kc), planes_to_oracle(vc)
+    for h in (0, 17, 39):
+        g = h // G
+        sub = lambda p: (p[0], np.ascontiguousarray(p[1][:, g:g + 1]), np.ascontiguousarray(p[2][:, g:g + 1]))
+        for i in range(nq):
+            ref, ref_lse = O.attend(to_host_u16(q[:, i, h:h + 1]), sub(kp), sub(vp), [L - nq + 1 + i], 1,
+                                    1 / math.sqrt(D), nthreads=oracle_threads())
+            assert_close(out[:, i, h:h + 1], lse[:, i, h:h + 1], ref, ref_lse, f"token {i} head {h}")
