@@ -262,6 +262,23 @@ def test_step_hybrid_d256_ctx32k_full_size(tk, tv):
     workload_step("hybrid_d256_ctx32k", tk, tv, heads=None)
 
 
+@pytest.mark.parametrize("tk,tv", [("q4_1", "q4_1"), ("q5_0", "q5_0"), ("q5_1", "q5_1"), ("q6_0", "q6_0"),
+                                   ("q6_0", "q4_0"), ("q8_0", "q5_0"), ("q8_0", "q6_0"), ("q5_1", "q4_0")])
+def test_step_types_stack48_layer_full_size(tk, tv):
+    """The further scalar types' pairs of the 64k types workload, a layer at
+    full size in the benchmark's launch configuration: the new row bit-exact
+    and sampled heads of three KV heads against the oracle."""
+    workload_step("stack48_d128_ctx64k_types", tk, tv, heads=[0, 17, 39], layer=2)
+
+
+@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q5_1", "q4_0"), ("q6_0", "q6_0"), ("q4_1", "q4_1"),
+                                   ("q5_0", "q5_0"), ("q8_0", "q6_0")])
+def test_step_types_hybrid_d256_ctx32k_full_size(tk, tv):
+    """The hybrid layer (head_dim 256, 2 KV heads, outlier K channels) with the
+    pairs its types profile measures, every head."""
+    workload_step("hybrid_d256_ctx32k", tk, tv, heads=None)
+
+
 @pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0")])
 @pytest.mark.parametrize("name", ["batch16_ragged", "batch16_ragged_d512"])
 def test_step_batch16_ragged_full_size(name, tk, tv):
