@@ -137,10 +137,26 @@ def test_step_mixed_is_append_attention_merge(tk, tv, case):
     kvq_combine_regions: window rows and tail partials bit for bit, window
     partials, output and LSE up to fp32 rounding (a sequence whose window
     length is 0 gets no row)."""
-    B, Hkv, G, D, tl, tcap, wl, wcap, st_t, st_w = CASES[case]
     note(f"step_mixed vs three calls {tk}/{tv} case {case}")
+    step_mixed_vs_three_calls(tk, tv, CASES[case], 3100 + case)
+
+
+@pytest.mark.parametrize("tk,tv", [("q8_0", "q4_0"), ("q4_0", "q4_0")])
+def test_step_mixed_full_size_64k_tail_and_window(tk, tv):
+    """The same comparison on a layer of the 64k workload as the benchmark
+    runs it: 63488 quantised tail rows, a 2048-row fp16 window whose last row
+    the step writes, the split sizes of mixed_splits."""
+    wl = synth.WORKLOADS["stack48_d128_ctx64k"]
+    Lw, Lt = 2048, wl.ctx - 2048
+    row_t = sum(_lib.kvq_data_row_bytes(t, wl.D) + _lib.kvq_scale_row_bytes(t, wl.D) for t in (tk, tv))
+    st, sw = C.mixed_splits(Lt, Lw, row_t, 4 * wl.D, wl.B, wl.Hkv, wl.D)
+    note(f"step_mixed vs three calls full size {tk}/{tv} splits {st}/{sw}")
+    step_mixed_vs_three_calls(tk, tv, (wl.B, wl.Hkv, wl.G, wl.D, [Lt], Lt, [Lw], Lw, st, sw), 3190)
+
+
+def step_mixed_vs_three_calls(tk, tv, shape, seed):
+    B, Hkv, G, D, tl, tcap, wl, wcap, st_t, st_w = shape
     dev = "cuda"
-    seed = 3100 + case
     kt = synth.normal_f16((B, Hkv, tcap, D), seed, dev)
     vt = synth.normal_f16((B, Hkv, tcap, D), seed + 1, dev)
     kw = synth.normal_f16((B, Hkv, wcap, D), seed + 2, dev)
