@@ -113,7 +113,7 @@ WORKLOADS = {
         "hybrid-model full-attention layer: 16 query / 2 KV heads, head_dim 256, ctx 32768, "
         "batch 1; K ~ N(0,1) with 1% of channels scaled x8, V, Q ~ N(0,1)",
         layers=1, B=1, Hq=16, Hkv=2, D=256, ctx=32768, arms=[("f16", "f16"), ("q8_0", "q8_0")],
-        seed=1002, split_tokens=128, k_outlier_frac=0.01),
+        seed=1002, split_tokens=256, k_outlier_frac=0.01),
     "stack48_d128_ctx64k": Workload(
         "stack48_d128_ctx64k",
         "48-layer decode stack: 40 query / 8 KV heads, head_dim 128, ctx 65536, batch 1; per "
