@@ -251,6 +251,16 @@ int kvq_quantize_rows(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cac
  *   part_lse       : device, [B][Hq][max_splits] fp32.
  *   Requirements: B >= 1, Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 16,
  *   D % 32 == 0, 32 <= D <= 512, K and V caches with the same strides' meaning.
+ *
+ * Choosing split_tokens: the result changes only by rounding; the time
+ * depends on it.  Measured on an MI355X (256 CUs): for one long sequence the
+ * fastest splits fill the GPU's resident workgroup slots once, Hkv *
+ * ceil(max_seq_len / split_tokens) = 512 at head_dim 128 (8 KV heads: 1024
+ * rows at 65536, 4096 at 262144) and 256 at head_dim 256 (2 KV heads: 256
+ * rows at 32768); short contexts take at least 128 rows per split at head_dim
+ * 128 (128 at 4096).  A batch of ragged sequences of 16k-128k rows was
+ * fastest with 2048 rows at head_dim 128 and 1024 at head_dim 512.  Fewer
+ * rows per split mean more partials for the merge to read.
  */
 int kvq_decode_attn(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cache,
                     const void* q, const int32_t* seq_lens, int B, int Hq, int Hkv, int D,
