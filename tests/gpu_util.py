@@ -235,3 +235,40 @@ def new_row_vmax(v_new, G):
     clamped codes)."""
     m = v_new.float().abs().amax(dim=-1).cpu().numpy().astype(np.float64)   # (B, Hkv)
     return np.repeat(m, G, axis=1) * 1.1
+
+
+def replay_and_compare(call, outputs, planes, scratch, what, replays=3):
+    """Runs call() eagerly, captures it in a graph and replays the graph
+    `replays` times; every replay's outputs and cache planes must equal the eager
+    call's bit for bit."""
+    call()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outputs]
+    want_planes = [t.clone() for t in planes]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for r in range(replays):
+        for t in list(outputs) + list(scratch):
+            t.fill_(float("nan"))
+        (torch.randn(1 << 20, device="cuda") * 2.0).sum().item()   # other eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (t, w) in enumerate(zip(outputs, want)):
+            assert torch.equal(t, w), f"{what}: replay {r}, output {i} differs from the eager call"
+        for i, (t, w) in enumerate(zip(planes, want_planes)):
+            assert torch.equal(t, w), f"{what}: replay {r}, cache plane {i} differs from the eager call"
+    return want
+
+
+def plane_tensors(*caches):
+    """The device tensors holding the given caches' planes (data, and scales
+    where the type has them)."""
+    out = []
+    for p in caches:
+        out.append(p.data)
+        if p.scales is not None:
+            out.append(p.scales)
+    return out

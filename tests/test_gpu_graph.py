@@ -12,54 +12,19 @@ import pytest
 
 from oracle import oracle as O
 
-from .gpu_util import assert_close, fill_pair, note, oracle_threads, require_gpu, to_host_u16
+from .gpu_util import (assert_close, fill_pair, note, oracle_threads, plane_tensors, replay_and_compare,
+                       require_gpu, to_host_u16)
 
 torch = pytest.importorskip("torch")
 from quantised_kv_long_amd import cache as C  # noqa: E402
 from quantised_kv_long_amd import synth  # noqa: E402
 
 pytestmark = pytest.mark.gpu
-REPLAYS = 3
 
 
 @pytest.fixture(autouse=True)
 def _gpu():
     require_gpu()
-
-
-def replay_and_compare(call, outputs, planes, scratch, what):
-    """Runs call() eagerly, captures it in a graph and replays the graph
-    REPLAYS times; every replay's outputs and cache planes must equal the eager
-    call's bit for bit."""
-    call()
-    torch.cuda.synchronize()
-    want = [t.clone() for t in outputs]
-    want_planes = [t.clone() for t in planes]
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        call()
-    torch.cuda.synchronize()
-    for r in range(REPLAYS):
-        for t in list(outputs) + list(scratch):
-            t.fill_(float("nan"))
-        (torch.randn(1 << 20, device="cuda") * 2.0).sum().item()   # other eager work
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        for i, (t, w) in enumerate(zip(outputs, want)):
-            assert torch.equal(t, w), f"{what}: replay {r}, output {i} differs from the eager call"
-        for i, (t, w) in enumerate(zip(planes, want_planes)):
-            assert torch.equal(t, w), f"{what}: replay {r}, cache plane {i} differs from the eager call"
-    return want
-
-
-def plane_tensors(*caches):
-    out = []
-    for p in caches:
-        out.append(p.data)
-        if p.scales is not None:
-            out.append(p.scales)
-    return out
 
 
 STEP_CASES = [

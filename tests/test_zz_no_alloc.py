@@ -1,12 +1,15 @@
 """kvq_decode_step_noalloc (partials in the library's own device array)
 against kvq_decode_step (partials in caller memory): the same cache rows and
-the same outputs, bit for bit, on two calls in a row, the second smaller."""
+the same outputs, bit for bit, on two calls in a row, the second smaller; and
+the call captured in a HIP graph, as its callers use it, replaying the eager
+call's results."""
 import math
 
 import numpy as np
 import pytest
 
-from .gpu_util import note, oracle_planes, require_gpu, to_host_u16, upload_oracle_planes
+from .gpu_util import (note, oracle_planes, plane_tensors, replay_and_compare, require_gpu, to_host_u16,
+                       upload_oracle_planes)
 
 torch = pytest.importorskip("torch")
 from quantised_kv_long_amd import _lib  # noqa: E402
@@ -79,3 +82,32 @@ def test_noalloc_rejects_oversize_partials():
     with pytest.raises(_lib.KVQError) as e:
         _lib.kvq_decode_step_noalloc(desc, desc, x, x, q, lt, B, Hkv * G, Hkv, D, 0.1, L, st, "f32", out)
     assert e.value.status == -5
+
+
+def test_noalloc_step_graph_replays_equal_eager():
+    # the array keeps the last call's partials: each replay must rewrite
+    # every partial the merge reads
+    B, Hkv, G, D, lens, st = 2, 2, 5, 128, [3000, 700], 256
+    note(f"noalloc step in a graph q8_0/q4_0 B={B} lens={lens} split={st}")
+    dev = "cuda"
+    cap = max(lens)
+    k = synth.normal_f16((B, Hkv, cap, D), 303, dev)
+    v = synth.normal_f16((B, Hkv, cap, D), 304, dev)
+    kc = upload_oracle_planes(*oracle_planes("q8_0", to_host_u16(k)))
+    vc = upload_oracle_planes(*oracle_planes("q4_0", to_host_u16(v)))
+    q = synth.normal_f16((B, Hkv * G, D), 305, dev)
+    k_new = synth.normal_f16((B, Hkv, D), 306, dev)
+    v_new = synth.normal_f16((B, Hkv, D), 307, dev)
+    lt = torch.tensor(lens, dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hkv * G, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hkv * G), dtype=torch.float32, device=dev)
+    scale = 1 / math.sqrt(D)
+
+    def call():
+        _lib.kvq_decode_step_noalloc(kc.desc(), vc.desc(), k_new, v_new, q, lt, B, Hkv * G, Hkv, D, scale,
+                                     cap, st, "f32", out, lse)
+
+    got = replay_and_compare(call, [out, lse], plane_tensors(kc, vc), [], "noalloc step")
+    # and the eager call is kvq_decode_step's result
+    ref = one_step("q8_0", "q4_0", B, Hkv, G, D, lens, st, 303, noalloc=False)
+    assert torch.equal(got[0], ref[2]) and torch.equal(got[1], ref[3])
