@@ -313,12 +313,15 @@ def workload_case(name, tk, tv, variant, heads=None, layer=0, needle_pos=None, s
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-def test_workload_gqa5_d128_ctx4k(variant):
-    workload_case("gqa5_d128_ctx4k", "q8_0", "q4_0", variant)
+@pytest.mark.parametrize("tk,tv", list(itertools.product(TYPES, repeat=2)))
+def test_workload_gqa5_d128_ctx4k(variant, tk, tv):
+    """The one-layer 4096-row workload (128-row splits), every pair of the
+    base types, every output against the oracle."""
+    workload_case("gqa5_d128_ctx4k", tk, tv, variant)
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-@pytest.mark.parametrize("tk,tv", [("f16", "f16"), ("q8_0", "q8_0")])
+@pytest.mark.parametrize("tk,tv", [("f16", "f16"), ("q8_0", "q8_0"), ("q8_0", "q4_0"), ("q4_0", "q4_0")])
 def test_workload_hybrid_d256_ctx32k(variant, tk, tv):
     workload_case("hybrid_d256_ctx32k", tk, tv, variant)
 
