@@ -255,7 +255,7 @@ def test_step_long_ctx256k_full_size(tk, tv):
     workload_step("long_d128_ctx256k", tk, tv, heads=None)
 
 
-@pytest.mark.parametrize("tk,tv", [("f16", "f16"), ("q8_0", "q8_0")])
+@pytest.mark.parametrize("tk,tv", [("f16", "f16"), ("q8_0", "q8_0"), ("q4_0", "q4_0")])
 def test_step_hybrid_d256_ctx32k_full_size(tk, tv):
     """The hybrid model's full-attention layer (16 query / 2 KV heads, head_dim
     256, 32768 rows, outlier K channels), every head."""
