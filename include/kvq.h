@@ -254,11 +254,13 @@ int kvq_quantize_rows(const kvq_plane_desc* k_cache, const kvq_plane_desc* v_cac
  *
  * Choosing split_tokens: the result changes only by rounding; the time
  * depends on it.  Measured on an MI355X (256 CUs): for one long sequence the
- * fastest splits fill the GPU's resident workgroup slots once, Hkv *
- * ceil(max_seq_len / split_tokens) = 512 at head_dim 128 (8 KV heads: 1024
- * rows at 65536, 4096 at 262144) and 256 at head_dim 256 (2 KV heads: 256
- * rows at 32768); short contexts take at least 128 rows per split at head_dim
- * 128 (128 at 4096).  A batch of ragged sequences of 16k-128k rows was
+ * fastest splits give one or two workgroups per CU, Hkv * ceil(max_seq_len /
+ * split_tokens) = 256 or 512 at head_dim 128 (8 KV heads: 1024 or 2048 rows
+ * at 65536, within 1 %; 4096 or 8192 at 262144, 8192 up to 3 % faster), and
+ * 256 at head_dim 256 (2 KV heads: 256 rows at 32768); counts in between
+ * leave some CUs with one workgroup and others with two (13 % slower at
+ * 65536).  Short contexts take at least 128 rows per split at head_dim 128
+ * (128 at 4096).  A batch of ragged sequences of 16k-128k rows was
  * fastest with 2048 rows at head_dim 128 and 1024 at head_dim 512.  Fewer
  * rows per split mean more partials for the merge to read.
  */
