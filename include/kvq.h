@@ -19,7 +19,10 @@
  * Conventions shared by every entry point:
  *   - The caller owns all memory.  Every pointer marked "device" is HIP device
  *     memory of the current device; the library allocates nothing and keeps
- *     no state between calls, so calls are thread-safe.
+ *     no state between calls, so calls are thread-safe.  The one exception is
+ *     kvq_decode_step_noalloc, whose partials live in a device array the
+ *     library holds per GPU (see there: its calls on one GPU must not
+ *     overlap).
  *   - Calls only enqueue work on `stream` (a hipStream_t; NULL means the
  *     legacy default stream) and return.  KVQ_OK means "enqueued".
  *   - Scalar arguments are validated on the host before any HIP call; an
